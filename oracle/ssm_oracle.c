@@ -1,0 +1,480 @@
+/*
+ * ssm_oracle.c -- plain float64 reference of the S6 (Mamba) selective scan.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the correctness oracle that the GPU
+ * library is compared against.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the product path never does.  It
+ * shares no source, header, table or helper with the HIP library.
+ *
+ * Every routine is the textbook definition written out as a sequential loop
+ * over time, in double precision, one (batch, channel) row at a time.  OpenMP
+ * is used only across rows that are independent by construction; there is no
+ * blocking, chunking or reordering of the time loop.
+ *
+ * Sources (the pages this follows):
+ *  - "mamba, live" (soundlark.studio), section "what is actually running":
+ *    the streaming pseudocode of one block -- causal 4-tap depthwise conv with
+ *    SiLU, dt = softplus(dt_proj(.)), A = -exp(A_log), the recurrence
+ *    h = exp(dt*A)*h + (dt*B)*xc, the readout y = <h,C> + D*xc and the gate
+ *    y*SiLU(z).
+ *  - "the s6 cell" (soundlark.studio), section "the recurrence": the same
+ *    update in base-2 form, with A < 0 and dt > 0 so the decay lies in (0,1).
+ *  - TensorViz "Carry context through a selective state" (explorer page and
+ *    model manifest): exact diagonal ZOH, Abar = exp(dt*A) and
+ *    Bbar = (exp(dt*A) - 1) * B / A; C reads the updated state (manifest step
+ *    "read"); the conv is left padded and reads the current and W-1 earlier
+ *    inputs (manifest step "local").
+ *
+ * Layouts (row-major, channel-last):
+ *   x, u, dt_raw, z, y, dy, du, ...   [B, L, D]
+ *   Bm, Cm, dB, dC                    [B, L, N]
+ *   A_log, dA_log                     [D, N]
+ *   dt_bias, Dskip, conv_b            [D]
+ *   conv_w                            [D, W]  (tap W-1 multiplies the current input)
+ *   h0, hT, dh0, dhT                  [B, D, N]
+ *   conv_state_in / conv_state_out    [B, W-1, D]  (oldest input first)
+ * A NULL optional pointer means "absent": dt_bias, Dskip and conv_b read as 0,
+ * z means "no gate", h0 and the conv state read as zeros, outputs are skipped.
+ *
+ * Return value: 0 on success, -1 on a bad argument, -2 on allocation failure.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_DISC_DELTA_B 0
+#define ORC_DISC_ZOH 1
+
+/* softplus(r) = log(1 + e^r), evaluated without overflow.
+ * ("mamba, live": dt = softplus(dt_proj(.)) > 0.) */
+static double orc_softplus(double r)
+{
+    return (r > 0.0 ? r : 0.0) + log1p(exp(-fabs(r)));
+}
+
+/* logistic sigmoid 1 / (1 + e^-x), evaluated without overflow. */
+static double orc_sigmoid(double x)
+{
+    if (x >= 0.0)
+        return 1.0 / (1.0 + exp(-x));
+    double e = exp(x);
+    return e / (1.0 + e);
+}
+
+/* SiLU(x) = x * sigmoid(x) ("mamba, live": the conv output and the gate). */
+static double orc_silu(double x) { return x * orc_sigmoid(x); }
+
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* ------------------------------------------------------------------------ */
+/* Causal depthwise convolution ("mamba, live": xc = SiLU(depthwise_conv4(xin)),
+ * 4-tap causal, per channel; TensorViz manifest step "local": left padded,
+ * reads the current and W-1 earlier inputs).  Cross-correlation as in a
+ * PyTorch Conv1d with groups = channels:
+ *   xc[t] = bias + sum_{k<W} w[k] * xt[t - (W-1) + k]
+ * where xt[i] = x[i] for i >= 0 and the carried history (or 0) for i < 0. */
+static double orc_conv_input(const double *x, const double *state_in,
+                             int64_t L, int64_t D, int32_t W,
+                             int64_t b, int64_t d, int64_t i)
+{
+    if (i >= 0)
+        return x[(b * L + i) * D + d];
+    if (!state_in)
+        return 0.0;
+    /* history slot j holds xt[-(W-1) + j] */
+    int64_t j = i + (W - 1);
+    return state_in[(b * (int64_t)(W - 1) + j) * D + d];
+}
+
+int orc_conv1d_causal(int64_t B, int64_t L, int64_t D, int32_t W,
+                      const double *x, const double *w, const double *bias,
+                      const double *state_in, double *state_out,
+                      int32_t silu, double *y)
+{
+    if (B < 0 || L < 0 || D < 0 || W < 1 || !w || (L > 0 && (!x || !y)))
+        return -1;
+    int64_t rows = B * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t b = r / D, d = r % D;
+        for (int64_t t = 0; t < L; ++t) {
+            double acc = bias ? bias[d] : 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                acc += w[d * W + k] *
+                       orc_conv_input(x, state_in, L, D, W, b, d, t - (W - 1) + k);
+            y[(b * L + t) * D + d] = silu ? orc_silu(acc) : acc;
+        }
+        if (state_out) {
+            for (int32_t j = 0; j < W - 1; ++j) {
+                int64_t i = L - (W - 1) + j;
+                state_out[(b * (int64_t)(W - 1) + j) * D + d] =
+                    orc_conv_input(x, state_in, L, D, W, b, d, i);
+            }
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Discretised input coefficient for one state coordinate.
+ *  - dt*B form ("mamba, live" pseudocode; "the s6 cell"): coef = dt.
+ *  - exact ZOH (TensorViz explorer page): Bbar = (exp(dt*A) - 1) * B / A,
+ *    so coef = expm1(dt*A) / A.
+ * The write is then coef * B[n] * u. */
+static double orc_write_coef(int32_t disc, double delta, double A)
+{
+    if (disc == ORC_DISC_ZOH)
+        return expm1(delta * A) / A;
+    return delta;
+}
+
+/* The selective scan given dt (already softplus'ed).  For every (b, d):
+ *   A[n] = -exp(A_log[d,n])
+ *   h[n] = h0 (default 0)
+ *   for t: a = exp(dt_t * A[n]);  h[n] = a*h[n] + coef(dt_t, A[n]) * B[t,n] * u_t
+ *          yv = sum_n C[t,n] * h[n] + Dskip * u_t      (C reads the updated state)
+ *          y  = yv * SiLU(z_t)  if z is given, else yv
+ * Optional traces record a, the write and h for every (b, t, d, n). */
+int orc_scan_core(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
+                  const double *u, const double *delta, const double *A_log,
+                  const double *Bm, const double *Cm, const double *Dskip,
+                  const double *z, const double *h0, double *hT, double *y,
+                  double *trace_a, double *trace_w, double *trace_h)
+{
+    if (B < 0 || L < 0 || D < 0 || N < 1 || !A_log ||
+        (disc != ORC_DISC_DELTA_B && disc != ORC_DISC_ZOH))
+        return -1;
+    if (L > 0 && (!u || !delta || !Bm || !Cm || !y))
+        return -1;
+    int64_t rows = B * D;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *h = (double *)malloc(sizeof(double) * (size_t)N);
+        double *A = (double *)malloc(sizeof(double) * (size_t)N);
+        {
+#pragma omp for schedule(static)
+            for (int64_t r = 0; r < rows; ++r) {
+                if (!h || !A) {
+#pragma omp atomic write
+                    failed = 1;
+                    continue;
+                }
+                int64_t b = r / D, d = r % D;
+                for (int64_t n = 0; n < N; ++n) {
+                    A[n] = -exp(A_log[d * N + n]);
+                    h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;
+                }
+                for (int64_t t = 0; t < L; ++t) {
+                    int64_t i = (b * L + t) * D + d;
+                    double dt = delta[i], ut = u[i];
+                    double yv = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        double a = exp(dt * A[n]);
+                        double wr = orc_write_coef(disc, dt, A[n]) * Bm[(b * L + t) * N + n] * ut;
+                        h[n] = a * h[n] + wr;
+                        yv += Cm[(b * L + t) * N + n] * h[n];
+                        if (trace_a) trace_a[i * N + n] = a;
+                        if (trace_w) trace_w[i * N + n] = wr;
+                        if (trace_h) trace_h[i * N + n] = h[n];
+                    }
+                    if (Dskip)
+                        yv += Dskip[d] * ut;
+                    y[i] = z ? yv * orc_silu(z[i]) : yv;
+                }
+                if (hT)
+                    for (int64_t n = 0; n < N; ++n)
+                        hT[(b * D + d) * N + n] = h[n];
+            }
+        }
+        free(h);
+        free(A);
+    }
+    return failed ? -2 : 0;
+}
+
+/* dt = softplus(dt_raw + dt_bias) for every (b, t, d). */
+int orc_delta(int64_t B, int64_t L, int64_t D, const double *dt_raw,
+              const double *dt_bias, double *delta)
+{
+    if (B < 0 || L < 0 || D < 0 || (B * L * D > 0 && (!dt_raw || !delta)))
+        return -1;
+    int64_t total = B * L * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < total; ++i)
+        delta[i] = orc_softplus(dt_raw[i] + (dt_bias ? dt_bias[i % D] : 0.0));
+    return 0;
+}
+
+/* Full forward: dt from dt_raw, then the scan.  delta_out may be NULL. */
+int orc_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
+                 const double *u, const double *dt_raw, const double *dt_bias,
+                 const double *A_log, const double *Bm, const double *Cm,
+                 const double *Dskip, const double *z, const double *h0,
+                 double *hT, double *y, double *delta_out)
+{
+    int64_t total = B * L * D;
+    double *delta = delta_out;
+    if (!delta && total > 0) {
+        delta = (double *)malloc(sizeof(double) * (size_t)total);
+        if (!delta)
+            return -2;
+    }
+    int rc = orc_delta(B, L, D, dt_raw, dt_bias, delta);
+    if (rc == 0)
+        rc = orc_scan_core(B, L, D, N, disc, u, delta, A_log, Bm, Cm, Dskip, z,
+                           h0, hT, y, NULL, NULL, NULL);
+    if (delta != delta_out)
+        free(delta);
+    return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Backward of orc_scan_fwd, derived by hand from the forward definition
+ * (reverse-mode adjoint of the time loop).  Let g[n] be dLoss/dh_t[n].  With
+ * yv_t the pre-gate output and s = sigmoid(z_t):
+ *   gate:   dyv = dy * z*s,   dz = dy * yv * s * (1 + z*(1 - s))
+ *   skip:   dDskip += dyv*u,  du = Dskip*dyv
+ *   start:  g = dhT (default 0); for t = L-1 .. 0 and every n:
+ *     g += C[t,n]*dyv;  dC[t,n] += h_t[n]*dyv;  da = g*h_{t-1}[n]  (h_{-1} = h0)
+ *     dt*B form:  ddt += da*a*A + g*B*u;  du += g*dt*B;  dB += g*dt*u;  dA += da*a*dt
+ *     ZOH form (c = expm1(dt*A)/A):
+ *                 ddt += da*a*A + g*a*B*u;  du += g*c*B;  dB += g*c*u;
+ *                 dA += da*a*dt + g*B*u*(dt*a*A - expm1(dt*A))/A^2
+ *     g = a*g
+ *   end:    dh0 = g;  dA_log = dA*A  (A = -exp(A_log));
+ *           d_dt_raw = ddt * sigmoid(dt_raw + dt_bias);  d_dt_bias = sum_{b,t} d_dt_raw
+ * dB, dC are summed over channels; dA_log, dDskip, d_dt_bias over batch and time.
+ * Channels are split into fixed groups whose partial sums are merged in group
+ * order, so the result does not depend on the thread count. */
+#define ORC_BWD_GROUPS 16
+
+int orc_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
+                 const double *u, const double *dt_raw, const double *dt_bias,
+                 const double *A_log, const double *Bm, const double *Cm,
+                 const double *Dskip, const double *z, const double *h0,
+                 const double *dy, const double *dhT,
+                 double *du, double *d_dt_raw, double *d_delta, double *d_dt_bias,
+                 double *dA_log, double *dB, double *dC, double *dDskip,
+                 double *dz, double *dh0)
+{
+    if (B < 0 || L < 0 || D < 1 || N < 1 || !A_log ||
+        (disc != ORC_DISC_DELTA_B && disc != ORC_DISC_ZOH))
+        return -1;
+    if (L > 0 && (!u || !dt_raw || !Bm || !Cm || !dy))
+        return -1;
+    int64_t G = D < ORC_BWD_GROUPS ? D : ORC_BWD_GROUPS;
+    size_t bln = (size_t)(B * L * N);
+    /* per-group partials */
+    double *pB = (double *)calloc((size_t)G * bln + 1, sizeof(double));
+    double *pC = (double *)calloc((size_t)G * bln + 1, sizeof(double));
+    /* per-(b,d) partials of the parameter gradients */
+    double *rA = (double *)calloc((size_t)(B * D * N) + 1, sizeof(double));
+    double *rD = (double *)calloc((size_t)(B * D) + 1, sizeof(double));
+    double *rT = (double *)calloc((size_t)(B * D) + 1, sizeof(double));
+    if (!pB || !pC || !rA || !rD || !rT) {
+        free(pB); free(pC); free(rA); free(rD); free(rT);
+        return -2;
+    }
+    int failed = 0;
+    int64_t tasks = B * G;
+#pragma omp parallel
+    {
+        size_t ln = (size_t)((L > 0 ? L : 1) * N);
+        double *A = (double *)malloc(sizeof(double) * (size_t)N);
+        double *g = (double *)malloc(sizeof(double) * (size_t)N);
+        double *dA = (double *)malloc(sizeof(double) * (size_t)N);
+        double *ha = (double *)malloc(sizeof(double) * ln);   /* a[t][n] */
+        double *hh = (double *)malloc(sizeof(double) * ln);   /* h_t[n] */
+        double *dl = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        double *yv = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+        {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t task = 0; task < tasks; ++task) {
+                if (!A || !g || !dA || !ha || !hh || !dl || !yv) {
+#pragma omp atomic write
+                    failed = 1;
+                    continue;
+                }
+                int64_t b = task / G, grp = task % G;
+                int64_t d_lo = grp * D / G, d_hi = (grp + 1) * D / G;
+                double *gB = pB + (size_t)grp * bln + (size_t)(b * L * N);
+                double *gC = pC + (size_t)grp * bln + (size_t)(b * L * N);
+                for (int64_t d = d_lo; d < d_hi; ++d) {
+                    double Dd = Dskip ? Dskip[d] : 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        A[n] = -exp(A_log[d * N + n]);
+                        g[n] = h0 ? h0[(b * D + d) * N + n] : 0.0; /* forward state */
+                        dA[n] = 0.0;
+                    }
+                    /* forward, recording a, h and the pre-gate output */
+                    for (int64_t t = 0; t < L; ++t) {
+                        int64_t i = (b * L + t) * D + d;
+                        double dt = orc_softplus(dt_raw[i] + (dt_bias ? dt_bias[d] : 0.0));
+                        double acc = 0.0;
+                        dl[t] = dt;
+                        for (int64_t n = 0; n < N; ++n) {
+                            double a = exp(dt * A[n]);
+                            g[n] = a * g[n] + orc_write_coef(disc, dt, A[n]) *
+                                                  Bm[(b * L + t) * N + n] * u[i];
+                            ha[t * N + n] = a;
+                            hh[t * N + n] = g[n];
+                            acc += Cm[(b * L + t) * N + n] * g[n];
+                        }
+                        yv[t] = acc + Dd * u[i];
+                    }
+                    /* reverse sweep */
+                    for (int64_t n = 0; n < N; ++n)
+                        g[n] = dhT ? dhT[(b * D + d) * N + n] : 0.0;
+                    double sD = 0.0, sT = 0.0;
+                    for (int64_t t = L - 1; t >= 0; --t) {
+                        int64_t i = (b * L + t) * D + d;
+                        double dt = dl[t], ut = u[i], dyv;
+                        if (z) {
+                            double s = orc_sigmoid(z[i]);
+                            dyv = dy[i] * z[i] * s;
+                            if (dz)
+                                dz[i] = dy[i] * yv[t] * s * (1.0 + z[i] * (1.0 - s));
+                        } else {
+                            dyv = dy[i];
+                        }
+                        sD += dyv * ut;
+                        double dut = Dd * dyv, ddt = 0.0;
+                        for (int64_t n = 0; n < N; ++n) {
+                            double a = ha[t * N + n], An = A[n];
+                            double Bv = Bm[(b * L + t) * N + n];
+                            double hprev = t > 0 ? hh[(t - 1) * N + n]
+                                                 : (h0 ? h0[(b * D + d) * N + n] : 0.0);
+                            g[n] += Cm[(b * L + t) * N + n] * dyv;
+                            gC[t * N + n] += hh[t * N + n] * dyv;
+                            double da = g[n] * hprev;
+                            if (disc == ORC_DISC_ZOH) {
+                                double em1 = expm1(dt * An), c = em1 / An;
+                                ddt += da * a * An + g[n] * a * Bv * ut;
+                                dut += g[n] * c * Bv;
+                                gB[t * N + n] += g[n] * c * ut;
+                                dA[n] += da * a * dt + g[n] * Bv * ut * (dt * a * An - em1) / (An * An);
+                            } else {
+                                ddt += da * a * An + g[n] * Bv * ut;
+                                dut += g[n] * dt * Bv;
+                                gB[t * N + n] += g[n] * dt * ut;
+                                dA[n] += da * a * dt;
+                            }
+                            g[n] *= a;
+                        }
+                        double sg = orc_sigmoid(dt_raw[i] + (dt_bias ? dt_bias[d] : 0.0));
+                        if (du) du[i] = dut;
+                        if (d_delta) d_delta[i] = ddt;
+                        if (d_dt_raw) d_dt_raw[i] = ddt * sg;
+                        sT += ddt * sg;
+                    }
+                    for (int64_t n = 0; n < N; ++n) {
+                        if (dh0) dh0[(b * D + d) * N + n] = g[n];
+                        rA[(b * D + d) * N + n] = dA[n] * A[n];
+                    }
+                    rD[b * D + d] = sD;
+                    rT[b * D + d] = sT;
+                }
+            }
+        }
+        free(A); free(g); free(dA); free(ha); free(hh); free(dl); free(yv);
+    }
+    if (!failed) {
+        if (dB || dC) {
+            for (size_t k = 0; k < bln; ++k) {
+                double sb = 0.0, sc = 0.0;
+                for (int64_t grp = 0; grp < G; ++grp) {
+                    sb += pB[(size_t)grp * bln + k];
+                    sc += pC[(size_t)grp * bln + k];
+                }
+                if (dB) dB[k] = sb;
+                if (dC) dC[k] = sc;
+            }
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            double sD = 0.0, sT = 0.0;
+            for (int64_t b = 0; b < B; ++b) {
+                sD += rD[b * D + d];
+                sT += rT[b * D + d];
+            }
+            if (dDskip) dDskip[d] = sD;
+            if (d_dt_bias) d_dt_bias[d] = sT;
+            for (int64_t n = 0; n < N; ++n) {
+                double s = 0.0;
+                for (int64_t b = 0; b < B; ++b)
+                    s += rA[(b * D + d) * N + n];
+                if (dA_log) dA_log[d * N + n] = s;
+            }
+        }
+    }
+    free(pB); free(pC); free(rA); free(rD); free(rT);
+    return failed ? -2 : 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* One streaming step ("mamba, live": one token in, one token out, constant
+ * work; the state is h plus a (W-1)-token conv history per channel).
+ * For every stream s and channel d:
+ *   window = [history[0..W-2], x]; xc = bias + sum_k w[k]*window[k]; u = SiLU(xc)
+ *   history <- [history[1..W-2], x]
+ *   then one time step of the scan with u, updating h[s,d,:] in place.
+ * With conv_w == NULL the input x is used as u directly and the history is
+ * left alone.  h is [S, D, N], conv_state [S, W-1, D], x/dt_raw/z/y [S, D],
+ * Bm/Cm [S, N]. */
+int orc_step(int64_t S, int64_t D, int64_t N, int32_t W, int32_t disc,
+             double *h, double *conv_state, const double *x,
+             const double *dt_raw, const double *Bm, const double *Cm,
+             const double *z, const double *conv_w, const double *conv_b,
+             const double *dt_bias, const double *A_log, const double *Dskip,
+             double *y)
+{
+    if (S < 0 || D < 0 || N < 1 || !h || !x || !dt_raw || !Bm || !Cm ||
+        !A_log || !y || (disc != ORC_DISC_DELTA_B && disc != ORC_DISC_ZOH))
+        return -1;
+    if (conv_w && (W < 1 || (W > 1 && !conv_state)))
+        return -1;
+    int64_t rows = S * D;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        int64_t s = r / D, d = r % D;
+        double xt = x[s * D + d], ut;
+        if (conv_w) {
+            double acc = conv_b ? conv_b[d] : 0.0;
+            for (int32_t k = 0; k < W - 1; ++k)
+                acc += conv_w[d * W + k] * conv_state[(s * (int64_t)(W - 1) + k) * D + d];
+            acc += conv_w[d * W + (W - 1)] * xt;
+            for (int32_t k = 0; k + 1 < W - 1; ++k)
+                conv_state[(s * (int64_t)(W - 1) + k) * D + d] =
+                    conv_state[(s * (int64_t)(W - 1) + k + 1) * D + d];
+            if (W > 1)
+                conv_state[(s * (int64_t)(W - 1) + (W - 2)) * D + d] = xt;
+            ut = orc_silu(acc);
+        } else {
+            ut = xt;
+        }
+        double dt = orc_softplus(dt_raw[s * D + d] + (dt_bias ? dt_bias[d] : 0.0));
+        double yv = 0.0;
+        for (int64_t n = 0; n < N; ++n) {
+            double An = -exp(A_log[d * N + n]);
+            double a = exp(dt * An);
+            double *hn = &h[(s * D + d) * N + n];
+            *hn = a * *hn + orc_write_coef(disc, dt, An) * Bm[s * N + n] * ut;
+            yv += Cm[s * N + n] * *hn;
+        }
+        if (Dskip)
+            yv += Dskip[d] * ut;
+        y[s * D + d] = z ? yv * orc_silu(z[s * D + d]) : yv;
+    }
+    return 0;
+}

@@ -1,0 +1,58 @@
+"""The oracle's pins must catch plausible mistakes.
+
+Each case plants one mistake in a copy of ssm_oracle.c (on the CPU, in a
+temporary directory), builds it, and runs the pin suite against that build in
+a subprocess.  The suite must fail for every mutant.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(ROOT, "oracle", "ssm_oracle.c")
+
+MUTANTS = {
+    "softplus_sign": ("log1p(exp(-fabs(r)))", "log1p(exp(fabs(r)))"),
+    "zoh_coef_sign": ("return expm1(delta * A) / A;", "return expm1(delta * A) / (-A);"),
+    "decay_sign": ("double a = exp(dt * A[n]);\n                        double wr",
+                   "double a = exp(-dt * A[n]);\n                        double wr"),
+    "A_not_exponentiated": ("A[n] = -exp(A_log[d * N + n]);\n                    h[n] = h0",
+                            "A[n] = -(A_log[d * N + n]);\n                    h[n] = h0"),
+    "readout_before_update": ("yv += Cm[(b * L + t) * N + n] * h[n];",
+                              "yv += Cm[(b * L + t) * N + n] * (h[n] - wr) / a;"),
+    "dropped_skip_term": ("                    if (Dskip)\n                        yv += Dskip[d] * ut;\n                    y[i]",
+                          "                    y[i]"),
+    "gate_sigmoid_not_silu": ("y[i] = z ? yv * orc_silu(z[i]) : yv;", "y[i] = z ? yv * orc_sigmoid(z[i]) : yv;"),
+    "h0_ignored": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
+    "dt_bias_ignored": ("(dt_bias ? dt_bias[i % D] : 0.0)", "0.0"),
+    "conv_taps_reversed": ("acc += w[d * W + k] *", "acc += w[d * W + (W - 1 - k)] *"),
+    "conv_state_out_off_by_one": ("int64_t i = L - (W - 1) + j;", "int64_t i = L - W + j;"),
+    "step_history_not_shifted": ("conv_state[(s * (int64_t)(W - 1) + k + 1) * D + d];",
+                                 "conv_state[(s * (int64_t)(W - 1) + k) * D + d];"),
+    "bwd_dA_missing_decay": ("dA[n] += da * a * dt;\n", "dA[n] += da * dt;\n"),
+    "bwd_dz_wrong": ("(1.0 + z[i] * (1.0 - s))", "(1.0 + z[i] * s)"),
+    "bwd_ddt_raw_missing_sigmoid": ("if (d_dt_raw) d_dt_raw[i] = ddt * sg;", "if (d_dt_raw) d_dt_raw[i] = ddt;"),
+    "bwd_dC_uses_previous_state": ("gC[t * N + n] += hh[t * N + n] * dyv;", "gC[t * N + n] += hprev * dyv;"),
+    "bwd_zoh_dA_sign": ("(dt * a * An - em1)", "(dt * a * An + em1)"),
+    "bwd_adjoint_not_decayed": ("                            g[n] *= a;\n", ""),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation site not unique / missing: %s" % name
+    mut = tmp_path / "mutant.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "libmutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-o", str(lib),
+                    str(mut), "-lm"], check=True)
+    env = dict(os.environ, SSM_ORACLE_LIB=str(lib), OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle_pins.py"),
+                        "-x", "-q", "-p", "no:cacheprovider"], cwd=ROOT, env=env,
+                       capture_output=True, text=True, timeout=600)
+    assert r.returncode == 1, "pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])
