@@ -1,0 +1,330 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 selective scan on one GPU.
+
+Headline workload: the Mamba-mini block forward at batch 8, L=2048,
+D_inner=1536, N=16, float32 -- fused 4-tap causal conv + SiLU, softplus step
+size, the dt*B recurrence, readout and SiLU(z) gate, one ssm_scan_fwd call
+per step on inputs already resident in HBM.  Two input replicas alternate so
+that no step finds the previous step's data in the 256 MB last-level cache.
+
+Printed: one JSON line with the headline value (scan elements/s =
+B*L*D*N / time), the dominant kernel's roofline figures (algorithmic bytes
+over its average HIP-event duration), the oracle's CPU baseline and, under
+"extra", the other workloads: backward, the L=256 block, the 65,536-token
+bf16 two-level scan and the six-block streaming decode.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def fwd_bytes(B, L, D, N, W, es, gate=True, conv=True):
+    per_tok = B * L * D * es * (3 + (1 if gate else 0))      # x, dt_raw, y (+ z)
+    bc = 2 * B * L * N * es
+    params = 4 * (D + D * N + D + (D * W + D if conv else 0))
+    return per_tok + bc + params
+
+
+def bwd_bytes(B, L, D, N, es, gate=True):
+    reads = B * L * D * es * (3 + (1 if gate else 0)) + 2 * B * L * N * es   # u, dt, dy (+z), B, C
+    writes = B * L * D * es * (2 + (1 if gate else 0)) + 2 * B * L * N * es  # du, ddt (+dz), dB, dC
+    params = 4 * (3 * D + D * N) + 4 * (3 * D + D * N)                        # read + grads written
+    return reads + writes + params
+
+
+class EventTimer:
+    """HIP-event durations of individual launches on the current stream."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def run(self, fn):
+        t = self.torch
+        s, e = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((s, e))
+
+    def mean_ms(self):
+        self.torch.cuda.synchronize()
+        return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle's CPU timing")
+    ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(requested --gpus %d, WORLD_SIZE %d)" % (args.gpus, world), file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import seeded_inputs as si
+    import selective_state_space_ssm_amd as ssm
+
+    ssm.lib()
+    torch.cuda.set_device(0)
+    dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda", dt)
+
+    # ------------------------------------------------------------ headline
+    B, L, D, N, W = 8, 2048, 1536, 16, 4
+    log("generating inputs B=%d L=%d D=%d N=%d" % (B, L, D, N))
+    reps = []
+    for r in range(2):
+        p = si.mamba_block(B, L, D, N, W, workload=si.WL_FWDBWD, seed=r)
+        reps.append({k: dev(v) for k, v in p.items()})
+        reps[-1]["y"] = torch.empty(B, L, D, device="cuda")
+
+    def fwd(rp):
+        ssm.ssm_scan_fwd(rp["x"], rp["dt_raw"], rp["A_log"], rp["B"], rp["C"], dt_bias=rp["dt_bias"],
+                         Dskip=rp["Dskip"], z=rp["z"], conv_w=rp["conv_w"], conv_b=rp["conv_b"], y=rp["y"])
+
+    for i in range(args.warmup):
+        fwd(reps[i % 2])
+    torch.cuda.synchronize()
+    timer = EventTimer(torch)
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        timer.run(lambda: fwd(reps[i % 2]))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = timer.mean_ms()
+    elems = B * L * D * N
+    nbytes = fwd_bytes(B, L, D, N, W, 4)
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    log("forward: %.2f us/launch, %.1f GB/s (%.1f%% of %.0f)" % (kern_ms * 1e3, achieved,
+                                                                  100 * achieved / HBM_PEAK_GBS, HBM_PEAK_GBS))
+    out = {
+        "metric": "scan elements/s (B*L*D*N), forward, Mamba-mini block",
+        "value": elems * args.steps / wall,
+        "unit": "elements/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall * 1e3 / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded normal inputs of the Mamba-mini shapes)",
+        "config": {"workload": "mamba-mini block forward scan, fused conv4+SiLU, dt*B, SiLU(z) gate",
+                   "batch": B, "seq_len": L, "d_inner": D, "d_state": N, "conv_width": W,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "scan_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(kern_ms * 1e3, 3)},
+    }
+    del reps
+    torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ extras
+    extra = {}
+    if not args.no_extra:
+        try:
+            extra.update(bench_extras(torch, np, si, ssm, dev, args))
+        except Exception as e:  # report, keep the headline line
+            log("extra workloads failed: %r" % (e,))
+            extra["error"] = repr(e)
+    if args.copy_probe:
+        n = 1 << 28
+        a = torch.empty(n, device="cuda")
+        bb = torch.empty(n, device="cuda")
+        for _ in range(5):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        extra["copy_probe_bytes_each_way"] = n * 4
+    out["extra"] = extra
+
+    # ------------------------------------------------------------ CPU baseline
+    if not args.no_cpu_baseline:
+        try:
+            out["cpu_baseline"] = cpu_baseline(np, si)
+        except Exception as e:
+            log("cpu baseline failed: %r" % (e,))
+            out["cpu_baseline"] = {"error": repr(e)}
+    print(json.dumps(out), flush=True)
+
+
+def bench_extras(torch, np, si, ssm, dev, args):
+    ex = {}
+    reps = max(5, args.steps // 2)
+
+    # backward at the headline shape
+    B, L, D, N = 8, 2048, 1536, 16
+    p = si.mamba_block(B, L, D, N, 4, workload=si.WL_FWDBWD, with_dy=True)
+    P = {k: dev(v) for k, v in p.items()}
+    u = ssm.conv1d_causal(P["x"], P["conv_w"], P["conv_b"])
+    out = {}
+    ws = torch.empty(ssm.ssm_scan_bwd_workspace_size(ssm.ssm_scan_desc(B, L, D, N, 0, 0, 0, 0)),
+                     dtype=torch.uint8, device="cuda")
+
+    def bwd():
+        ssm.ssm_scan_bwd(u, P["dt_raw"], P["A_log"], P["B"], P["C"], P["dy"], dt_bias=P["dt_bias"],
+                         Dskip=P["Dskip"], z=P["z"], out=out, workspace=ws)
+
+    for _ in range(2):
+        bwd()
+    tm = EventTimer(torch)
+    for _ in range(reps):
+        tm.run(bwd)
+    ms = tm.mean_ms()
+    nb = bwd_bytes(B, L, D, N, 4)
+    ex["backward_B8_L2048"] = {"us_per_call": round(ms * 1e3, 2), "elements_per_s": B * L * D * N / (ms * 1e-3),
+                               "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": nb}
+    log("backward: %.1f us" % (ms * 1e3))
+
+    # conv alone and the L=256 block
+    tm = EventTimer(torch)
+    for _ in range(reps):
+        tm.run(lambda: ssm.conv1d_causal(P["x"], P["conv_w"], P["conv_b"], y=u))
+    ms = tm.mean_ms()
+    nb = 2 * B * L * D * 4 + 4 * D * 5
+    ex["conv1d_B8_L2048"] = {"us_per_call": round(ms * 1e3, 2), "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    del P, u, out, ws
+    torch.cuda.empty_cache()
+
+    B2, L2 = 8, 256
+    q = si.mamba_block(B2, L2, D, N, 4, workload=si.WL_BLOCK)
+    Q = {k: dev(v) for k, v in q.items()}
+    y2 = torch.empty(B2, L2, D, device="cuda")
+    f2 = lambda: ssm.ssm_scan_fwd(Q["x"], Q["dt_raw"], Q["A_log"], Q["B"], Q["C"], dt_bias=Q["dt_bias"],
+                                  Dskip=Q["Dskip"], z=Q["z"], conv_w=Q["conv_w"], conv_b=Q["conv_b"], y=y2)
+    for _ in range(3):
+        f2()
+    tm = EventTimer(torch)
+    for _ in range(reps):
+        tm.run(f2)
+    ms = tm.mean_ms()
+    nb = fwd_bytes(B2, L2, D, N, 4, 4)
+    ex["forward_B8_L256"] = {"us_per_call": round(ms * 1e3, 2), "elements_per_s": B2 * L2 * D * N / (ms * 1e-3),
+                             "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                             "note": "working set fits the 256 MB last-level cache"}
+    del Q, y2
+    torch.cuda.empty_cache()
+
+    # long sequence, bf16, two-level scan
+    L4 = 65536
+    r = si.mamba_block(1, L4, D, N, 4, workload=si.WL_LONG, bf16=True)
+    bf = torch.bfloat16
+    R = {k: dev(r[k], bf) for k in ("x", "dt_raw", "B", "C", "z")}
+    R.update({k: dev(r[k]) for k in ("dt_bias", "A_log", "Dskip")})
+    y4 = torch.empty(1, L4, D, device="cuda", dtype=bf)
+    desc = ssm.ssm_scan_desc(1, L4, D, N, 0, 1, 0, 0)
+    ws4 = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_size(desc)), dtype=torch.uint8, device="cuda")
+    f4 = lambda: ssm.ssm_scan_fwd(R["x"], R["dt_raw"], R["A_log"], R["B"], R["C"], dt_bias=R["dt_bias"],
+                                  Dskip=R["Dskip"], z=R["z"], y=y4, workspace=ws4)
+    for _ in range(2):
+        f4()
+    tm = EventTimer(torch)
+    for _ in range(reps):
+        tm.run(f4)
+    ms = tm.mean_ms()
+    nb = fwd_bytes(1, L4, D, N, 4, 2, conv=False)
+    ex["forward_bf16_B1_L65536_chunked"] = {"us_per_call": round(ms * 1e3, 2),
+                                            "elements_per_s": L4 * D * N / (ms * 1e-3),
+                                            "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    del R, y4, ws4
+    torch.cuda.empty_cache()
+
+    # streaming decode: 6 blocks x 256 streams x 1536 channels x 16 states,
+    # 1,024 token steps; inputs for a pool of 32 steps are resident and
+    # cycled.  Token steps are captured in a HIP graph (32 steps per graph)
+    # so that host launch overhead stays out of the device timeline.
+    nblk, S, steps, pool = 6, 256, 1024, 32
+    prm = {k: dev(v) for k, v in si.stream_params(nblk, D, N, 4).items()}
+    h = torch.zeros(nblk, S, D, N, device="cuda")
+    cs = torch.zeros(nblk, S, 3, D, device="cuda")
+    toks = []
+    for t in range(pool):
+        per = [si.stream_token_torch(k, t, S, D, N, "cuda") for k in range(nblk)]
+        toks.append({kk: torch.stack([pp[kk] for pp in per]).contiguous() for kk in per[0]})
+    ys = torch.empty(nblk, S, D, device="cuda")
+
+    def per_block(t):
+        i = toks[t]
+        for k in range(nblk):
+            ssm.ssm_step(h[k:k + 1], i["x"][k:k + 1], i["dt_raw"][k:k + 1], prm["A_log"][k:k + 1],
+                         i["B"][k:k + 1], i["C"][k:k + 1], conv_state=cs[k:k + 1], z=i["z"][k:k + 1],
+                         conv_w=prm["conv_w"][k:k + 1], conv_b=prm["conv_b"][k:k + 1],
+                         dt_bias=prm["dt_bias"][k:k + 1], Dskip=prm["Dskip"][k:k + 1], y=ys[k:k + 1])
+
+    def stacked(t):
+        i = toks[t]
+        ssm.ssm_step(h, i["x"], i["dt_raw"], prm["A_log"], i["B"], i["C"], conv_state=cs, z=i["z"],
+                     conv_w=prm["conv_w"], conv_b=prm["conv_b"], dt_bias=prm["dt_bias"], Dskip=prm["Dskip"], y=ys)
+
+    per_block_bytes = (2 * S * D * N * 4 + 2 * S * 3 * D * 4 + S * D * 4 * 4 + 2 * S * N * 4
+                       + 4 * (D * N + 3 * D + 4 * D))
+    for name, fn in (("per_block_launches", per_block), ("stacked_one_launch", stacked)):
+        for t in range(4):
+            fn(t)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for t in range(pool):
+                fn(t)
+        gr.replay()
+        torch.cuda.synchronize()
+        tm = EventTimer(torch)
+        t0 = time.perf_counter()
+        for _ in range(steps // pool):
+            tm.run(gr.replay)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = tm.mean_ms() / pool       # per token step
+        ex["streaming_6blk_256streams_" + name] = {
+            "tokens_per_s": S / (ms * 1e-3), "tokens_per_s_wall": S * steps / wall,
+            "us_per_token_step": round(ms * 1e3, 2),
+            "algorithmic_GBps": round(nblk * per_block_bytes / (ms * 1e-3) / 1e9, 1),
+            "note": "state + history of the 6 blocks (179 MB) fit the 256 MB last-level cache"}
+        log("streaming %s: %.1f us per token step" % (name, ms * 1e3))
+    return ex
+
+
+def cpu_baseline(np, si):
+    """The float64 oracle, as it stands, on the host cores: the same forward
+    (conv, then the scan with the gate) on a bounded sample of 2 of the 8
+    batch rows."""
+    import oracle
+    oracle.build(force=False)
+    Bs, L, D, N, W = 2, 2048, 1536, 16, 4
+    p = si.mamba_block(8, L, D, N, W, workload=si.WL_FWDBWD)
+    x = np.ascontiguousarray(p["x"][:Bs], np.float64)
+    f = lambda k: np.ascontiguousarray(p[k][:Bs] if p[k].ndim == 3 else p[k], np.float64)
+    args = {k: f(k) for k in ("dt_raw", "B", "C", "z", "dt_bias", "A_log", "Dskip", "conv_w", "conv_b")}
+    t0 = time.perf_counter()
+    u, _ = oracle.conv1d_causal(x, args["conv_w"], args["conv_b"], want_state=False)
+    oracle.scan_fwd(u, args["dt_raw"], args["A_log"], args["B"], args["C"], dt_bias=args["dt_bias"],
+                    Dskip=args["Dskip"], z=args["z"])
+    dt = time.perf_counter() - t0
+    return {"value": Bs * L * D * N / dt, "unit": "elements/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "forward (conv + scan + gate) of batch rows 0-1 of the 8, L=2048, D=1536, N=16; %.2f s" % dt}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,230 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) S6 selective-scan library.
+ *
+ * The method (pages: "mamba, live", section "what is actually running";
+ * "the s6 cell", section "the recurrence"; TensorViz "Carry context through a
+ * selective state", explorer page and manifest steps "local", "select",
+ * "state", "read"):
+ *
+ *   u      = SiLU(causal_depthwise_conv_W(x))         (optional, fused)
+ *   dt     = softplus(dt_raw + dt_bias)                per (b, t, d)
+ *   A      = -exp(A_log)                               per (d, n)
+ *   h[n]  <- exp(dt*A[n]) * h[n] + coef(dt, A[n]) * B[t, n] * u
+ *            coef = dt                 (SSM_DISC_DELTA_B, the dt*B form)
+ *            coef = expm1(dt*A) / A    (SSM_DISC_ZOH, exact zero-order hold)
+ *   y      = (sum_n C[t, n] * h[n] + Dskip * u) * SiLU(z)   (C reads the
+ *            updated state; the gate only when z is given)
+ *
+ * Conventions shared by every call
+ *  - Layouts are row-major and channel-last:
+ *      x, u, dt_raw, z, y and their gradients       [B, L, D]
+ *      B, C and their gradients                     [B, L, N]  (shared by all channels)
+ *      A_log, dA_log                                [D, N]
+ *      dt_bias, Dskip, conv_b and their gradients   [D]
+ *      conv_w                                       [D, W]  (tap W-1 multiplies the current input)
+ *      h0, hT, dh0, dhT                             [B, D, N]
+ *      conv_state_in / conv_state_out               [B, W-1, D]  (oldest input first)
+ *  - Tensors marked "io" hold SSM_F32 or SSM_BF16 values as chosen by the
+ *    descriptor's io_dtype; every parameter, state and parameter gradient is
+ *    float32.  bf16 results are rounded to nearest, ties to even.
+ *  - Every pointer is a DEVICE pointer, except the descriptor pointers, which
+ *    are host pointers read before the call returns.  The caller owns all
+ *    memory: the library never allocates, frees or keeps a pointer after a
+ *    call returns.  Every tensor must start on a 16-byte boundary.
+ *  - A NULL optional pointer means "absent": dt_bias, Dskip, conv_b read as 0;
+ *    z means "no gate"; h0 and conv_state_in read as zeros; a NULL output is
+ *    not written.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and is asynchronous: nothing synchronises inside a call.  Calls are
+ *    reentrant; concurrent calls on different streams must use different
+ *    workspaces and outputs.
+ *  - Errors: every call returns an ssm_status.  Argument errors are detected
+ *    on the host before any HIP call is made, and then nothing is enqueued.
+ *    SSM_ERR_HIP reports a failed launch; a fault inside a kernel surfaces at
+ *    the caller's next synchronisation.
+ *  - Inputs must be finite.  Outputs may not overlap inputs or each other,
+ *    except the exact in-place pairs named below.
+ */
+#ifndef SSM_AMD_SSM_H
+#define SSM_AMD_SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef int32_t ssm_status;
+#define SSM_OK 0
+#define SSM_ERR_NULL_ARG 1     /* a required pointer is NULL */
+#define SSM_ERR_BAD_SHAPE 2    /* a size is out of range or inconsistent */
+#define SSM_ERR_UNSUPPORTED 3  /* a valid request this build does not implement */
+#define SSM_ERR_WORKSPACE 4    /* workspace NULL or smaller than the queried size */
+#define SSM_ERR_ALIGNMENT 5    /* a tensor does not start on a 16-byte boundary */
+#define SSM_ERR_ALIAS 6        /* buffers overlap in a way the call does not allow */
+#define SSM_ERR_HIP 7          /* a HIP launch failed */
+
+#define SSM_F32 0
+#define SSM_BF16 1
+
+#define SSM_DISC_DELTA_B 0     /* write = dt * B * u ("mamba, live"; "the s6 cell") */
+#define SSM_DISC_ZOH 1         /* write = expm1(dt*A)/A * B * u (TensorViz explorer) */
+
+#define SSM_MAX_DSTATE 64
+#define SSM_MAX_CONV_WIDTH 8
+
+/* Descriptor of a sequence scan (forward or backward). */
+typedef struct ssm_scan_desc {
+    int64_t batch;       /* B >= 1 */
+    int64_t seqlen;      /* L >= 0 */
+    int64_t dim;         /* D >= 1, inner channels */
+    int64_t dstate;      /* N in [1, SSM_MAX_DSTATE] */
+    int32_t conv_width;  /* 0: x already is the scan input u; 1..8: fused causal conv + SiLU */
+    int32_t io_dtype;    /* SSM_F32 or SSM_BF16 */
+    int32_t disc;        /* SSM_DISC_DELTA_B or SSM_DISC_ZOH */
+    int32_t chunk_len;   /* 0: library's choice; > 0: split time into chunks of this
+                            length (two-level scan); -1: never split time */
+} ssm_scan_desc;
+
+/* Descriptor of one streaming step for a stack of independent blocks. */
+typedef struct ssm_step_desc {
+    int64_t nblocks;     /* >= 1; every per-block tensor gains a leading [nblocks] axis */
+    int64_t nstreams;    /* S >= 1 concurrent sequences */
+    int64_t dim;         /* D >= 1 */
+    int64_t dstate;      /* N in [1, SSM_MAX_DSTATE] */
+    int32_t conv_width;  /* 0: x is u; 1..8: causal conv over the carried history + SiLU */
+    int32_t io_dtype;    /* SSM_F32 or SSM_BF16 for x, dt_raw, B, C, z, y */
+    int32_t disc;        /* SSM_DISC_DELTA_B or SSM_DISC_ZOH */
+    int32_t reserved;    /* must be 0 */
+} ssm_step_desc;
+
+/* Descriptor of a causal depthwise convolution. */
+typedef struct ssm_conv_desc {
+    int64_t batch;       /* B >= 1 */
+    int64_t seqlen;      /* L >= 0 */
+    int64_t dim;         /* D >= 1 */
+    int32_t width;       /* W in [1, SSM_MAX_CONV_WIDTH] */
+    int32_t fuse_silu;   /* 1: y = SiLU(conv), 0: y = conv */
+    int32_t io_dtype;    /* SSM_F32 or SSM_BF16 for x and y */
+    int32_t reserved;    /* must be 0 */
+} ssm_conv_desc;
+
+/* Library version (SSM_ABI_VERSION * 100 + minor). */
+int32_t ssm_version(void);
+
+/* Static English text of a status code (never NULL). */
+const char *ssm_status_string(ssm_status status);
+
+/*
+ * conv1d_causal -- causal depthwise convolution, optionally followed by SiLU
+ * ("mamba, live": xc = SiLU(depthwise_conv4(xin)), 4-tap causal, per channel;
+ * TensorViz manifest step "local": left padded, reads the current and W-1
+ * earlier inputs).
+ *   y[b,t,d] = act(b[d] + sum_{k<W} w[d,k] * xt[b, t-(W-1)+k, d])
+ * with xt = x for index >= 0 and the carried history state_in (or 0) before.
+ *   x         io  [B, L, D]     input
+ *   w         f32 [D, W]        taps (required)
+ *   b         f32 [D]           bias, optional
+ *   state_in  f32 [B, W-1, D]   history before x, optional (zeros)
+ *   state_out f32 [B, W-1, D]   the last W-1 inputs after x, optional; must not
+ *                               overlap state_in (SSM_ERR_ALIAS)
+ *   y         io  [B, L, D]     output (required when L > 0)
+ */
+ssm_status conv1d_causal(const ssm_conv_desc *desc, const void *x, const float *w,
+                         const float *b, const float *state_in, float *state_out,
+                         void *y, void *stream);
+
+/* Bytes of device workspace ssm_scan_fwd needs for this descriptor (0 when
+ * time is not split). */
+ssm_status ssm_scan_fwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes);
+
+/*
+ * ssm_scan_fwd -- the selective scan over a whole sequence (the recurrence
+ * above, run for t = 0 .. L-1 from h0).  Long sequences with little batch and
+ * channel parallelism are split in time into chunks whose end states are
+ * combined by the associative rule (P1, W1) then (P2, W2) = (P1*P2, P2*W1 + W2)
+ * and then re-scanned from their exact starting states; the result equals the
+ * sequential recurrence up to rounding.
+ *   x              io  [B, L, D]   u, or the conv input when conv_width > 0 (required)
+ *   dt_raw         io  [B, L, D]   required
+ *   dt_bias        f32 [D]         optional
+ *   A_log          f32 [D, N]      required
+ *   B, C           io  [B, L, N]   required
+ *   Dskip          f32 [D]         optional
+ *   z              io  [B, L, D]   gate input, optional
+ *   conv_w         f32 [D, W]      required when conv_width > 0, else ignored
+ *   conv_b         f32 [D]         optional
+ *   conv_state_in  f32 [B, W-1, D] optional
+ *   conv_state_out f32 [B, W-1, D] optional (may be exactly conv_state_in)
+ *   h0             f32 [B, D, N]   optional
+ *   hT             f32 [B, D, N]   optional (may be exactly h0)
+ *   y              io  [B, L, D]   required when L > 0
+ *   workspace      device memory of ssm_scan_fwd_workspace_size bytes (may be
+ *                  NULL when that size is 0)
+ */
+ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt_raw,
+                        const float *dt_bias, const float *A_log, const void *B,
+                        const void *C, const float *Dskip, const void *z,
+                        const float *conv_w, const float *conv_b,
+                        const float *conv_state_in, float *conv_state_out,
+                        const float *h0, float *hT, void *y,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of device workspace ssm_scan_bwd needs for this descriptor. */
+ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes);
+
+/*
+ * ssm_scan_bwd -- gradients of ssm_scan_fwd (conv_width must be 0: u is the
+ * scan input) for the loss sum(y * dy) + sum(hT * dhT).  The pages state that
+ * the selection maps receive gradients (TensorViz explorer, numerical checks)
+ * but give no backward; this is the reverse-mode adjoint of the recurrence:
+ * with g = dLoss/dh_t, g_{t-1} = exp(dt_t*A) * g_t + C_{t-1} * dyv_{t-1}.
+ *   u, dt_raw, B, C, z, dy    io  as in ssm_scan_fwd (dy [B, L, D] required)
+ *   dt_bias, A_log, Dskip, h0 f32 as in ssm_scan_fwd
+ *   dhT        f32 [B, D, N]  optional upstream gradient of hT
+ *   du, d_dt_raw, dz   io [B, L, D]  optional outputs (dz needs z)
+ *   dB, dC             io [B, L, N]  optional outputs (summed over channels)
+ *   d_dt_bias, dDskip  f32 [D]       optional outputs (summed over batch and time)
+ *   dA_log             f32 [D, N]    optional output (summed over batch and time)
+ *   dh0                f32 [B, D, N] optional output
+ *   workspace  device memory of ssm_scan_bwd_workspace_size bytes (required)
+ */
+ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void *dt_raw,
+                        const float *dt_bias, const float *A_log, const void *B,
+                        const void *C, const float *Dskip, const void *z,
+                        const float *h0, const void *dy, const float *dhT,
+                        void *du, void *d_dt_raw, float *d_dt_bias, float *dA_log,
+                        void *dB, void *dC, float *dDskip, void *dz, float *dh0,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ssm_step -- one token of batched streaming decode ("mamba, live": one token
+ * in, one token out, constant work; the whole memory is h plus a (W-1)-token
+ * conv history per channel).  For every block k, stream s and channel d:
+ *   u = SiLU(conv_b + sum_{j<W-1} conv_w[j] * hist[j] + conv_w[W-1] * x)   (conv_width > 0)
+ *   hist <- [hist[1..W-2], x]
+ *   then one recurrence step of the scan with u, updating h in place.
+ * Tensors (each with a leading [nblocks] axis, block-major):
+ *   h          f32 [S, D, N]   state, in/out (required)
+ *   conv_state f32 [S, W-1, D] history, in/out (required when conv_width > 1)
+ *   x, dt_raw  io  [S, D]      required
+ *   B, C       io  [S, N]      required
+ *   z          io  [S, D]      optional gate input
+ *   conv_w     f32 [D, W]      required when conv_width > 0
+ *   conv_b, dt_bias, Dskip  f32 [D]  optional
+ *   A_log      f32 [D, N]      required
+ *   y          io  [S, D]      output (required)
+ */
+ssm_status ssm_step(const ssm_step_desc *desc, float *h, float *conv_state, const void *x,
+                    const void *dt_raw, const void *B, const void *C, const void *z,
+                    const float *conv_w, const float *conv_b, const float *dt_bias,
+                    const float *A_log, const float *Dskip, void *y, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_AMD_SSM_H */

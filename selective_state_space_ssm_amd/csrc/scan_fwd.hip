@@ -1,0 +1,587 @@
+// scan_fwd.hip -- forward selective scan for gfx950.
+//
+// The recurrence (pages: "mamba, live", section "what is actually running";
+// "the s6 cell", section "the recurrence"; TensorViz explorer, exact ZOH):
+//   dt = softplus(dt_raw + dt_bias),  a = 2^(dt * A * log2 e),  A = -exp(A_log)
+//   h  = a * h + coef * B * u,  y = (<h, C> + Dskip * u) * SiLU(z)
+//
+// Work decomposition.  One 64-lane wavefront owns 16 channels of one batch
+// row and one time chunk.  Tokens are processed in tiles of 32:
+//  - fetch: the next tile's x, dt_raw, z and its B, C rows are loaded into
+//    registers while the current tile is scanned (one tile of prefetch);
+//  - stage: the raw conv input goes to LDS (with 8 rows of history for the
+//    causal window) and B, C rows go to LDS;
+//  - transform: each lane takes one channel and 8 consecutive tokens and
+//    computes, once per (token, channel), the conv + SiLU, dt = softplus,
+//    dt*u, the gate SiLU(z) and Dskip*u into an LDS record;
+//  - scan: four lanes own a channel, lane q keeping states q*SPL ..
+//    q*SPL+SPL-1 in registers; per token a lane reads the channel's record
+//    and its B, C values from LDS, updates its states with one exp2 each,
+//    and the readout <h, C> is finished with two DPP adds in the lane quad.
+// The recurrence itself stays strictly sequential in time inside a chunk.
+//
+// Long sequences with few independent channels are split in time (two-level
+// scan): MODE_LOCAL scans every chunk from a zero state and records its end
+// state W_k and sum of dt S_k; carry_kernel walks the chunks in order with
+// H_{k+1} = 2^(A*log2e*S_k) * H_k + W_k, the associative composition of the
+// chunk's affine maps; MODE_FINAL then re-scans every chunk from its exact
+// starting state H_k and writes y.  Time order inside a chunk is untouched.
+#include <algorithm>
+
+#include "launch.hpp"
+#include "ssm_device.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kLPC = 4;             // lanes per channel
+constexpr int kCPW = 64 / kLPC;     // channels per wavefront
+enum { MODE_FINAL = 0, MODE_LOCAL = 1 };
+enum { DISC_DB = 0, DISC_ZOH = 1 };
+
+struct FwdParams {
+    const void *x, *dt;
+    const float *dt_bias, *A_log;
+    const void *Bm, *Cm;
+    const float *Dskip;
+    const void *z;
+    const float *conv_w, *conv_b;
+    const float *conv_hist;        // history for t < 0: [B, W-1, D]
+    float *conv_state_out;
+    const float *init;             // starting states, nullable
+    int64_t init_bstride, init_kstride;
+    float *hT;
+    void *y;
+    float *agg_h;                  // MODE_LOCAL: [B, K, D, N] end states
+    float *agg_s;                  // MODE_LOCAL: [B, K, D] sums of dt
+    int64_t B, L, D, N;
+    int W;
+    int64_t chunk;
+    int K;                         // chunks along time (array stride)
+    int Kgrid;                     // chunks covered by this launch (0 .. Kgrid-1)
+    int groups;                    // channel groups of kCPW
+};
+
+constexpr int kTile = 32;           // tokens staged per tile
+constexpr int kXS = 17;             // padded row stride of the conv staging rows (LDS banks)
+
+// Raw loads of one tile, held in registers while the previous tile is
+// scanned.  Transform role: lane -> channel tc = lane & 15 and rows
+// rg*8 .. rg*8+7 with rg = lane >> 4.  B/C: 4-wide chunks (vector path) or
+// single elements (guarded path) dealt round-robin over the lanes.
+template <int NP>
+struct RawTile {
+    // enough for either layout: whole 4-wide chunks, or single elements
+    static constexpr int BCV = 4 * ((kTile * NP / 4 + 63) / 64);
+    static constexpr int BCS = (kTile * NP + 63) / 64;
+    static constexpr int BCE = BCV > BCS ? BCV : BCS;
+    float x[8], dt[8], z[8];
+    float b[BCE], c[BCE];
+};
+
+template <typename IOT, int NP, bool WANT_C>
+__device__ __forceinline__ void load_raw(RawTile<NP> &r, const IOT *X, const IOT *DT, const IOT *Z,
+                                         const IOT *Bp, const IOT *Cp, int64_t b, int64_t L, int64_t D,
+                                         int64_t N, int64_t ts, int nv, int64_t tdc, bool tvalid, int rg,
+                                         int lane, bool vecBC) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = rg * 8 + i;
+        const bool v = tvalid && row < nv;
+        const int64_t e = (b * L + ts + row) * D + tdc;
+        r.x[i] = v ? to_f32(X[e]) : 0.0f;
+        r.dt[i] = v ? to_f32(DT[e]) : 0.0f;
+        r.z[i] = (v && Z != nullptr) ? to_f32(Z[e]) : 0.0f;
+    }
+    constexpr int BCE = RawTile<NP>::BCS;
+    if (vecBC) {
+        // chunk f = lane + 64*i holds row f / (NP/4), states 4*(f % (NP/4)) .. +3
+        constexpr int NCH = kTile * NP / 4;
+#pragma unroll
+        for (int i = 0; i < RawTile<NP>::BCV / 4; ++i) {
+            const int f = lane + 64 * i;
+            const int row = f / (NP / 4), c4 = (f % (NP / 4)) * 4;
+            const bool v = f < NCH && row < nv;
+            float tb[4] = {0.f, 0.f, 0.f, 0.f}, tc[4] = {0.f, 0.f, 0.f, 0.f};
+            if (v) {
+                const int64_t o = (b * L + ts + row) * N + c4;
+                load_k<4>(Bp + o, tb, true);
+                if constexpr (WANT_C) load_k<4>(Cp + o, tc, true);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                r.b[4 * i + k] = tb[k];
+                r.c[4 * i + k] = tc[k];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BCE; ++i) {
+            const int e = lane + 64 * i;
+            const int row = e / NP, n = e % NP;
+            const bool v = e < kTile * NP && row < nv && n < N;
+            const int64_t o = (b * L + ts + row) * N + n;
+            r.b[i] = v ? to_f32(Bp[o]) : 0.0f;
+            r.c[i] = (WANT_C && v) ? to_f32(Cp[o]) : 0.0f;
+        }
+    }
+}
+
+template <int NP, bool WANT_C>
+__device__ __forceinline__ void store_bc(const RawTile<NP> &r, float *sB, float *sC, int lane, bool vecBC) {
+    constexpr int BCE = RawTile<NP>::BCS;
+    if (vecBC) {
+        constexpr int NCH = kTile * NP / 4;
+#pragma unroll
+        for (int i = 0; i < RawTile<NP>::BCV / 4; ++i) {
+            const int f = lane + 64 * i;
+            if (f < NCH) {
+                const int row = f / (NP / 4), c4 = (f % (NP / 4)) * 4;
+                *reinterpret_cast<float4 *>(sB + row * NP + c4) =
+                    make_float4(r.b[4 * i], r.b[4 * i + 1], r.b[4 * i + 2], r.b[4 * i + 3]);
+                if constexpr (WANT_C)
+                    *reinterpret_cast<float4 *>(sC + row * NP + c4) =
+                        make_float4(r.c[4 * i], r.c[4 * i + 1], r.c[4 * i + 2], r.c[4 * i + 3]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < BCE; ++i) {
+            const int e = lane + 64 * i;
+            if (e < kTile * NP) {
+                sB[e] = r.b[i];
+                if constexpr (WANT_C) sC[e] = r.c[i];
+            }
+        }
+    }
+}
+
+template <int K>
+__device__ __forceinline__ void lds_read_k(const float *p, float (&o)[K]) {
+    if constexpr (K % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < K; i += 4) {
+            const float4 v = *reinterpret_cast<const float4 *>(p + i);
+            o[i] = v.x; o[i + 1] = v.y; o[i + 2] = v.z; o[i + 3] = v.w;
+        }
+    } else if constexpr (K == 2) {
+        const float2 v = *reinterpret_cast<const float2 *>(p);
+        o[0] = v.x; o[1] = v.y;
+    } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i) o[i] = p[i];
+    }
+}
+
+template <typename IOT, int SPL, int DISC, bool CONV, int MODE>
+__global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
+    constexpr int T = kTile;
+    constexpr int NP = kLPC * SPL;
+    constexpr bool FINAL = MODE == MODE_FINAL;
+    __shared__ float s_x[CONV ? (T + 8) * kXS : 1];
+    __shared__ float4 s_pk[T][kCPW];      // per (token, channel): {dt, dt*u or u, gate, Dskip*u}
+    __shared__ __align__(16) float s_B[T * NP];
+    __shared__ __align__(16) float s_C[FINAL ? T * NP : 1];
+    __shared__ float s_y[FINAL ? T : 1][kXS];   // gated outputs of the tile
+
+    const IOT *X = static_cast<const IOT *>(p.x);
+    const IOT *DT = static_cast<const IOT *>(p.dt);
+    const IOT *Bp = static_cast<const IOT *>(p.Bm);
+    const IOT *Cp = static_cast<const IOT *>(p.Cm);
+    const IOT *Z = FINAL ? static_cast<const IOT *>(p.z) : nullptr;
+    IOT *Y = static_cast<IOT *>(p.y);
+
+    const int lane = threadIdx.x;
+    const int64_t bid = blockIdx.x;
+    const int64_t g = bid % p.groups;
+    const int64_t rest = bid / p.groups;
+    const int k = (int)(rest % p.Kgrid);
+    const int64_t b = rest / p.Kgrid;
+    const int64_t N = p.N, D = p.D, L = p.L;
+    const int64_t d0 = g * kCPW;
+    const int64_t t0 = (int64_t)k * p.chunk;
+    const int64_t t1 = min(L, t0 + p.chunk);
+    const int ntiles = (int)((t1 - t0 + T - 1) / T);
+
+    // scan role: four lanes per channel, SPL states each
+    const int ch = lane / kLPC, q = lane % kLPC;
+    const int64_t d = d0 + ch;
+    const bool dvalid = d < D;
+    const int64_t dc = dvalid ? d : (D - 1);
+    const int n0 = q * SPL;
+    const int nvalid = max(0, min(SPL, (int)(N - n0)));
+    const bool vecN = (N % 4) == 0;
+    // transform role: one channel, eight consecutive rows of the tile
+    const int tc = lane & 15, rg = lane >> 4;
+    const int64_t td = d0 + tc;
+    const bool tvalid = td < D;
+    const int64_t tdc = tvalid ? td : (D - 1);
+    const bool vecBC = (N == NP) && (N % 4 == 0);
+
+    float A2[SPL], An[SPL], Ainv[SPL], h[SPL];
+#pragma unroll
+    for (int j = 0; j < SPL; ++j) {
+        const bool v = j < nvalid;
+        const float A = neg_exp_f(v ? p.A_log[dc * N + n0 + j] : 0.0f);
+        A2[j] = v ? A * kLog2e : 0.0f;
+        An[j] = A;
+        Ainv[j] = 1.0f / A;
+        h[j] = 0.0f;
+    }
+    if (p.init != nullptr && nvalid > 0)
+        load_k_guard<SPL>(p.init + b * p.init_bstride + (int64_t)k * p.init_kstride + dc * N + n0, h, nvalid,
+                          vecN);
+
+    const float dtb = p.dt_bias ? p.dt_bias[tdc] : 0.0f;
+    const float Dd = p.Dskip ? p.Dskip[tdc] : 0.0f;
+    float wk[8], cb = 0.0f;
+    const int W = p.W;
+    if constexpr (CONV) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int kk = i - (8 - W);
+            wk[i] = (kk >= 0) ? p.conv_w[tdc * W + kk] : 0.0f;
+        }
+        cb = p.conv_b ? p.conv_b[tdc] : 0.0f;
+    }
+    // conv input before the chunk: x for t >= 0, else the carried history
+    auto x_before = [&](int64_t tt) -> float {
+        if (tt >= 0) return to_f32(X[(b * L + tt) * D + tdc]);
+        if (p.conv_hist != nullptr && tt >= -(int64_t)(W - 1))
+            return p.conv_hist[(b * (W - 1) + (W - 1) + tt) * D + tdc];
+        return 0.0f;
+    };
+
+    RawTile<NP> raw;
+    float xh[8];          // raw conv input of the previous tile's last 8 rows (rg == 3 lanes)
+
+    // Per-(token, channel) quantities, computed once per tile element.
+    auto transform = [&](int nv) {
+        float uu[8];
+        if constexpr (CONV) {
+            float win[15];
+#pragma unroll
+            for (int i = 0; i < 15; ++i) win[i] = s_x[(rg * 8 + 1 + i) * kXS + tc];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float acc = cb;
+#pragma unroll
+                for (int kk = 0; kk < 8; ++kk) acc = fmaf(wk[kk], win[i + kk], acc);
+                uu[i] = silu_f(acc);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) uu[i] = raw.x[i];
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = rg * 8 + i;
+            if (row < nv) {
+                const float dl = softplus_f(raw.dt[i] + dtb);
+                float4 v;
+                v.x = dl;
+                v.y = (DISC == DISC_DB) ? dl * uu[i] : uu[i];
+                if constexpr (FINAL) {
+                    v.z = (Z != nullptr) ? silu_f(raw.z[i]) : 1.0f;
+                    v.w = Dd * uu[i];
+                } else {
+                    v.z = 0.0f;
+                    v.w = 0.0f;
+                }
+                s_pk[row][tc] = v;
+            }
+        }
+    };
+
+    auto stage = [&](int it) {
+        const int64_t ts = t0 + (int64_t)it * T;
+        const int nv = (int)min((int64_t)T, t1 - ts);
+        if constexpr (CONV) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s_x[(8 + rg * 8 + i) * kXS + tc] = raw.x[i];
+        }
+        store_bc<NP, FINAL>(raw, s_B, s_C, lane, vecBC);
+        __syncthreads();
+        transform(nv);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xh[i] = raw.x[i];
+        __syncthreads();
+    };
+
+    auto fetch = [&](int it) {
+        const int64_t ts = t0 + (int64_t)it * T;
+        const int nv = (int)min((int64_t)T, t1 - ts);
+        load_raw<IOT, NP, FINAL>(raw, X, DT, Z, Bp, Cp, b, L, D, N, ts, nv, tdc, tvalid, rg, lane, vecBC);
+    };
+
+    float ssum = 0.0f;
+    if (ntiles > 0) {
+        fetch(0);
+        if constexpr (CONV) {
+            if (rg == 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s_x[i * kXS + tc] = x_before(t0 - 8 + i);
+            }
+        }
+        stage(0);
+        if (ntiles > 1) fetch(1);
+    }
+    auto scan_step = [&](int t) {
+        const float4 pk = s_pk[t][ch];
+        float Bq[SPL], Cq[SPL];
+        lds_read_k<SPL>(s_B + t * NP + n0, Bq);
+        if constexpr (FINAL) lds_read_k<SPL>(s_C + t * NP + n0, Cq);
+        const float dl = pk.x;
+        float yacc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < SPL; ++j) {
+            const float a = hw_exp2(dl * A2[j]);
+            float w;
+            if constexpr (DISC == DISC_DB)
+                w = pk.y * Bq[j];
+            else
+                w = expm1f(dl * An[j]) * Ainv[j] * Bq[j] * pk.y;
+            h[j] = fmaf(a, h[j], w);
+            if constexpr (FINAL) yacc = fmaf(Cq[j], h[j], yacc);
+        }
+        if constexpr (FINAL) {
+            // every lane of the quad holds the sum; all write the same value
+            s_y[t][ch] = (group_sum<kLPC>(yacc) + pk.w) * pk.z;
+        } else {
+            ssum += dl;
+        }
+    };
+
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t ts = t0 + (int64_t)it * T;
+        const int nv = (int)min((int64_t)T, t1 - ts);
+        if (nv == T) {
+            // full tile: straight-line code, LDS reads hoisted ahead of the math
+#pragma unroll
+            for (int t = 0; t < T; ++t) scan_step(t);
+        } else {
+            for (int t = 0; t < nv; ++t) scan_step(t);
+        }
+        __syncthreads();
+        if constexpr (FINAL) {
+            if (tvalid) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int row = rg * 8 + i;
+                    if (row < nv) store_io(Y + (b * L + ts + row) * D + td, s_y[row][tc]);
+                }
+            }
+        }
+        if (it + 1 < ntiles) {
+            if constexpr (CONV) {
+                if (rg == 3) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) s_x[i * kXS + tc] = xh[i];
+                }
+            }
+            stage(it + 1);
+            if (it + 2 < ntiles) fetch(it + 2);
+        }
+    }
+
+    if constexpr (FINAL) {
+        if (k == p.K - 1) {
+            if (dvalid && p.hT != nullptr && nvalid > 0)
+                store_k<SPL>(p.hT + (b * D + d) * N + n0, h, nvalid, vecN);
+            if constexpr (CONV) {
+                if (p.conv_state_out != nullptr && rg == 0 && tvalid) {
+                    // the last W-1 conv inputs: staged rows of the last tile, or
+                    // the carried history when the sequence is empty
+                    const int64_t tl = t0 + (int64_t)max(ntiles - 1, 0) * T;
+                    for (int j = 0; j < W - 1; ++j) {
+                        const int64_t tt = L - (W - 1) + j;
+                        const float v = (ntiles > 0) ? s_x[(int)(tt - (tl - 8)) * kXS + tc] : x_before(tt);
+                        p.conv_state_out[(b * (W - 1) + j) * D + td] = v;
+                    }
+                }
+            }
+        }
+    } else {
+        if (dvalid) {
+            const int64_t o = (b * p.K + k) * D + d;
+            if (nvalid > 0) store_k<SPL>(p.agg_h + o * N + n0, h, nvalid, vecN);
+            if (q == 0) p.agg_s[o] = ssum;
+        }
+    }
+}
+
+// Walks the chunks of every (b, d, n) in time order, replacing each chunk's
+// local end state by the exact state at the chunk's start.  Also copies the
+// incoming conv history so that MODE_FINAL never reads a buffer the same
+// launch writes.
+__global__ __launch_bounds__(256) void carry_kernel(const float *A_log, const float *h0, float *agg_h,
+                                                    const float *agg_s, int64_t B, int64_t D,
+                                                    int64_t N, int K, const float *conv_in,
+                                                    float *conv_copy, int64_t conv_count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = B * D * N;
+    if (i < total) {
+        const int64_t n = i % N, d = (i / N) % D, b = i / (N * D);
+        const float A2 = neg_exp_f(A_log[d * N + n]) * kLog2e;
+        float H = h0 ? h0[i] : 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int64_t o = ((b * K + k) * D + d) * N + n;
+            const float Wk = agg_h[o];
+            agg_h[o] = H;
+            if (k + 1 < K) H = fmaf(hw_exp2(A2 * agg_s[(b * K + k) * D + d]), H, Wk);
+        }
+    }
+    if (conv_in != nullptr)
+        for (int64_t j = i; j < conv_count; j += (int64_t)gridDim.x * blockDim.x) conv_copy[j] = conv_in[j];
+}
+
+template <typename IOT, int SPL, int DISC, bool CONV, int MODE>
+hipError_t launch_one(const FwdParams &p, hipStream_t s) {
+    const int64_t blocks = (int64_t)p.groups * p.Kgrid * p.B;
+    if (blocks <= 0) return hipSuccess;
+    hipLaunchKernelGGL((scan_fwd_kernel<IOT, SPL, DISC, CONV, MODE>),
+                       dim3((unsigned)blocks), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+template <typename IOT, int SPL>
+hipError_t dispatch_mode(const FwdParams &p, int disc, bool conv, int mode, hipStream_t s) {
+#define SSM_FWD_CASE(DI, CV, MO)                                                   \
+    if (disc == DI && conv == CV && mode == MO) return launch_one<IOT, SPL, DI, CV, MO>(p, s);
+    SSM_FWD_CASE(DISC_DB, false, MODE_FINAL)
+    SSM_FWD_CASE(DISC_DB, true, MODE_FINAL)
+    SSM_FWD_CASE(DISC_DB, false, MODE_LOCAL)
+    SSM_FWD_CASE(DISC_DB, true, MODE_LOCAL)
+    SSM_FWD_CASE(DISC_ZOH, false, MODE_FINAL)
+    SSM_FWD_CASE(DISC_ZOH, true, MODE_FINAL)
+    SSM_FWD_CASE(DISC_ZOH, false, MODE_LOCAL)
+    SSM_FWD_CASE(DISC_ZOH, true, MODE_LOCAL)
+#undef SSM_FWD_CASE
+    return hipErrorInvalidValue;
+}
+
+template <typename IOT>
+hipError_t dispatch_spl(const FwdParams &p, int disc, bool conv, int mode, hipStream_t s) {
+    if (p.N <= 4) return dispatch_mode<IOT, 1>(p, disc, conv, mode, s);
+    if (p.N <= 8) return dispatch_mode<IOT, 2>(p, disc, conv, mode, s);
+    if (p.N <= 16) return dispatch_mode<IOT, 4>(p, disc, conv, mode, s);
+    if (p.N <= 32) return dispatch_mode<IOT, 8>(p, disc, conv, mode, s);
+    return dispatch_mode<IOT, 16>(p, disc, conv, mode, s);
+}
+
+hipError_t dispatch(const FwdParams &p, int bf16, int disc, bool conv, int mode, hipStream_t s) {
+    if (bf16) return dispatch_spl<bf16_t>(p, disc, conv, mode, s);
+    return dispatch_spl<float>(p, disc, conv, mode, s);
+}
+
+struct FwdWs {
+    float *agg_h, *agg_s, *conv_copy;
+};
+
+FwdWs carve(void *ws, int64_t B, int64_t D, int64_t N, int W, int K) {
+    char *base = static_cast<char *>(ws);
+    FwdWs r;
+    r.agg_h = reinterpret_cast<float *>(base);
+    base += ws_align(sizeof(float) * (size_t)(B * K * D * N));
+    r.agg_s = reinterpret_cast<float *>(base);
+    base += ws_align(sizeof(float) * (size_t)(B * K * D));
+    r.conv_copy = reinterpret_cast<float *>(base);
+    (void)W;
+    return r;
+}
+
+int64_t num_chunks(int64_t L, int64_t chunk) {
+    if (L <= 0 || chunk >= L) return 1;
+    return (L + chunk - 1) / chunk;
+}
+
+}  // namespace
+
+int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N) {
+    (void)N;
+    const int64_t waves = B * ((D + kCPW - 1) / kCPW);
+    if (waves >= 640 || L <= 512) return L > 0 ? L : 1;
+    int64_t K = (2048 + waves - 1) / waves;
+    K = std::min<int64_t>(K, (L + 255) / 256);
+    if (K <= 1) return L;
+    int64_t chunk = (L + K - 1) / K;
+    chunk = (chunk + 7) / 8 * 8;
+    return chunk;
+}
+
+size_t scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int W, int64_t chunk_len) {
+    const int64_t K = num_chunks(L, chunk_len);
+    if (K <= 1) return 0;
+    return ws_align(sizeof(float) * (size_t)(B * K * D * N)) + ws_align(sizeof(float) * (size_t)(B * K * D)) +
+           ws_align(sizeof(float) * (size_t)(B * (W > 1 ? W - 1 : 0) * D));
+}
+
+hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s) {
+    FwdParams p{};
+    p.x = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
+    p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z;
+    p.conv_w = a.conv_w; p.conv_b = a.conv_b;
+    p.conv_state_out = a.conv_state_out;
+    p.hT = a.hT; p.y = a.y;
+    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N; p.W = a.W;
+    p.groups = (int)((a.D + kCPW - 1) / kCPW);
+    const bool conv = a.W > 0;
+    const int64_t K = num_chunks(a.L, a.chunk_len);
+    if (K <= 1) {
+        p.chunk = a.L > 0 ? a.L : 1;
+        p.K = 1; p.Kgrid = 1;
+        p.init = a.h0; p.init_bstride = a.D * a.N; p.init_kstride = 0;
+        p.conv_hist = a.conv_state_in;
+        return dispatch(p, a.bf16, a.disc, conv, MODE_FINAL, s);
+    }
+    FwdWs w = carve(a.ws, a.B, a.D, a.N, a.W, (int)K);
+    p.chunk = a.chunk_len;
+    p.K = (int)K;
+    p.agg_h = w.agg_h; p.agg_s = w.agg_s;
+    // level 1: local scans of chunks 0 .. K-2 (the last chunk's summary is unused)
+    p.Kgrid = (int)K - 1;
+    p.init = nullptr; p.init_bstride = 0; p.init_kstride = 0;
+    p.conv_hist = a.conv_state_in;
+    hipError_t e = dispatch(p, a.bf16, a.disc, conv, MODE_LOCAL, s);
+    if (e != hipSuccess) return e;
+    // level 2: carries across chunks
+    const int64_t total = a.B * a.D * a.N;
+    const int64_t conv_count = (conv && a.conv_state_in && a.W > 1) ? a.B * (a.W - 1) * a.D : 0;
+    const int64_t threads = std::max(total, conv_count);
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a.A_log,
+                       a.h0, w.agg_h, w.agg_s, a.B, a.D, a.N, (int)K,
+                       conv_count ? a.conv_state_in : nullptr, w.conv_copy, conv_count);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // fix-up: every chunk re-scanned from its exact starting state
+    p.Kgrid = (int)K;
+    p.init = w.agg_h; p.init_bstride = K * a.D * a.N; p.init_kstride = a.D * a.N;
+    p.conv_hist = conv_count ? w.conv_copy : nullptr;
+    return dispatch(p, a.bf16, a.disc, conv, MODE_FINAL, s);
+}
+
+hipError_t launch_scan_checkpoints(const ScanFwdArgs &a, int64_t chunk, float *ckpt, float *agg_s,
+                                   hipStream_t s) {
+    // States at the start of every chunk of `chunk` tokens: local scans of
+    // chunks 0 .. K-2, then the carry walk writes the exact starting states.
+    FwdParams p{};
+    p.x = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
+    p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip;
+    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N; p.W = 0;
+    p.groups = (int)((a.D + kCPW - 1) / kCPW);
+    const int64_t K = num_chunks(a.L, chunk);
+    p.chunk = chunk;
+    p.K = (int)K;
+    p.agg_h = ckpt; p.agg_s = agg_s;
+    if (K > 1) {
+        p.Kgrid = (int)K - 1;
+        hipError_t e = dispatch(p, a.bf16, a.disc, false, MODE_LOCAL, s);
+        if (e != hipSuccess) return e;
+    }
+    const int64_t total = a.B * a.D * a.N;
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.A_log,
+                       a.h0, ckpt, agg_s, a.B, a.D, a.N, (int)K, nullptr, nullptr, (int64_t)0);
+    return hipGetLastError();
+}
+
+}  // namespace ssm

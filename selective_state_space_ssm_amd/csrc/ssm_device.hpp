@@ -1,0 +1,179 @@
+// ssm_device.hpp -- device helpers shared by the gfx950 kernels of the
+// selective-scan library: I/O conversion, the per-token elementwise math,
+// and in-register wavefront reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+typedef uint16_t bf16_t;
+
+// widest causal conv the kernels carry in registers
+#define SSM_MAX_CONV_WIDTH_DEV 8
+
+// ---------------------------------------------------------------- I/O types
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+__device__ __forceinline__ void store_io(float *p, float v) { *p = v; }
+// float -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ void store_io(bf16_t *p, float v) {
+    uint32_t b = __float_as_uint(v);
+    uint16_t r;
+    if ((b & 0x7fffffffu) > 0x7f800000u)
+        r = (uint16_t)((b >> 16) | 0x40u);
+    else
+        r = (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
+    *p = r;
+}
+
+// Load K consecutive io values into floats.  `vec` says the address is
+// aligned to the full vector (K*sizeof(T) bytes, capped at 16).
+template <int K>
+__device__ __forceinline__ void load_k(const float *p, float (&o)[K], bool vec) {
+    if constexpr (K % 4 == 0) {
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < K; i += 4) {
+                float4 v = *reinterpret_cast<const float4 *>(p + i);
+                o[i] = v.x; o[i + 1] = v.y; o[i + 2] = v.z; o[i + 3] = v.w;
+            }
+            return;
+        }
+    } else if constexpr (K == 2) {
+        if (vec) {
+            float2 v = *reinterpret_cast<const float2 *>(p);
+            o[0] = v.x; o[1] = v.y;
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) o[i] = p[i];
+}
+
+template <int K>
+__device__ __forceinline__ void load_k(const bf16_t *p, float (&o)[K], bool vec) {
+    if constexpr (K % 4 == 0) {
+        if (vec) {
+#pragma unroll
+            for (int i = 0; i < K; i += 4) {
+                uint2 v = *reinterpret_cast<const uint2 *>(p + i);
+                o[i] = __uint_as_float(v.x << 16);
+                o[i + 1] = __uint_as_float(v.x & 0xffff0000u);
+                o[i + 2] = __uint_as_float(v.y << 16);
+                o[i + 3] = __uint_as_float(v.y & 0xffff0000u);
+            }
+            return;
+        }
+    } else if constexpr (K == 2) {
+        if (vec) {
+            uint32_t v = *reinterpret_cast<const uint32_t *>(p);
+            o[0] = __uint_as_float(v << 16);
+            o[1] = __uint_as_float(v & 0xffff0000u);
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) o[i] = to_f32(p[i]);
+}
+
+// Guarded load of K values of which only the first `valid` exist (rest 0).
+template <int K, typename T>
+__device__ __forceinline__ void load_k_guard(const T *p, float (&o)[K], int valid, bool vec) {
+    if (valid >= K) {
+        load_k<K>(p, o, vec);
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) o[i] = (i < valid) ? to_f32(p[i]) : 0.0f;
+}
+
+template <int K>
+__device__ __forceinline__ void store_k(float *p, const float (&v)[K], int valid, bool vec) {
+    if constexpr (K % 4 == 0) {
+        if (valid >= K && vec) {
+#pragma unroll
+            for (int i = 0; i < K; i += 4)
+                *reinterpret_cast<float4 *>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        if (i < valid) p[i] = v[i];
+}
+
+// ------------------------------------------------------------ fast math
+// Hardware transcendentals (v_exp_f32 = 2^x, v_log_f32 = log2, v_rcp_f32).
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float hw_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float hw_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// softplus(r) = log(1 + e^r) = max(r, 0) + log1p(e^-|r|).  log1p(e) for
+// e in (0, 1] uses the identity log1p(e) = e * log(1+e) / ((1+e) - 1), which
+// cancels the rounding of 1+e (D. Goldberg, "What every computer scientist
+// should know about floating-point arithmetic", 1991, Theorem 4).
+__device__ __forceinline__ float softplus_f(float r) {
+    float e = hw_exp2(-fabsf(r) * kLog2e);
+    float u = 1.0f + e;
+    float l = (u == 1.0f) ? e : e * (hw_log2(u) * kLn2) * hw_rcp(u - 1.0f);
+    return fmaxf(r, 0.0f) + l;
+}
+
+// A = -exp(A_log) through the hardware 2^x (every kernel uses this same
+// formula, so the sequence, streaming and backward kernels agree bit for bit
+// on the decay; relative error ~3e-7 for |A_log| < 4).
+__device__ __forceinline__ float neg_exp_f(float a_log) { return -hw_exp2(a_log * kLog2e); }
+
+// logistic sigmoid and SiLU
+__device__ __forceinline__ float sigmoid_f(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
+__device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
+
+// ------------------------------------------------------------ DPP reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+constexpr int kDppQuadSwap1 = 0xB1;    // quad_perm [1,0,3,2]
+constexpr int kDppQuadSwap2 = 0x4E;    // quad_perm [2,3,0,1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowShr4 = 0x114;
+constexpr int kDppRowShr8 = 0x118;
+
+// Sum over each aligned group of G consecutive lanes (G in 1,2,4,8,16); every
+// lane of the group receives the sum.  All 64 lanes must be active.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(G == 1 || G == 2 || G == 4 || G == 8 || G == 16, "group size");
+    if constexpr (G >= 2) v += dpp_f<kDppQuadSwap1>(v);
+    if constexpr (G >= 4) v += dpp_f<kDppQuadSwap2>(v);
+    if constexpr (G >= 8) v += dpp_f<kDppRowHalfMirror>(v);
+    if constexpr (G >= 16) v += dpp_f<kDppRowMirror>(v);
+    return v;
+}
+
+// Within each 16-lane row, lanes 12..15 receive the sum over lanes
+// {p, p-4, p-8, p-12} (the four lanes of the row with the same p mod 4).
+// All 64 lanes must be active.
+__device__ __forceinline__ float row_stride4_sum(float v) {
+    v += dpp_f<kDppRowShr4>(v);
+    v += dpp_f<kDppRowShr8>(v);
+    return v;
+}
+
+// Map a linear block index so that blocks sharing data land on one XCD:
+// consecutive logical blocks get consecutive physical slots on the same XCD
+// (the hardware deals physical block ids round-robin over `nxcd` XCDs).
+__device__ __forceinline__ int64_t xcd_remap(int64_t bid, int64_t nblocks, int nxcd) {
+    if (nblocks % nxcd != 0) return bid;
+    int64_t per = nblocks / nxcd;
+    return (bid % nxcd) * per + bid / nxcd;
+}
+
+}  // namespace ssm

@@ -1,0 +1,187 @@
+// step.hip -- one token of batched streaming decode for gfx950.
+//
+// "mamba, live" (section "what is actually running"): one token in, one out,
+// constant work per token; the whole memory is the state h plus a
+// (W-1)-token conv history per channel.  For every block k, stream s and
+// channel d this kernel shifts the history, applies the causal conv + SiLU,
+// takes one recurrence step of every state in place, and writes the gated
+// output.
+//
+// The step is bound by memory traffic on the state (4 B read + 4 B written
+// per state coordinate against a handful of VALU ops).  One lane owns a
+// channel's 16 states (LPC = 2 or 4 lanes for N up to 32 or 64), so a
+// wavefront covers 64 consecutive channels of one stream: x, z, y and each
+// history slot move as 256-byte rows, the state as 64-byte runs per lane.
+// Every load of a lane is issued before any arithmetic.
+//
+// Arithmetic follows the sequence kernel operation by operation: the same
+// conv tap order, softplus, decay 2^(dt*A*log2 e) with A = -exp(A_log), and
+// a readout summed as ((p0 + p1) + (p2 + p3)) over the four state groups the
+// sequence kernel gives its four lanes -- so for N <= 16 a token-by-token
+// decode reproduces the full forward bit for bit.
+#include <algorithm>
+
+#include "launch.hpp"
+#include "ssm_device.hpp"
+
+namespace ssm {
+namespace {
+
+constexpr int kSPL = 16;   // states per lane
+enum { DISC_DB = 0, DISC_ZOH = 1 };
+
+// LPC lanes per channel; G = states per readout group (the sequence
+// kernel's states per lane for this N); MAXW = widest conv carried.
+template <typename IOT, int LPC, int G, int DISC, bool CONV, int MAXW>
+__global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
+    const IOT *X = static_cast<const IOT *>(a.x);
+    const IOT *DT = static_cast<const IOT *>(a.dt);
+    const IOT *Bp = static_cast<const IOT *>(a.Bm);
+    const IOT *Cp = static_cast<const IOT *>(a.Cm);
+    const IOT *Z = static_cast<const IOT *>(a.z);
+    IOT *Y = static_cast<IOT *>(a.y);
+    const int64_t D = a.D, N = a.N, S = a.S;
+    const int W = a.W;
+    const int64_t total = a.nblk * S * D * LPC;
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    // lanes past the end take the last unit's values and store nothing
+    const bool active = gid < total;
+    const int64_t gc = active ? gid : (total - 1);
+    const int q = (int)(gc % LPC);
+    const int64_t d = (gc / LPC) % D;
+    const int64_t s = (gc / (LPC * D)) % S;
+    const int64_t k = gc / (LPC * D * S);
+    const int64_t sd = (k * S + s) * D + d;      // [nblk, S, D]
+    const int64_t kd = k * D + d;                // [nblk, D]
+    const int n0 = q * kSPL;
+    const int nvalid = max(0, min(kSPL, (int)(N - n0)));
+    const bool vecN = (N % 4) == 0;
+
+    // ---- loads
+    float hq[kSPL], Bq[kSPL], Cq[kSPL], al[kSPL];
+    float *hp = a.h + sd * N + n0;
+    const int64_t bc = (k * S + s) * N + n0;     // [nblk, S, N]
+    load_k_guard<kSPL>(hp, hq, nvalid, vecN);
+    load_k_guard<kSPL>(Bp + bc, Bq, nvalid, vecN);
+    load_k_guard<kSPL>(Cp + bc, Cq, nvalid, vecN);
+    load_k_guard<kSPL>(a.A_log + kd * N + n0, al, nvalid, vecN);
+    const float xr = to_f32(X[sd]);
+    const float dtr = to_f32(DT[sd]);
+    const float zr = Z != nullptr ? to_f32(Z[sd]) : 0.0f;
+    const float dtb = a.dt_bias ? a.dt_bias[kd] : 0.0f;
+    const float Dd = a.Dskip ? a.Dskip[kd] : 0.0f;
+    float hv[MAXW > 1 ? MAXW - 1 : 1], cw[MAXW], cb = 0.0f;
+    float *hist = nullptr;
+    if constexpr (CONV) {
+        if (W > 1) hist = a.conv_state + (k * S + s) * (int64_t)(W - 1) * D + d;   // slot j at hist[j*D]
+#pragma unroll
+        for (int j = 0; j < MAXW - 1; ++j) hv[j] = (j < W - 1) ? hist[j * D] : 0.0f;
+#pragma unroll
+        for (int j = 0; j < MAXW; ++j) cw[j] = (j < W) ? a.conv_w[kd * W + j] : 0.0f;
+        cb = a.conv_b ? a.conv_b[kd] : 0.0f;
+    }
+
+    // ---- arithmetic
+    float uu;
+    if constexpr (CONV) {
+        // bias, then taps oldest to newest
+        float acc = cb;
+#pragma unroll
+        for (int j = 0; j < MAXW - 1; ++j)
+            if (j < W - 1) acc = fmaf(cw[j], hv[j], acc);
+        float cwl = cw[0];
+#pragma unroll
+        for (int j = 1; j < MAXW; ++j)
+            if (j == W - 1) cwl = cw[j];
+        acc = fmaf(cwl, xr, acc);
+        uu = silu_f(acc);
+    } else {
+        uu = xr;
+    }
+    const float dl = softplus_f(dtr + dtb);
+    const float du = dl * uu;
+    float part[kSPL / G];
+#pragma unroll
+    for (int gI = 0; gI < kSPL / G; ++gI) part[gI] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSPL; ++j) {
+        const bool v = j < nvalid;
+        const float A = neg_exp_f(v ? al[j] : 0.0f);
+        const float A2 = v ? A * kLog2e : 0.0f;
+        const float dec = hw_exp2(dl * A2);
+        float w;
+        if constexpr (DISC == DISC_DB)
+            w = du * Bq[j];
+        else
+            w = expm1f(dl * A) * (1.0f / A) * Bq[j] * uu;
+        hq[j] = fmaf(dec, hq[j], w);
+        part[j / G] = fmaf(Cq[j], hq[j], part[j / G]);
+    }
+    if (active && nvalid > 0) store_k<kSPL>(hp, hq, nvalid, vecN);
+    // pairwise in the order of the sequence kernel's lane-quad reduction
+    float ysum;
+    if constexpr (kSPL / G >= 4) {
+        ysum = (part[0] + part[1]) + (part[2] + part[3]);
+#pragma unroll
+        for (int gI = 4; gI < kSPL / G; ++gI) ysum += part[gI];
+    } else {
+        ysum = 0.0f;
+#pragma unroll
+        for (int gI = 0; gI < kSPL / G; ++gI) ysum += part[gI];
+    }
+    ysum = group_sum<LPC>(ysum);
+    // readout in the sequence kernel's order: (sum_n C h + Dskip*u) * SiLU(z)
+    float yv = ysum + Dd * uu;
+    if (Z != nullptr) yv *= silu_f(zr);
+    if (q == 0 && active) {
+        store_io(Y + sd, yv);
+        if constexpr (CONV) {
+            if (W > 1) {
+#pragma unroll
+                for (int j = 0; j < MAXW - 2; ++j)
+                    if (j < W - 2) hist[j * D] = hv[j + 1];
+                hist[(W - 2) * D] = xr;
+            }
+        }
+    }
+}
+
+template <typename IOT, int LPC, int G>
+hipError_t launch_g(const StepArgs &a, hipStream_t s) {
+    const int64_t threads = a.nblk * a.S * a.D * LPC;
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const bool conv = a.W > 0;
+#define SSM_STEP_CASE(DI, CV, MW)                                                                        \
+    if (a.disc == DI && conv == CV && (!CV || a.W <= MW)) {                                              \
+        hipLaunchKernelGGL((step_kernel<IOT, LPC, G, DI, CV, MW>), dim3(blocks), dim3(256), 0, s, a); \
+        return hipGetLastError();                                                                        \
+    }
+    SSM_STEP_CASE(DISC_DB, false, 1)
+    SSM_STEP_CASE(DISC_DB, true, 4)
+    SSM_STEP_CASE(DISC_DB, true, 8)
+    SSM_STEP_CASE(DISC_ZOH, false, 1)
+    SSM_STEP_CASE(DISC_ZOH, true, 4)
+    SSM_STEP_CASE(DISC_ZOH, true, 8)
+#undef SSM_STEP_CASE
+    return hipErrorInvalidValue;
+}
+
+template <typename IOT>
+hipError_t launch_io(const StepArgs &a, hipStream_t s) {
+    // readout groups mirror the sequence kernel's states per lane (N <= 16)
+    if (a.N <= 4) return launch_g<IOT, 1, 1>(a, s);
+    if (a.N <= 8) return launch_g<IOT, 1, 2>(a, s);
+    if (a.N <= 16) return launch_g<IOT, 1, 4>(a, s);
+    if (a.N <= 32) return launch_g<IOT, 2, 4>(a, s);
+    return launch_g<IOT, 4, 4>(a, s);
+}
+
+}  // namespace
+
+hipError_t launch_step(const StepArgs &a, hipStream_t s) {
+    if (a.nblk * a.S * a.D == 0) return hipSuccess;
+    if (a.bf16) return launch_io<bf16_t>(a, s);
+    return launch_io<float>(a, s);
+}
+
+}  // namespace ssm

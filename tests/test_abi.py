@@ -1,0 +1,198 @@
+"""The C ABI on a machine without a GPU: the library loads, exports every
+symbol include/ssm.h declares, and rejects bad arguments with the documented
+status before any HIP call.  Device pointers here are fake addresses that the
+library never dereferences (validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    import selective_state_space_ssm_amd as m
+    if not os.path.exists(m.LIB_PATH):
+        from selective_state_space_ssm_amd import build
+        build.build()
+    return m
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "ssm.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", txt)) - {"sizeof"})
+
+
+def test_header_declares_the_four_calls():
+    fns = _header_functions()
+    for f in ("ssm_scan_fwd", "ssm_scan_bwd", "ssm_step", "conv1d_causal"):
+        assert f in fns
+
+
+def test_library_exports_every_declared_symbol(ssm):
+    lib = ctypes.CDLL(ssm.LIB_PATH)
+    fns = _header_functions()
+    assert set(fns) == set(ssm.EXPORTED_SYMBOLS)
+    for f in fns:
+        assert hasattr(lib, f), f
+
+
+def test_version_and_status_strings(ssm):
+    assert ssm.ssm_version() // 100 == 1
+    for code in range(0, 8):
+        s = ssm.ssm_status_string(code)
+        assert isinstance(s, str) and len(s) > 3
+    assert ssm.ssm_status_string(99) == "unknown status"
+
+
+A = 0x10000000  # fake, 16-byte aligned device addresses (never dereferenced)
+
+
+def _addr(k, off=0):
+    return ctypes.c_void_p(A + k * 0x1000000 + off)
+
+
+def _fwd(ssm, desc, **over):
+    names = ["x", "dt_raw", "dt_bias", "A_log", "B", "C", "Dskip", "z", "conv_w", "conv_b",
+             "conv_state_in", "conv_state_out", "h0", "hT", "y", "workspace"]
+    args = {n: _addr(i) for i, n in enumerate(names)}
+    for n in ("dt_bias", "Dskip", "z", "conv_w", "conv_b", "conv_state_in", "conv_state_out", "h0", "hT",
+              "workspace"):
+        args[n] = None
+    args.update(over)
+    ws_bytes = over.pop("ws_bytes", 0) if "ws_bytes" in over else 0
+    return ssm.lib().ssm_scan_fwd(ctypes.byref(desc), *[args[n] for n in names], ctypes.c_size_t(ws_bytes), None)
+
+
+def _desc(ssm, B=2, L=16, D=32, N=16, W=0, io=0, disc=0, chunk=-1):
+    return ssm.ssm_scan_desc(B, L, D, N, W, io, disc, chunk)
+
+
+@pytest.mark.parametrize("field,value", [("batch", 0), ("seqlen", -1), ("dim", 0), ("dstate", 0),
+                                         ("dstate", 65), ("conv_width", 9), ("conv_width", -1),
+                                         ("chunk_len", -2)])
+def test_scan_fwd_bad_shape(ssm, field, value):
+    d = _desc(ssm)
+    setattr(d, field, value)
+    assert _fwd(ssm, d) == ssm.SSM_ERR_BAD_SHAPE
+
+
+@pytest.mark.parametrize("field,value", [("io_dtype", 2), ("disc", 2), ("disc", -1)])
+def test_scan_fwd_unsupported(ssm, field, value):
+    d = _desc(ssm)
+    setattr(d, field, value)
+    assert _fwd(ssm, d) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_scan_fwd_null_desc(ssm):
+    assert ssm.lib().ssm_scan_fwd(None, *([None] * 16), ctypes.c_size_t(0), None) == ssm.SSM_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("name", ["x", "dt_raw", "A_log", "B", "C", "y"])
+def test_scan_fwd_required_pointers(ssm, name):
+    assert _fwd(ssm, _desc(ssm), **{name: None}) == ssm.SSM_ERR_NULL_ARG
+
+
+def test_scan_fwd_conv_needs_weights(ssm):
+    assert _fwd(ssm, _desc(ssm, W=4)) == ssm.SSM_ERR_NULL_ARG
+
+
+@pytest.mark.parametrize("name", ["x", "B", "A_log", "y", "h0"])
+def test_scan_fwd_alignment(ssm, name):
+    assert _fwd(ssm, _desc(ssm), **{name: _addr(40, 4)}) == ssm.SSM_ERR_ALIGNMENT
+
+
+def test_scan_fwd_output_overlapping_input(ssm):
+    assert _fwd(ssm, _desc(ssm), y=_addr(0, 64)) == ssm.SSM_ERR_ALIAS
+
+
+def test_scan_fwd_outputs_overlapping_each_other(ssm):
+    assert _fwd(ssm, _desc(ssm), hT=_addr(14, 16)) == ssm.SSM_ERR_ALIAS
+
+
+def test_scan_fwd_partial_state_alias_rejected(ssm):
+    assert _fwd(ssm, _desc(ssm), h0=_addr(20), hT=_addr(20, 16)) == ssm.SSM_ERR_ALIAS
+
+
+def test_scan_fwd_workspace_required_when_split(ssm):
+    d = _desc(ssm, B=1, L=4096, D=32, N=16, chunk=256)
+    n = ssm.ssm_scan_fwd_workspace_size(d)
+    assert n > 0
+    assert _fwd(ssm, d) == ssm.SSM_ERR_WORKSPACE
+    assert _fwd(ssm, d, workspace=_addr(30), ws_bytes=n - 1) == ssm.SSM_ERR_WORKSPACE
+
+
+def test_scan_fwd_workspace_zero_without_split(ssm):
+    assert ssm.ssm_scan_fwd_workspace_size(_desc(ssm, chunk=-1)) == 0
+    assert ssm.ssm_scan_fwd_workspace_size(_desc(ssm, L=64, chunk=1000)) == 0
+
+
+def test_scan_bwd_rejects_fused_conv(ssm):
+    with pytest.raises(ssm.SSMError) as e:
+        ssm.ssm_scan_bwd_workspace_size(_desc(ssm, W=4))
+    assert e.value.code == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_scan_bwd_workspace_and_nulls(ssm):
+    d = _desc(ssm)
+    n = ssm.ssm_scan_bwd_workspace_size(d)
+    assert n > 0
+    args = [_addr(i) for i in range(21)]
+    # optional inputs absent
+    for i in (2, 6, 7, 8, 10, 18):
+        args[i] = None
+    rc = ssm.lib().ssm_scan_bwd(ctypes.byref(d), *args[:20], None, ctypes.c_size_t(0), None)
+    assert rc == ssm.SSM_ERR_WORKSPACE
+    args2 = list(args)
+    args2[9] = None  # dy
+    rc = ssm.lib().ssm_scan_bwd(ctypes.byref(d), *args2[:20], _addr(50), ctypes.c_size_t(n), None)
+    assert rc == ssm.SSM_ERR_NULL_ARG
+    args3 = list(args)
+    args3[18] = _addr(1)  # dz without z
+    rc = ssm.lib().ssm_scan_bwd(ctypes.byref(d), *args3[:20], _addr(50), ctypes.c_size_t(n), None)
+    assert rc == ssm.SSM_ERR_NULL_ARG
+
+
+def test_step_validation(ssm):
+    L = ssm.lib()
+    good = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, 0, 0)
+    ptrs = [_addr(i) for i in range(13)]
+    bad = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, 0, 1)
+    assert L.ssm_step(ctypes.byref(bad), *ptrs, None) == ssm.SSM_ERR_UNSUPPORTED
+    bad = ssm.ssm_step_desc(0, 8, 32, 16, 4, 0, 0, 0)
+    assert L.ssm_step(ctypes.byref(bad), *ptrs, None) == ssm.SSM_ERR_BAD_SHAPE
+    p2 = list(ptrs)
+    p2[1] = None  # conv_state with W = 4
+    assert L.ssm_step(ctypes.byref(good), *p2, None) == ssm.SSM_ERR_NULL_ARG
+    p3 = list(ptrs)
+    p3[12] = _addr(2, 32)  # y inside x
+    assert L.ssm_step(ctypes.byref(good), *p3, None) == ssm.SSM_ERR_ALIAS
+    p4 = list(ptrs)
+    p4[0] = _addr(0, 8)
+    assert L.ssm_step(ctypes.byref(good), *p4, None) == ssm.SSM_ERR_ALIGNMENT
+
+
+def test_conv_validation(ssm):
+    L = ssm.lib()
+    d = ssm.ssm_conv_desc(2, 16, 32, 4, 1, 0, 0)
+    ptrs = [_addr(i) for i in range(6)]
+    bad = ssm.ssm_conv_desc(2, 16, 32, 9, 1, 0, 0)
+    assert L.conv1d_causal(ctypes.byref(bad), *ptrs, None) == ssm.SSM_ERR_BAD_SHAPE
+    bad = ssm.ssm_conv_desc(2, 16, 32, 4, 2, 0, 0)
+    assert L.conv1d_causal(ctypes.byref(bad), *ptrs, None) == ssm.SSM_ERR_UNSUPPORTED
+    p = list(ptrs)
+    p[1] = None
+    assert L.conv1d_causal(ctypes.byref(d), *p, None) == ssm.SSM_ERR_NULL_ARG
+    p = list(ptrs)
+    p[4] = p[3]  # state_out == state_in
+    assert L.conv1d_causal(ctypes.byref(d), *p, None) == ssm.SSM_ERR_ALIAS
+
+
+def test_binding_rejects_host_tensors(ssm):
+    import torch
+    x = torch.zeros(1, 4, 8)
+    with pytest.raises(ValueError):
+        ssm.conv1d_causal(x, torch.zeros(8, 4))

@@ -1,0 +1,443 @@
+"""GPU parity: every HIP path against the float64 oracle on the same seeded
+inputs, element by element, at the tolerances of the workloads (relative
+L-inf 1e-5 for float32 I/O, 2e-2 for bf16 I/O with float32 state)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import seeded_inputs as si
+from parity import BF16_TOL, FP32_TOL, dev, host, rel_linf, tol
+
+pytestmark = pytest.mark.gpu
+
+DB, ZOH = 0, 1
+
+
+@pytest.fixture(scope="module")
+def ssm():
+    import selective_state_space_ssm_amd as m
+    m.lib()  # raises if the library is not built
+    assert torch.cuda.is_available(), "no GPU visible"
+    return m
+
+
+def _rand(seed, Bn, L, D, N, W=4, bf16=False, scale_dt=1.0):
+    r = np.random.default_rng(seed)
+    f = lambda *s: r.standard_normal(s).astype(np.float32)
+    p = dict(x=f(Bn, L, D), dt_raw=(f(Bn, L, D) * np.float32(scale_dt)), B=f(Bn, L, N), C=f(Bn, L, N),
+             z=f(Bn, L, D), dy=f(Bn, L, D), dt_bias=(0.3 * f(D)), A_log=(0.5 * f(D, N)),
+             Dskip=f(D), h0=f(Bn, D, N), dhT=f(Bn, D, N), conv_w=f(D, W), conv_b=f(D),
+             conv_state=f(Bn, max(W - 1, 0), D))
+    if bf16:
+        for k in ("x", "dt_raw", "B", "C", "z", "dy"):
+            p[k] = si.bf16_round(p[k])
+    return p
+
+
+def _fwd_gpu(ssm, p, dtype, disc=DB, conv=True, gate=True, h0=True, chunk=-1, state=True):
+    N = p["A_log"].shape[1]
+    W = p["conv_w"].shape[1]
+    Bn, L, D = p["x"].shape
+    hT = torch.empty(Bn, D, N, device="cuda") if state else None
+    cso = torch.empty(Bn, W - 1, D, device="cuda") if (conv and state and W > 1) else None
+    y = ssm.ssm_scan_fwd(dev(p["x"], dtype), dev(p["dt_raw"], dtype), dev(p["A_log"]), dev(p["B"], dtype),
+                         dev(p["C"], dtype), dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]),
+                         z=dev(p["z"], dtype) if gate else None,
+                         conv_w=dev(p["conv_w"]) if conv else None, conv_b=dev(p["conv_b"]) if conv else None,
+                         conv_state_in=dev(p["conv_state"]) if (conv and state and W > 1) else None,
+                         conv_state_out=cso, h0=dev(p["h0"]) if h0 else None, hT=hT, disc=disc, chunk_len=chunk)
+    torch.cuda.synchronize()
+    return y, hT, cso
+
+
+def _fwd_oracle(p, disc=DB, conv=True, gate=True, h0=True, state=True):
+    W = p["conv_w"].shape[1]
+    if conv:
+        u, cso = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"],
+                                      p["conv_state"] if (state and W > 1) else None)
+    else:
+        u, cso = p["x"], None
+    y, hT = oracle.scan_fwd(u, p["dt_raw"], p["A_log"], p["B"], p["C"], dt_bias=p["dt_bias"],
+                            Dskip=p["Dskip"], z=p["z"] if gate else None, h0=p["h0"] if h0 else None, disc=disc)
+    return y, hT, cso, u
+
+
+# --------------------------------------------------------------------------- conv
+
+@pytest.mark.parametrize("Bn,L,D,W,state,silu,bf16", [
+    (1, 6, 8, 3, False, True, False),        # tiny teaching block
+    (3, 77, 100, 4, True, True, False),      # ragged: L, D not multiples of the tiles
+    (2, 40, 33, 1, False, False, False),
+    (2, 5, 17, 8, True, True, False),        # L < W - 1
+    (2, 130, 64, 4, True, True, True),       # bf16 I/O
+    (1, 0, 16, 4, True, True, False),        # empty sequence: history passes through
+])
+def test_conv1d_parity(ssm, Bn, L, D, W, state, silu, bf16):
+    p = _rand(11, Bn, L, D, 4, W, bf16=bf16)
+    dtype = torch.bfloat16 if bf16 else torch.float32
+    so = torch.empty(Bn, W - 1, D, device="cuda") if (state and W > 1) else None
+    y = ssm.conv1d_causal(dev(p["x"], dtype), dev(p["conv_w"]), dev(p["conv_b"]),
+                          state_in=dev(p["conv_state"]) if (state and W > 1) else None, state_out=so, silu=silu)
+    torch.cuda.synchronize()
+    ref, rso = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"],
+                                    p["conv_state"] if (state and W > 1) else None, silu=silu)
+    if L > 0:
+        assert rel_linf(y, ref) <= tol(dtype)
+    if so is not None:
+        np.testing.assert_array_equal(host(so), rso)
+
+
+# --------------------------------------------------------------------------- forward
+
+@pytest.mark.parametrize("disc", [DB, ZOH])
+@pytest.mark.parametrize("conv", [False, True])
+def test_fwd_tiny_block(ssm, disc, conv):
+    """The teaching block's size (B=1, L=6, D=8, N=3, W=3), seed 0, both
+    discretisations, with and without the fused conv."""
+    t = si.tiny_block()
+    p = dict(t, h0=np.zeros((1, 8, 3), np.float32), conv_state=np.zeros((1, 2, 8), np.float32))
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32, disc=disc, conv=conv)
+    yr, hr, csr, _ = _fwd_oracle(p, disc=disc, conv=conv)
+    assert rel_linf(y, yr) <= FP32_TOL
+    assert rel_linf(hT, hr) <= FP32_TOL
+    if conv:
+        np.testing.assert_array_equal(host(cso), csr)
+
+
+@pytest.mark.parametrize("Bn,L,D,N,W", [
+    (2, 300, 40, 16, 4),    # D not a multiple of 16, L not a multiple of the unroll
+    (1, 33, 24, 1, 4),
+    (2, 50, 20, 3, 3),
+    (1, 64, 16, 5, 2),
+    (2, 41, 48, 8, 4),
+    (1, 40, 16, 17, 4),
+    (1, 37, 32, 33, 4),
+    (1, 29, 16, 64, 8),
+    (1, 64, 1, 16, 4),      # one channel
+    (1, 1, 48, 16, 4),      # one token
+])
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_fwd_shapes(ssm, Bn, L, D, N, W, disc):
+    p = _rand(5, Bn, L, D, N, W)
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32, disc=disc)
+    yr, hr, csr, _ = _fwd_oracle(p, disc=disc)
+    assert rel_linf(y, yr) <= FP32_TOL
+    assert rel_linf(hT, hr) <= FP32_TOL
+    np.testing.assert_array_equal(host(cso), csr)
+
+
+@pytest.mark.parametrize("gate,h0,conv", [(False, False, False), (True, False, False), (False, True, True)])
+def test_fwd_optional_inputs(ssm, gate, h0, conv):
+    p = _rand(6, 2, 70, 32, 16)
+    y, hT, _ = _fwd_gpu(ssm, p, torch.float32, gate=gate, h0=h0, conv=conv)
+    yr, hr, _, _ = _fwd_oracle(p, gate=gate, h0=h0, conv=conv)
+    assert rel_linf(y, yr) <= FP32_TOL
+    assert rel_linf(hT, hr) <= FP32_TOL
+
+
+def test_fwd_empty_sequence(ssm):
+    """L = 0: no output tokens, hT = h0 and the conv history passes through."""
+    p = _rand(7, 2, 0, 32, 16)
+    _, hT, cso = _fwd_gpu(ssm, p, torch.float32)
+    np.testing.assert_array_equal(host(hT), p["h0"])
+    np.testing.assert_array_equal(host(cso), p["conv_state"])
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 37, 64, 100, 0])
+@pytest.mark.parametrize("conv", [False, True])
+def test_fwd_chunked_matches_oracle(ssm, chunk, conv):
+    """Two-level time split (local chunk scans, carry walk, re-scan) against
+    the sequential oracle, for chunk lengths that leave ragged tails."""
+    p = _rand(8, 2, 333, 40, 16)
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32, conv=conv, chunk=chunk)
+    yr, hr, csr, _ = _fwd_oracle(p, conv=conv)
+    assert rel_linf(y, yr) <= FP32_TOL
+    assert rel_linf(hT, hr) <= FP32_TOL
+    if conv:
+        np.testing.assert_array_equal(host(cso), csr)
+
+
+def test_fwd_split_sequence_equals_whole(ssm):
+    """fwd(x[:k]) then fwd(x[k:]) from the carried state and conv history
+    gives the single call's outputs bit for bit."""
+    p = _rand(9, 2, 90, 48, 16)
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32)
+    k = 37
+    a = {kk: (v[:, :k] if (v.ndim == 3 and v.shape[1] == 90) else v) for kk, v in p.items()}
+    b = {kk: (v[:, k:] if (v.ndim == 3 and v.shape[1] == 90) else v) for kk, v in p.items()}
+    y1, h1, c1 = _fwd_gpu(ssm, a, torch.float32)
+    b["h0"], b["conv_state"] = host(h1).astype(np.float32), host(c1).astype(np.float32)
+    y2, h2, c2 = _fwd_gpu(ssm, b, torch.float32)
+    assert torch.equal(torch.cat([y1, y2], 1), y)
+    assert torch.equal(h2, hT) and torch.equal(c2, cso)
+
+
+def test_fwd_in_place_state(ssm):
+    """hT may be h0 and conv_state_out may be conv_state_in (in-place)."""
+    p = _rand(10, 2, 200, 32, 16)
+    yr, hr, csr, _ = _fwd_oracle(p)
+    for chunk in (-1, 50):
+        h = dev(p["h0"])
+        cs = dev(p["conv_state"])
+        y = ssm.ssm_scan_fwd(dev(p["x"]), dev(p["dt_raw"]), dev(p["A_log"]), dev(p["B"]), dev(p["C"]),
+                             dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]), z=dev(p["z"]),
+                             conv_w=dev(p["conv_w"]), conv_b=dev(p["conv_b"]), conv_state_in=cs,
+                             conv_state_out=cs, h0=h, hT=h, chunk_len=chunk)
+        torch.cuda.synchronize()
+        assert rel_linf(y, yr) <= FP32_TOL
+        assert rel_linf(h, hr) <= FP32_TOL
+        np.testing.assert_array_equal(host(cs), csr)
+
+
+def test_fwd_bf16_io(ssm):
+    p = _rand(12, 2, 160, 48, 16, bf16=True)
+    for chunk in (-1, 40):
+        y, hT, _ = _fwd_gpu(ssm, p, torch.bfloat16, chunk=chunk)
+        assert y.dtype == torch.bfloat16
+        yr, hr, _, _ = _fwd_oracle(p)
+        assert rel_linf(y, yr) <= BF16_TOL
+        assert rel_linf(hT, hr) <= BF16_TOL
+
+
+def test_fwd_deterministic(ssm):
+    p = _rand(13, 2, 300, 64, 16)
+    a = _fwd_gpu(ssm, p, torch.float32, chunk=64)
+    b = _fwd_gpu(ssm, p, torch.float32, chunk=64)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ------------------------------------------------------------ workloads at full size
+
+def _mamba_fwd(ssm, p, dtype, chunk=0):
+    Bn, L, D = p["x"].shape
+    N = p["A_log"].shape[1]
+    hT = torch.empty(Bn, D, N, device="cuda")
+    y = ssm.ssm_scan_fwd(dev(p["x"], dtype), dev(p["dt_raw"], dtype), dev(p["A_log"]), dev(p["B"], dtype),
+                         dev(p["C"], dtype), dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]),
+                         z=dev(p["z"], dtype), conv_w=dev(p["conv_w"]), conv_b=dev(p["conv_b"]), hT=hT,
+                         chunk_len=chunk)
+    torch.cuda.synchronize()
+    return y, hT
+
+
+@pytest.mark.parametrize("perturbed", [False, True])
+def test_mamba_mini_block_L256(ssm, perturbed):
+    """Mamba-mini block forward: batch 8, L=256, D_inner=1536, N=16, fp32,
+    4-tap causal conv fused before the scan, SiLU(z) gate; the perturbed run
+    uses A_log = log(n+1) + 0.1*normal and Dskip = normal."""
+    p = si.mamba_block(8, 256, 1536, 16, 4, workload=si.WL_BLOCK, perturbed=perturbed)
+    y, hT = _mamba_fwd(ssm, p, torch.float32)
+    u, _ = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"])
+    yr, hr = oracle.scan_fwd(u, p["dt_raw"], p["A_log"], p["B"], p["C"], dt_bias=p["dt_bias"],
+                             Dskip=p["Dskip"], z=p["z"])
+    assert rel_linf(y, yr) <= FP32_TOL
+    assert rel_linf(hT, hr) <= FP32_TOL
+
+
+def test_mamba_mini_block_L2048(ssm):
+    """The forward at batch 8, L=2048, D_inner=1536, N=16, fp32 (the
+    benchmark's workload and launch configuration)."""
+    p = si.mamba_block(8, 2048, 1536, 16, 4, workload=si.WL_FWDBWD)
+    y, hT = _mamba_fwd(ssm, p, torch.float32)
+    u, _ = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"])
+    yr, hr = oracle.scan_fwd(u, p["dt_raw"], p["A_log"], p["B"], p["C"], dt_bias=p["dt_bias"],
+                             Dskip=p["Dskip"], z=p["z"])
+    assert rel_linf(y, yr) <= FP32_TOL
+    assert rel_linf(hT, hr) <= FP32_TOL
+
+
+def test_long_sequence_bf16_chunked(ssm):
+    """Long-sequence two-level scan: batch 1, L=65,536, D_inner=1536, N=16,
+    bf16 inputs and output, float32 state, fused SiLU(z) gate."""
+    p = si.mamba_block(1, 65536, 1536, 16, 4, workload=si.WL_LONG, bf16=True)
+    u = p["x"]  # the scan input itself (no conv on this workload)
+    Bn, L, D = u.shape
+    hT = torch.empty(Bn, D, 16, device="cuda")
+    y = ssm.ssm_scan_fwd(dev(u, torch.bfloat16), dev(p["dt_raw"], torch.bfloat16), dev(p["A_log"]),
+                         dev(p["B"], torch.bfloat16), dev(p["C"], torch.bfloat16), dt_bias=dev(p["dt_bias"]),
+                         Dskip=dev(p["Dskip"]), z=dev(p["z"], torch.bfloat16), hT=hT)
+    torch.cuda.synchronize()
+    yr, hr = oracle.scan_fwd(u, p["dt_raw"], p["A_log"], p["B"], p["C"], dt_bias=p["dt_bias"],
+                             Dskip=p["Dskip"], z=p["z"])
+    assert rel_linf(y, yr) <= BF16_TOL
+    assert rel_linf(hT, hr) <= BF16_TOL
+
+
+# --------------------------------------------------------------------------- step
+
+def _step_oracle_loop(p, steps, disc=DB, gate=True):
+    h = p["h0"].astype(np.float64).copy()
+    cs = p["conv_state"].astype(np.float64).copy()
+    ys = []
+    for t in range(steps):
+        ys.append(oracle.step(h, cs, p["x"][:, t], p["dt_raw"][:, t], p["B"][:, t], p["C"][:, t], p["A_log"],
+                              z=p["z"][:, t] if gate else None, conv_w=p["conv_w"], conv_b=p["conv_b"],
+                              dt_bias=p["dt_bias"], Dskip=p["Dskip"], disc=disc))
+    return np.stack(ys, 1), h, cs
+
+
+@pytest.mark.parametrize("disc", [DB, ZOH])
+@pytest.mark.parametrize("S,D,N,W", [(4, 40, 16, 4), (3, 8, 3, 3), (2, 16, 33, 2), (5, 24, 16, 1)])
+def test_step_parity(ssm, disc, S, D, N, W):
+    """Token-by-token streaming with one block against the oracle's step."""
+    p = _rand(14, S, 12, D, N, W)
+    y_ref, h_ref, cs_ref = _step_oracle_loop(p, 12, disc=disc)
+    h = dev(p["h0"])[None].contiguous()
+    cs = dev(p["conv_state"])[None].contiguous() if W > 1 else None
+    ys = []
+    for t in range(12):
+        ys.append(ssm.ssm_step(h, dev(p["x"][:, t])[None], dev(p["dt_raw"][:, t])[None], dev(p["A_log"])[None],
+                               dev(p["B"][:, t])[None], dev(p["C"][:, t])[None], conv_state=cs,
+                               z=dev(p["z"][:, t])[None], conv_w=dev(p["conv_w"])[None],
+                               conv_b=dev(p["conv_b"])[None], dt_bias=dev(p["dt_bias"])[None],
+                               Dskip=dev(p["Dskip"])[None], disc=disc)[0])
+    torch.cuda.synchronize()
+    assert rel_linf(torch.stack(ys, 1), y_ref) <= FP32_TOL
+    assert rel_linf(h[0], h_ref) <= FP32_TOL
+    if cs is not None:
+        np.testing.assert_array_equal(host(cs[0]), cs_ref)
+
+
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_step_loop_equals_forward(ssm, disc):
+    """Streaming with the (W-1)*D history and D*N state reproduces the full
+    forward on the GPU (the two kernels share one operation order)."""
+    p = _rand(15, 3, 25, 48, 16, 4)
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32, disc=disc)
+    h = dev(p["h0"])[None].contiguous()
+    cs = dev(p["conv_state"])[None].contiguous()
+    ys = []
+    for t in range(25):
+        ys.append(ssm.ssm_step(h, dev(p["x"][:, t])[None], dev(p["dt_raw"][:, t])[None], dev(p["A_log"])[None],
+                               dev(p["B"][:, t])[None], dev(p["C"][:, t])[None], conv_state=cs,
+                               z=dev(p["z"][:, t])[None], conv_w=dev(p["conv_w"])[None],
+                               conv_b=dev(p["conv_b"])[None], dt_bias=dev(p["dt_bias"])[None],
+                               Dskip=dev(p["Dskip"])[None], disc=disc)[0])
+    torch.cuda.synchronize()
+    ys = torch.stack(ys, 1)
+    assert rel_linf(ys, y) <= 1e-6
+    assert rel_linf(h[0], hT) <= 1e-6
+    assert torch.equal(cs[0], cso)
+
+
+def test_step_bf16(ssm):
+    p = _rand(16, 4, 6, 32, 16, 4, bf16=True)
+    y_ref, h_ref, _ = _step_oracle_loop(p, 6)
+    h = dev(p["h0"])[None].contiguous()
+    cs = dev(p["conv_state"])[None].contiguous()
+    bf = torch.bfloat16
+    for t in range(6):
+        y = ssm.ssm_step(h, dev(p["x"][:, t], bf)[None], dev(p["dt_raw"][:, t], bf)[None], dev(p["A_log"])[None],
+                         dev(p["B"][:, t], bf)[None], dev(p["C"][:, t], bf)[None], conv_state=cs,
+                         z=dev(p["z"][:, t], bf)[None], conv_w=dev(p["conv_w"])[None],
+                         conv_b=dev(p["conv_b"])[None], dt_bias=dev(p["dt_bias"])[None],
+                         Dskip=dev(p["Dskip"])[None])[0]
+        torch.cuda.synchronize()
+        assert y.dtype == bf
+        assert rel_linf(y, y_ref[:, t]) <= BF16_TOL
+    assert rel_linf(h[0], h_ref) <= BF16_TOL
+
+
+def test_streaming_decode_six_blocks(ssm):
+    """Batched streaming decode: 6 blocks x 256 streams x 1536 channels x 16
+    states, 3-token conv history, 1,024 consecutive steps, one launch per
+    block and step.  Every stream of every block is stepped on the GPU;
+    the oracle replays a sample of 6 streams over all steps."""
+    nblk, S, D, N, W, steps = 6, 256, 1536, 16, 4, 1024
+    sample = [0, 37, 101, 128, 200, 255]
+    prm = si.stream_params(nblk, D, N, W)
+    P = {k: dev(v) for k, v in prm.items()}
+    h = torch.zeros(nblk, S, D, N, device="cuda")
+    cs = torch.zeros(nblk, S, W - 1, D, device="cuda")
+    ho = np.zeros((nblk, len(sample), D, N))
+    co = np.zeros((nblk, len(sample), W - 1, D))
+    y_last_ref = None
+    for t in range(steps):
+        for k in range(nblk):
+            inp = si.stream_token_torch(k, t, S, D, N, "cuda")
+            y = ssm.ssm_step(h[k:k + 1], inp["x"][None], inp["dt_raw"][None], P["A_log"][k:k + 1],
+                             inp["B"][None], inp["C"][None], conv_state=cs[k:k + 1], z=inp["z"][None],
+                             conv_w=P["conv_w"][k:k + 1], conv_b=P["conv_b"][k:k + 1],
+                             dt_bias=P["dt_bias"][k:k + 1], Dskip=P["Dskip"][k:k + 1])
+            sl = {kk: host(v[sample]) for kk, v in inp.items()}
+            yr = oracle.step(ho[k], co[k], sl["x"], sl["dt_raw"], sl["B"], sl["C"], prm["A_log"][k], z=sl["z"],
+                             conv_w=prm["conv_w"][k], conv_b=prm["conv_b"][k], dt_bias=prm["dt_bias"][k],
+                             Dskip=prm["Dskip"][k])
+            if t in (0, 511, steps - 1):
+                assert rel_linf(y[0][sample], yr) <= FP32_TOL, (t, k)
+    torch.cuda.synchronize()
+    for k in range(nblk):
+        assert rel_linf(h[k][sample], ho[k]) <= FP32_TOL
+        np.testing.assert_array_equal(host(cs[k][sample]), co[k])
+
+
+# --------------------------------------------------------------------------- backward
+
+_GRADS = ["du", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dD", "dz", "dh0"]
+
+
+def _bwd_check(ssm, p, dtype, disc, gate=True, h0=True, dhT=True, tolerance=None):
+    Bn, L, D = p["x"].shape
+    g = ssm.ssm_scan_bwd(dev(p["x"], dtype), dev(p["dt_raw"], dtype), dev(p["A_log"]), dev(p["B"], dtype),
+                         dev(p["C"], dtype), dev(p["dy"], dtype), dt_bias=dev(p["dt_bias"]),
+                         Dskip=dev(p["Dskip"]), z=dev(p["z"], dtype) if gate else None,
+                         h0=dev(p["h0"]) if h0 else None, dhT=dev(p["dhT"]) if dhT else None, disc=disc)
+    torch.cuda.synchronize()
+    r = oracle.scan_bwd(p["x"], p["dt_raw"], p["A_log"], p["B"], p["C"], p["dy"], dt_bias=p["dt_bias"],
+                        Dskip=p["Dskip"], z=p["z"] if gate else None, h0=p["h0"] if h0 else None,
+                        dhT=p["dhT"] if dhT else None, disc=disc)
+    errs = {}
+    for k in _GRADS:
+        if k == "dz" and not gate:
+            continue
+        errs[k] = rel_linf(g[k], r[k])
+    lim = tolerance if tolerance is not None else tol(dtype)
+    bad = {k: v for k, v in errs.items() if not v <= lim}
+    assert not bad, (bad, errs)
+    return g
+
+
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_bwd_tiny_block(ssm, disc):
+    t = si.tiny_block()
+    p = dict(t, h0=np.zeros((1, 8, 3), np.float32), dhT=np.zeros((1, 8, 3), np.float32))
+    _bwd_check(ssm, p, torch.float32, disc)
+
+
+@pytest.mark.parametrize("Bn,L,D,N", [(2, 100, 40, 16), (1, 37, 24, 3), (2, 21, 16, 8), (1, 50, 70, 33),
+                                      (1, 9, 16, 64), (1, 1, 1, 16)])
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_bwd_shapes(ssm, Bn, L, D, N, disc):
+    p = _rand(17, Bn, L, D, N)
+    _bwd_check(ssm, p, torch.float32, disc)
+
+
+@pytest.mark.parametrize("gate,h0,dhT", [(False, False, False), (True, False, True), (False, True, False)])
+def test_bwd_optional_inputs(ssm, gate, h0, dhT):
+    p = _rand(18, 2, 64, 32, 16)
+    _bwd_check(ssm, p, torch.float32, DB, gate=gate, h0=h0, dhT=dhT)
+
+
+def test_bwd_bf16(ssm):
+    p = _rand(19, 2, 80, 48, 16, bf16=True)
+    _bwd_check(ssm, p, torch.bfloat16, DB)
+
+
+def test_bwd_deterministic(ssm):
+    p = _rand(20, 2, 96, 128, 16)
+    a = _bwd_check(ssm, p, torch.float32, DB)
+    b = _bwd_check(ssm, p, torch.float32, DB)
+    for k in _GRADS:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_bwd_forward_backward_workload(ssm):
+    """Forward plus backward at batch 8, L=2,048, D_inner=1536, N=16, fp32:
+    gradients w.r.t. u, dt (as d_dt_raw and d_dt_bias), A_log, B, C, Dskip,
+    z and h0 against the oracle.  u = SiLU(conv4(x)) from the oracle's conv."""
+    p = si.mamba_block(8, 2048, 1536, 16, 4, workload=si.WL_FWDBWD, with_dy=True)
+    u, _ = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"])
+    q = dict(p, x=u.astype(np.float32), h0=np.zeros((8, 1536, 16), np.float32),
+             dhT=np.zeros((8, 1536, 16), np.float32))
+    _bwd_check(ssm, q, torch.float32, DB, h0=False, dhT=False)
