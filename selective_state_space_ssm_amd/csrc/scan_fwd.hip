@@ -5,19 +5,22 @@
 //   dt = softplus(dt_raw + dt_bias),  a = 2^(dt * A * log2 e),  A = -exp(A_log)
 //   h  = a * h + coef * B * u,  y = (<h, C> + Dskip * u) * SiLU(z)
 //
-// Work decomposition.  One 64-lane wavefront owns 16 channels of one batch
-// row and one time chunk.  Tokens are processed in tiles of 32:
+// Work decomposition.  A block of four wavefronts owns 16 channels of one
+// batch row and one time chunk; wavefront w keeps states 4w .. 4w+3 of every
+// channel (one state per lane at N = 16, four lanes per channel), so config
+// shapes with B*D/16 = 768 blocks put three wavefronts on every SIMD.
+// Tokens are processed in tiles of 64:
 //  - fetch: the next tile's x, dt_raw, z and its B, C rows are loaded into
 //    registers while the current tile is scanned (one tile of prefetch);
 //  - stage: the raw conv input goes to LDS (with 8 rows of history for the
 //    causal window) and B, C rows go to LDS;
-//  - transform: each lane takes one channel and 8 consecutive tokens and
+//  - transform: each thread takes one channel and 4 consecutive tokens and
 //    computes, once per (token, channel), the conv + SiLU, dt = softplus,
-//    dt*u, the gate SiLU(z) and Dskip*u into an LDS record;
-//  - scan: four lanes own a channel, lane q keeping states q*SPL ..
-//    q*SPL+SPL-1 in registers; per token a lane reads the channel's record
-//    and its B, C values from LDS, updates its states with one exp2 each,
-//    and the readout <h, C> is finished with two DPP adds in the lane quad.
+//    dt*u, the gate SiLU(z) and Dskip*u into LDS;
+//  - scan: per token a lane reads its channel's (dt, dt*u) and its B, C
+//    values from LDS and updates its state with one exp2; the readout
+//    <h, C> is summed in the lane quad with DPP and across the four
+//    wavefronts through LDS, in the fixed order ((w0 + w1) + (w2 + w3)).
 // The recurrence itself stays strictly sequential in time inside a chunk.
 //
 // Long sequences with few independent channels are split in time (two-level
@@ -34,8 +37,7 @@
 namespace ssm {
 namespace {
 
-constexpr int kLPC = 4;             // lanes per channel
-constexpr int kCPW = 64 / kLPC;     // channels per wavefront
+constexpr int kCPW = 16;            // channels per block
 enum { MODE_FINAL = 0, MODE_LOCAL = 1 };
 enum { DISC_DB = 0, DISC_ZOH = 1 };
 
@@ -59,101 +61,115 @@ struct FwdParams {
     int64_t chunk;
     int K;                         // chunks along time (array stride)
     int Kgrid;                     // chunks covered by this launch (0 .. Kgrid-1)
-    int groups;                    // channel groups of kCPW
+    int groups;                    // channel groups of kCPW per batch row
 };
 
-constexpr int kTile = 32;           // tokens staged per tile
-constexpr int kXS = 17;             // padded row stride of the conv staging rows (LDS banks)
+constexpr int kTile = 64;           // tokens staged per tile
+constexpr int kXS = 17;             // padded LDS row stride (16 channels + 1)
+constexpr int kThreads = 256;       // four wavefronts per block
+constexpr int kRows = kTile / 16;   // tile rows per thread in the transform role
 
 // Raw loads of one tile, held in registers while the previous tile is
-// scanned.  Transform role: lane -> channel tc = lane & 15 and rows
-// rg*8 .. rg*8+7 with rg = lane >> 4.  B/C: 4-wide chunks (vector path) or
-// single elements (guarded path) dealt round-robin over the lanes.
+// scanned.  Transform role: thread -> channel tc = tid & 15 and rows
+// kRows*rp .. kRows*rp + kRows-1 with rp = tid >> 4.  B and C: 4-wide
+// chunks (vector path) or single elements (guarded path) dealt over the
+// block's threads, B first then C.
 template <int NP>
 struct RawTile {
-    // enough for either layout: whole 4-wide chunks, or single elements
-    static constexpr int BCV = 4 * ((kTile * NP / 4 + 63) / 64);
-    static constexpr int BCS = (kTile * NP + 63) / 64;
+    static constexpr int NCH = kTile * NP / 4;                      // chunks per tensor
+    static constexpr int BCV = 4 * ((2 * NCH + kThreads - 1) / kThreads);
+    static constexpr int BCS = (2 * kTile * NP + kThreads - 1) / kThreads;
     static constexpr int BCE = BCV > BCS ? BCV : BCS;
-    float x[8], dt[8], z[8];
-    float b[BCE], c[BCE];
+    float x[kRows], dt[kRows], z[kRows];
+    float bc[BCE];
 };
 
 template <typename IOT, int NP, bool WANT_C>
 __device__ __forceinline__ void load_raw(RawTile<NP> &r, const IOT *X, const IOT *DT, const IOT *Z,
                                          const IOT *Bp, const IOT *Cp, int64_t b, int64_t L, int64_t D,
-                                         int64_t N, int64_t ts, int nv, int64_t tdc, bool tvalid, int rg,
-                                         int lane, bool vecBC) {
+                                         int64_t N, int64_t ts, int nv, int64_t tdc, bool tvalid, int rp,
+                                         int tid, bool vecBC) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = rg * 8 + i;
+    for (int i = 0; i < kRows; ++i) {
+        const int row = rp * kRows + i;
         const bool v = tvalid && row < nv;
         const int64_t e = (b * L + ts + row) * D + tdc;
         r.x[i] = v ? to_f32(X[e]) : 0.0f;
         r.dt[i] = v ? to_f32(DT[e]) : 0.0f;
         r.z[i] = (v && Z != nullptr) ? to_f32(Z[e]) : 0.0f;
     }
-    constexpr int BCE = RawTile<NP>::BCS;
+    constexpr int NCH = RawTile<NP>::NCH;
+    const int ntens = WANT_C ? 2 : 1;
     if (vecBC) {
-        // chunk f = lane + 64*i holds row f / (NP/4), states 4*(f % (NP/4)) .. +3
-        constexpr int NCH = kTile * NP / 4;
 #pragma unroll
         for (int i = 0; i < RawTile<NP>::BCV / 4; ++i) {
-            const int f = lane + 64 * i;
-            const int row = f / (NP / 4), c4 = (f % (NP / 4)) * 4;
-            const bool v = f < NCH && row < nv;
-            float tb[4] = {0.f, 0.f, 0.f, 0.f}, tc[4] = {0.f, 0.f, 0.f, 0.f};
-            if (v) {
-                const int64_t o = (b * L + ts + row) * N + c4;
-                load_k<4>(Bp + o, tb, true);
-                if constexpr (WANT_C) load_k<4>(Cp + o, tc, true);
-            }
+            const int f = tid + kThreads * i;
+            const int tens = f / NCH, fc = f % NCH;
+            const int row = fc / (NP / 4), c4 = (fc % (NP / 4)) * 4;
+            float t4[4] = {0.f, 0.f, 0.f, 0.f};
+            if (tens < ntens && row < nv)
+                load_k<4>((tens == 0 ? Bp : Cp) + (b * L + ts + row) * N + c4, t4, true);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                r.b[4 * i + k] = tb[k];
-                r.c[4 * i + k] = tc[k];
-            }
+            for (int k = 0; k < 4; ++k) r.bc[4 * i + k] = t4[k];
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < BCE; ++i) {
-            const int e = lane + 64 * i;
-            const int row = e / NP, n = e % NP;
-            const bool v = e < kTile * NP && row < nv && n < N;
-            const int64_t o = (b * L + ts + row) * N + n;
-            r.b[i] = v ? to_f32(Bp[o]) : 0.0f;
-            r.c[i] = (WANT_C && v) ? to_f32(Cp[o]) : 0.0f;
+        for (int i = 0; i < RawTile<NP>::BCS; ++i) {
+            const int e = tid + kThreads * i;
+            const int tens = e / (kTile * NP), ec = e % (kTile * NP);
+            const int row = ec / NP, n = ec % NP;
+            const bool v = tens < ntens && row < nv && n < N;
+            r.bc[i] = v ? to_f32((tens == 0 ? Bp : Cp)[(b * L + ts + row) * N + n]) : 0.0f;
         }
     }
 }
 
+// B and C go to LDS transposed, [state][token] with a padded row of
+// kTile + 4 floats, so that a lane reads four consecutive tokens of its
+// state with one 16-byte access.
+constexpr int kTS = kTile + 4;
+
 template <int NP, bool WANT_C>
-__device__ __forceinline__ void store_bc(const RawTile<NP> &r, float *sB, float *sC, int lane, bool vecBC) {
-    constexpr int BCE = RawTile<NP>::BCS;
+__device__ __forceinline__ void store_bc(const RawTile<NP> &r, float *sB, float *sC, int tid, bool vecBC) {
+    constexpr int NCH = RawTile<NP>::NCH;
+    const int ntens = WANT_C ? 2 : 1;
     if (vecBC) {
-        constexpr int NCH = kTile * NP / 4;
 #pragma unroll
         for (int i = 0; i < RawTile<NP>::BCV / 4; ++i) {
-            const int f = lane + 64 * i;
-            if (f < NCH) {
-                const int row = f / (NP / 4), c4 = (f % (NP / 4)) * 4;
-                *reinterpret_cast<float4 *>(sB + row * NP + c4) =
-                    make_float4(r.b[4 * i], r.b[4 * i + 1], r.b[4 * i + 2], r.b[4 * i + 3]);
-                if constexpr (WANT_C)
-                    *reinterpret_cast<float4 *>(sC + row * NP + c4) =
-                        make_float4(r.c[4 * i], r.c[4 * i + 1], r.c[4 * i + 2], r.c[4 * i + 3]);
+            const int f = tid + kThreads * i;
+            const int tens = f / NCH, fc = f % NCH;
+            if (tens < ntens) {
+                const int row = fc / (NP / 4), c4 = (fc % (NP / 4)) * 4;
+                float *dst = (tens == 0 ? sB : sC);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) dst[(c4 + k) * kTS + row] = r.bc[4 * i + k];
             }
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < BCE; ++i) {
-            const int e = lane + 64 * i;
-            if (e < kTile * NP) {
-                sB[e] = r.b[i];
-                if constexpr (WANT_C) sC[e] = r.c[i];
-            }
+        for (int i = 0; i < RawTile<NP>::BCS; ++i) {
+            const int e = tid + kThreads * i;
+            const int tens = e / (kTile * NP), ec = e % (kTile * NP);
+            if (tens < ntens) (tens == 0 ? sB : sC)[(ec % NP) * kTS + ec / NP] = r.bc[i];
         }
     }
+}
+
+// Quad transpose-reduce: lane j of each lane quad holds partial sums p[i]
+// for four consecutive tokens; on return lane j holds the quad's sum for
+// token j, associated as ((lane0 + lane1) + (lane2 + lane3)).
+__device__ __forceinline__ float quad_transpose_sum(const float (&p)[4], int j) {
+    const bool odd = (j & 1) != 0, high = (j & 2) != 0;
+    float v[2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const float mine = odd ? p[2 * m + 1] : p[2 * m];
+        const float send = odd ? p[2 * m] : p[2 * m + 1];
+        v[m] = mine + dpp_f<kDppQuadSwap1>(send);
+    }
+    const float mine = high ? v[1] : v[0];
+    const float send = high ? v[0] : v[1];
+    return mine + dpp_f<kDppQuadSwap2>(send);
 }
 
 template <int K>
@@ -173,16 +189,21 @@ __device__ __forceinline__ void lds_read_k(const float *p, float (&o)[K]) {
     }
 }
 
+// One block = four wavefronts = 16 channels of one batch row and one time
+// chunk.  Wavefront w, lane-quad position j of channel ch owns states
+// n = (4w + j)*SPL .. +SPL-1.
 template <typename IOT, int SPL, int DISC, bool CONV, int MODE>
-__global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     constexpr int T = kTile;
-    constexpr int NP = kLPC * SPL;
+    constexpr int NP = 16 * SPL;
     constexpr bool FINAL = MODE == MODE_FINAL;
-    __shared__ float s_x[CONV ? (T + 8) * kXS : 1];
-    __shared__ float4 s_pk[T][kCPW];      // per (token, channel): {dt, dt*u or u, gate, Dskip*u}
-    __shared__ __align__(16) float s_B[T * NP];
-    __shared__ __align__(16) float s_C[FINAL ? T * NP : 1];
-    __shared__ float s_y[FINAL ? T : 1][kXS];   // gated outputs of the tile
+    // LDS, token-minor ([channel or state][token]) with padded rows
+    __shared__ float s_x[CONV ? (T + 8) * kXS : 1];               // raw conv input, [token][channel]
+    __shared__ __align__(16) float2 s_dl[kCPW][T + 2];            // {dt, dt*u} (ZOH: {dt, u})
+    __shared__ __align__(16) float2 s_gd[FINAL ? kCPW : 1][T + 2];  // {gate, Dskip*u}
+    __shared__ __align__(16) float s_B[NP * kTS];
+    __shared__ __align__(16) float s_C[FINAL ? NP * kTS : 1];
+    __shared__ __align__(16) float s_yp[FINAL ? 4 : 1][FINAL ? kCPW : 1][kTS];  // per-wavefront readout partials
 
     const IOT *X = static_cast<const IOT *>(p.x);
     const IOT *DT = static_cast<const IOT *>(p.dt);
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
     const IOT *Z = FINAL ? static_cast<const IOT *>(p.z) : nullptr;
     IOT *Y = static_cast<IOT *>(p.y);
 
-    const int lane = threadIdx.x;
+    const int tid = threadIdx.x;
     const int64_t bid = blockIdx.x;
     const int64_t g = bid % p.groups;
     const int64_t rest = bid / p.groups;
@@ -203,16 +224,17 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
     const int64_t t1 = min(L, t0 + p.chunk);
     const int ntiles = (int)((t1 - t0 + T - 1) / T);
 
-    // scan role: four lanes per channel, SPL states each
-    const int ch = lane / kLPC, q = lane % kLPC;
+    // scan role
+    const int wv = tid >> 6, lane = tid & 63;
+    const int ch = lane >> 2, j = lane & 3;
     const int64_t d = d0 + ch;
     const bool dvalid = d < D;
     const int64_t dc = dvalid ? d : (D - 1);
-    const int n0 = q * SPL;
+    const int n0 = (wv * 4 + j) * SPL;
     const int nvalid = max(0, min(SPL, (int)(N - n0)));
     const bool vecN = (N % 4) == 0;
-    // transform role: one channel, eight consecutive rows of the tile
-    const int tc = lane & 15, rg = lane >> 4;
+    // transform / output role
+    const int tc = tid & 15, rp = tid >> 4;
     const int64_t td = d0 + tc;
     const bool tvalid = td < D;
     const int64_t tdc = tvalid ? td : (D - 1);
@@ -220,17 +242,17 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
 
     float A2[SPL], An[SPL], Ainv[SPL], h[SPL];
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        const bool v = j < nvalid;
-        const float A = neg_exp_f(v ? p.A_log[dc * N + n0 + j] : 0.0f);
-        A2[j] = v ? A * kLog2e : 0.0f;
-        An[j] = A;
-        Ainv[j] = 1.0f / A;
-        h[j] = 0.0f;
+    for (int s = 0; s < SPL; ++s) {
+        const bool v = s < nvalid;
+        const float A = neg_exp_f(v ? p.A_log[dc * N + n0 + s] : 0.0f);
+        A2[s] = v ? A * kLog2e : 0.0f;
+        An[s] = A;
+        Ainv[s] = 1.0f / A;
+        h[s] = 0.0f;
     }
     if (p.init != nullptr && nvalid > 0)
         load_k_guard<SPL>(p.init + b * p.init_bstride + (int64_t)k * p.init_kstride + dc * N + n0, h, nvalid,
-                          vecN);
+                          vecN && (SPL % 4 == 0));
 
     const float dtb = p.dt_bias ? p.dt_bias[tdc] : 0.0f;
     const float Dd = p.Dskip ? p.Dskip[tdc] : 0.0f;
@@ -253,17 +275,17 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
     };
 
     RawTile<NP> raw;
-    float xh[8];          // raw conv input of the previous tile's last 8 rows (rg == 3 lanes)
+    float xh[kRows];   // raw conv input of the previous tile (threads holding its last 8 rows)
 
-    // Per-(token, channel) quantities, computed once per tile element.
+    // Per-(token, channel) quantities, once per tile element.
     auto transform = [&](int nv) {
-        float uu[8];
+        float uu[kRows];
         if constexpr (CONV) {
-            float win[15];
+            float win[kRows + 7];
 #pragma unroll
-            for (int i = 0; i < 15; ++i) win[i] = s_x[(rg * 8 + 1 + i) * kXS + tc];
+            for (int i = 0; i < kRows + 7; ++i) win[i] = s_x[(rp * kRows + 1 + i) * kXS + tc];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
+            for (int i = 0; i < kRows; ++i) {
                 float acc = cb;
 #pragma unroll
                 for (int kk = 0; kk < 8; ++kk) acc = fmaf(wk[kk], win[i + kk], acc);
@@ -271,26 +293,17 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) uu[i] = raw.x[i];
+            for (int i = 0; i < kRows; ++i) uu[i] = raw.x[i];
         }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = rg * 8 + i;
-            if (row < nv) {
-                const float dl = softplus_f(raw.dt[i] + dtb);
-                float4 v;
-                v.x = dl;
-                v.y = (DISC == DISC_DB) ? dl * uu[i] : uu[i];
-                if constexpr (FINAL) {
-                    v.z = (Z != nullptr) ? silu_f(raw.z[i]) : 1.0f;
-                    v.w = Dd * uu[i];
-                } else {
-                    v.z = 0.0f;
-                    v.w = 0.0f;
-                }
-                s_pk[row][tc] = v;
-            }
+        for (int i = 0; i < kRows; ++i) {
+            const int row = rp * kRows + i;
+            const float dl = softplus_f(raw.dt[i] + dtb);
+            s_dl[tc][row] = make_float2(dl, (DISC == DISC_DB) ? dl * uu[i] : uu[i]);
+            if constexpr (FINAL)
+                s_gd[tc][row] = make_float2((Z != nullptr) ? silu_f(raw.z[i]) : 1.0f, Dd * uu[i]);
         }
+        (void)nv;
     };
 
     auto stage = [&](int it) {
@@ -298,27 +311,87 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
         const int nv = (int)min((int64_t)T, t1 - ts);
         if constexpr (CONV) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) s_x[(8 + rg * 8 + i) * kXS + tc] = raw.x[i];
+            for (int i = 0; i < kRows; ++i) s_x[(8 + rp * kRows + i) * kXS + tc] = raw.x[i];
         }
-        store_bc<NP, FINAL>(raw, s_B, s_C, lane, vecBC);
+        store_bc<NP, FINAL>(raw, s_B, s_C, tid, vecBC);
         __syncthreads();
         transform(nv);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) xh[i] = raw.x[i];
+        for (int i = 0; i < kRows; ++i) xh[i] = raw.x[i];
         __syncthreads();
     };
 
     auto fetch = [&](int it) {
         const int64_t ts = t0 + (int64_t)it * T;
         const int nv = (int)min((int64_t)T, t1 - ts);
-        load_raw<IOT, NP, FINAL>(raw, X, DT, Z, Bp, Cp, b, L, D, N, ts, nv, tdc, tvalid, rg, lane, vecBC);
+        load_raw<IOT, NP, FINAL>(raw, X, DT, Z, Bp, Cp, b, L, D, N, ts, nv, tdc, tvalid, rp, tid, vecBC);
     };
 
     float ssum = 0.0f;
+    // one token (tail of the last tile)
+    auto scan_step = [&](int t) {
+        const float2 pk = s_dl[ch][t];
+        const float dl = pk.x;
+        float part = 0.0f;
+#pragma unroll
+        for (int s2 = 0; s2 < SPL; ++s2) {
+            const float bq = s_B[(n0 + s2) * kTS + t];
+            const float a = hw_exp2(dl * A2[s2]);
+            float w;
+            if constexpr (DISC == DISC_DB)
+                w = pk.y * bq;
+            else
+                w = expm1f(dl * An[s2]) * Ainv[s2] * bq * pk.y;
+            h[s2] = fmaf(a, h[s2], w);
+            if constexpr (FINAL) part = fmaf(s_C[(n0 + s2) * kTS + t], h[s2], part);
+        }
+        if constexpr (FINAL) {
+            s_yp[wv][ch][t] = group_sum<4>(part);   // all lanes of the quad write the same value
+        } else {
+            ssum += dl;
+        }
+    };
+    // four tokens t .. t+3: 16-byte LDS reads, one transposed quad reduction
+    auto scan_group = [&](int t) {
+        const float4 d01 = *reinterpret_cast<const float4 *>(&s_dl[ch][t]);
+        const float4 d23 = *reinterpret_cast<const float4 *>(&s_dl[ch][t + 2]);
+        const float dl[4] = {d01.x, d01.z, d23.x, d23.z};
+        const float dy[4] = {d01.y, d01.w, d23.y, d23.w};
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s2 = 0; s2 < SPL; ++s2) {
+            const float4 b4 = *reinterpret_cast<const float4 *>(&s_B[(n0 + s2) * kTS + t]);
+            const float bq[4] = {b4.x, b4.y, b4.z, b4.w};
+            float cq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if constexpr (FINAL) {
+                const float4 c4 = *reinterpret_cast<const float4 *>(&s_C[(n0 + s2) * kTS + t]);
+                cq[0] = c4.x; cq[1] = c4.y; cq[2] = c4.z; cq[3] = c4.w;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float a = hw_exp2(dl[i] * A2[s2]);
+                float w;
+                if constexpr (DISC == DISC_DB)
+                    w = dy[i] * bq[i];
+                else
+                    w = expm1f(dl[i] * An[s2]) * Ainv[s2] * bq[i] * dy[i];
+                h[s2] = fmaf(a, h[s2], w);
+                if constexpr (FINAL) part[i] = fmaf(cq[i], h[s2], part[i]);
+            }
+        }
+        if constexpr (FINAL) {
+            s_yp[wv][ch][t + j] = quad_transpose_sum(part, j);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ssum += dl[i];
+        }
+    };
+
+    constexpr int kHaloRp = (T - 8) / kRows;   // first thread row-group holding the last 8 rows
     if (ntiles > 0) {
         fetch(0);
         if constexpr (CONV) {
-            if (rg == 0) {
+            if (rp == 0) {
 #pragma unroll
                 for (int i = 0; i < 8; ++i) s_x[i * kXS + tc] = x_before(t0 - 8 + i);
             }
@@ -326,57 +399,38 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
         stage(0);
         if (ntiles > 1) fetch(1);
     }
-    auto scan_step = [&](int t) {
-        const float4 pk = s_pk[t][ch];
-        float Bq[SPL], Cq[SPL];
-        lds_read_k<SPL>(s_B + t * NP + n0, Bq);
-        if constexpr (FINAL) lds_read_k<SPL>(s_C + t * NP + n0, Cq);
-        const float dl = pk.x;
-        float yacc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) {
-            const float a = hw_exp2(dl * A2[j]);
-            float w;
-            if constexpr (DISC == DISC_DB)
-                w = pk.y * Bq[j];
-            else
-                w = expm1f(dl * An[j]) * Ainv[j] * Bq[j] * pk.y;
-            h[j] = fmaf(a, h[j], w);
-            if constexpr (FINAL) yacc = fmaf(Cq[j], h[j], yacc);
-        }
-        if constexpr (FINAL) {
-            // every lane of the quad holds the sum; all write the same value
-            s_y[t][ch] = (group_sum<kLPC>(yacc) + pk.w) * pk.z;
-        } else {
-            ssum += dl;
-        }
-    };
-
     for (int it = 0; it < ntiles; ++it) {
         const int64_t ts = t0 + (int64_t)it * T;
         const int nv = (int)min((int64_t)T, t1 - ts);
         if (nv == T) {
-            // full tile: straight-line code, LDS reads hoisted ahead of the math
 #pragma unroll
-            for (int t = 0; t < T; ++t) scan_step(t);
+            for (int t = 0; t < T; t += 4) scan_group(t);
         } else {
-            for (int t = 0; t < nv; ++t) scan_step(t);
+            int t = 0;
+            for (; t + 4 <= nv; t += 4) scan_group(t);
+            for (; t < nv; ++t) scan_step(t);
         }
         __syncthreads();
         if constexpr (FINAL) {
+            // readout: ((w0 + w1) + (w2 + w3)) + Dskip*u, then the gate
             if (tvalid) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int row = rg * 8 + i;
-                    if (row < nv) store_io(Y + (b * L + ts + row) * D + td, s_y[row][tc]);
+                for (int i = 0; i < kRows; ++i) {
+                    const int row = rp * kRows + i;
+                    if (row < nv) {
+                        const float2 gd = s_gd[tc][row];
+                        const float ys = (s_yp[0][tc][row] + s_yp[1][tc][row]) +
+                                         (s_yp[2][tc][row] + s_yp[3][tc][row]);
+                        store_io(Y + (b * L + ts + row) * D + td, (ys + gd.y) * gd.x);
+                    }
                 }
             }
         }
         if (it + 1 < ntiles) {
             if constexpr (CONV) {
-                if (rg == 3) {
+                if (rp >= kHaloRp) {
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) s_x[i * kXS + tc] = xh[i];
+                    for (int i = 0; i < kRows; ++i) s_x[(rp * kRows + i - (T - 8)) * kXS + tc] = xh[i];
                 }
             }
             stage(it + 1);
@@ -387,16 +441,16 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
     if constexpr (FINAL) {
         if (k == p.K - 1) {
             if (dvalid && p.hT != nullptr && nvalid > 0)
-                store_k<SPL>(p.hT + (b * D + d) * N + n0, h, nvalid, vecN);
+                store_k<SPL>(p.hT + (b * D + d) * N + n0, h, nvalid, vecN && (SPL % 4 == 0));
             if constexpr (CONV) {
-                if (p.conv_state_out != nullptr && rg == 0 && tvalid) {
+                if (p.conv_state_out != nullptr && rp == 0 && tvalid) {
                     // the last W-1 conv inputs: staged rows of the last tile, or
                     // the carried history when the sequence is empty
                     const int64_t tl = t0 + (int64_t)max(ntiles - 1, 0) * T;
-                    for (int j = 0; j < W - 1; ++j) {
-                        const int64_t tt = L - (W - 1) + j;
+                    for (int jj = 0; jj < W - 1; ++jj) {
+                        const int64_t tt = L - (W - 1) + jj;
                         const float v = (ntiles > 0) ? s_x[(int)(tt - (tl - 8)) * kXS + tc] : x_before(tt);
-                        p.conv_state_out[(b * (W - 1) + j) * D + td] = v;
+                        p.conv_state_out[(b * (W - 1) + jj) * D + td] = v;
                     }
                 }
             }
@@ -404,8 +458,8 @@ __global__ __launch_bounds__(64) void scan_fwd_kernel(FwdParams p) {
     } else {
         if (dvalid) {
             const int64_t o = (b * p.K + k) * D + d;
-            if (nvalid > 0) store_k<SPL>(p.agg_h + o * N + n0, h, nvalid, vecN);
-            if (q == 0) p.agg_s[o] = ssum;
+            if (nvalid > 0) store_k<SPL>(p.agg_h + o * N + n0, h, nvalid, vecN && (SPL % 4 == 0));
+            if (wv == 0 && j == 0) p.agg_s[o] = ssum;
         }
     }
 }
@@ -440,7 +494,7 @@ hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int64_t blocks = (int64_t)p.groups * p.Kgrid * p.B;
     if (blocks <= 0) return hipSuccess;
     hipLaunchKernelGGL((scan_fwd_kernel<IOT, SPL, DISC, CONV, MODE>),
-                       dim3((unsigned)blocks), dim3(64), 0, s, p);
+                       dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -462,11 +516,9 @@ hipError_t dispatch_mode(const FwdParams &p, int disc, bool conv, int mode, hipS
 
 template <typename IOT>
 hipError_t dispatch_spl(const FwdParams &p, int disc, bool conv, int mode, hipStream_t s) {
-    if (p.N <= 4) return dispatch_mode<IOT, 1>(p, disc, conv, mode, s);
-    if (p.N <= 8) return dispatch_mode<IOT, 2>(p, disc, conv, mode, s);
-    if (p.N <= 16) return dispatch_mode<IOT, 4>(p, disc, conv, mode, s);
-    if (p.N <= 32) return dispatch_mode<IOT, 8>(p, disc, conv, mode, s);
-    return dispatch_mode<IOT, 16>(p, disc, conv, mode, s);
+    if (p.N <= 16) return dispatch_mode<IOT, 1>(p, disc, conv, mode, s);
+    if (p.N <= 32) return dispatch_mode<IOT, 2>(p, disc, conv, mode, s);
+    return dispatch_mode<IOT, 4>(p, disc, conv, mode, s);
 }
 
 hipError_t dispatch(const FwdParams &p, int bf16, int disc, bool conv, int mode, hipStream_t s) {
@@ -499,13 +551,14 @@ int64_t num_chunks(int64_t L, int64_t chunk) {
 
 int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N) {
     (void)N;
-    const int64_t waves = B * ((D + kCPW - 1) / kCPW);
-    if (waves >= 640 || L <= 512) return L > 0 ? L : 1;
-    int64_t K = (2048 + waves - 1) / waves;
-    K = std::min<int64_t>(K, (L + 255) / 256);
+    // aim for three four-wavefront blocks per CU (256 CUs)
+    const int64_t blocks = B * ((D + kCPW - 1) / kCPW);
+    if (blocks >= 512 || L <= 2 * kTile) return L > 0 ? L : 1;
+    int64_t K = (768 + blocks - 1) / blocks;
+    K = std::min<int64_t>(K, (L + 4 * kTile - 1) / (4 * kTile));
     if (K <= 1) return L;
     int64_t chunk = (L + K - 1) / K;
-    chunk = (chunk + 7) / 8 * 8;
+    chunk = (chunk + kTile - 1) / kTile * kTile;
     return chunk;
 }
 

@@ -16,9 +16,10 @@
 //
 // Arithmetic follows the sequence kernel operation by operation: the same
 // conv tap order, softplus, decay 2^(dt*A*log2 e) with A = -exp(A_log), and
-// a readout summed as ((p0 + p1) + (p2 + p3)) over the four state groups the
-// sequence kernel gives its four lanes -- so for N <= 16 a token-by-token
-// decode reproduces the full forward bit for bit.
+// the same readout tree -- per-lane partials over the sequence kernel's
+// states per lane, pairwise within lane quads, then pairwise across the four
+// wavefronts -- so a token-by-token decode reproduces the full forward bit
+// for bit.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -30,9 +31,9 @@ namespace {
 constexpr int kSPL = 16;   // states per lane
 enum { DISC_DB = 0, DISC_ZOH = 1 };
 
-// LPC lanes per channel; G = states per readout group (the sequence
-// kernel's states per lane for this N); MAXW = widest conv carried.
-template <typename IOT, int LPC, int G, int DISC, bool CONV, int MAXW>
+// LPC lanes per channel, 16 states per lane; VL = states per lane of the
+// sequence kernel (readout leaves); MAXW = widest conv carried.
+template <typename IOT, int LPC, int VL, int DISC, bool CONV, int MAXW>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     const IOT *X = static_cast<const IOT *>(a.x);
     const IOT *DT = static_cast<const IOT *>(a.dt);
@@ -100,9 +101,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
     const float dl = softplus_f(dtr + dtb);
     const float du = dl * uu;
-    float part[kSPL / G];
+    float part[kSPL / VL];
 #pragma unroll
-    for (int gI = 0; gI < kSPL / G; ++gI) part[gI] = 0.0f;
+    for (int gI = 0; gI < kSPL / VL; ++gI) part[gI] = 0.0f;
 #pragma unroll
     for (int j = 0; j < kSPL; ++j) {
         const bool v = j < nvalid;
@@ -115,20 +116,22 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
         else
             w = expm1f(dl * A) * (1.0f / A) * Bq[j] * uu;
         hq[j] = fmaf(dec, hq[j], w);
-        part[j / G] = fmaf(Cq[j], hq[j], part[j / G]);
+        part[j / VL] = fmaf(Cq[j], hq[j], part[j / VL]);
     }
     if (active && nvalid > 0) store_k<kSPL>(hp, hq, nvalid, vecN);
-    // pairwise in the order of the sequence kernel's lane-quad reduction
+    // the sequence kernel's tree: quads of leaves, then quads pairwise
+    constexpr int NQ = kSPL / VL / 4;
+    float Q[NQ];
+#pragma unroll
+    for (int qi = 0; qi < NQ; ++qi)
+        Q[qi] = (part[4 * qi] + part[4 * qi + 1]) + (part[4 * qi + 2] + part[4 * qi + 3]);
     float ysum;
-    if constexpr (kSPL / G >= 4) {
-        ysum = (part[0] + part[1]) + (part[2] + part[3]);
-#pragma unroll
-        for (int gI = 4; gI < kSPL / G; ++gI) ysum += part[gI];
-    } else {
-        ysum = 0.0f;
-#pragma unroll
-        for (int gI = 0; gI < kSPL / G; ++gI) ysum += part[gI];
-    }
+    if constexpr (NQ == 4)
+        ysum = (Q[0] + Q[1]) + (Q[2] + Q[3]);
+    else if constexpr (NQ == 2)
+        ysum = Q[0] + Q[1];
+    else
+        ysum = Q[0];
     ysum = group_sum<LPC>(ysum);
     // readout in the sequence kernel's order: (sum_n C h + Dskip*u) * SiLU(z)
     float yv = ysum + Dd * uu;
@@ -146,14 +149,14 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
 }
 
-template <typename IOT, int LPC, int G>
+template <typename IOT, int LPC, int VL>
 hipError_t launch_g(const StepArgs &a, hipStream_t s) {
     const int64_t threads = a.nblk * a.S * a.D * LPC;
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     const bool conv = a.W > 0;
 #define SSM_STEP_CASE(DI, CV, MW)                                                                        \
     if (a.disc == DI && conv == CV && (!CV || a.W <= MW)) {                                              \
-        hipLaunchKernelGGL((step_kernel<IOT, LPC, G, DI, CV, MW>), dim3(blocks), dim3(256), 0, s, a); \
+        hipLaunchKernelGGL((step_kernel<IOT, LPC, VL, DI, CV, MW>), dim3(blocks), dim3(256), 0, s, a); \
         return hipGetLastError();                                                                        \
     }
     SSM_STEP_CASE(DISC_DB, false, 1)
@@ -168,11 +171,9 @@ hipError_t launch_g(const StepArgs &a, hipStream_t s) {
 
 template <typename IOT>
 hipError_t launch_io(const StepArgs &a, hipStream_t s) {
-    // readout groups mirror the sequence kernel's states per lane (N <= 16)
-    if (a.N <= 4) return launch_g<IOT, 1, 1>(a, s);
-    if (a.N <= 8) return launch_g<IOT, 1, 2>(a, s);
-    if (a.N <= 16) return launch_g<IOT, 1, 4>(a, s);
-    if (a.N <= 32) return launch_g<IOT, 2, 4>(a, s);
+    // one lane per 16 states; readout leaves = the sequence kernel's states per lane
+    if (a.N <= 16) return launch_g<IOT, 1, 1>(a, s);
+    if (a.N <= 32) return launch_g<IOT, 2, 2>(a, s);
     return launch_g<IOT, 4, 4>(a, s);
 }
 
