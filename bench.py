@@ -24,6 +24,31 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+COPY_PROBE_ELEMS = 1 << 26          # 256 MiB read + 256 MiB written
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_B8_L2048_traffic.md")
+FWD_SOURCE = os.path.join(ROOT, "selective_state_space_ssm_amd", "csrc", "scan_fwd.hip")
+
+
+def measured_traffic():
+    """HBM bytes per launch of the forward kernel from the committed counter
+    summary, if it was taken on the current kernel source (else None)."""
+    import hashlib
+    try:
+        txt = open(TRAFFIC_FILE).read()
+        sha = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
+    except OSError:
+        return None
+    vals = {}
+    for line in txt.splitlines():
+        if ":" in line and line.strip().startswith("- "):
+            k, v = line.strip()[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != sha:
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(*a):
@@ -135,7 +160,7 @@ def main():
                    "batch": B, "seq_len": L, "d_inner": D, "d_state": N, "conv_width": W,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
                      "kernel": "scan_fwd_kernel", "algorithmic_bytes_per_launch": nbytes,
                      "avg_launch_us": round(kern_ms * 1e3, 3)},
     }
@@ -151,11 +176,13 @@ def main():
             log("extra workloads failed: %r" % (e,))
             extra["error"] = repr(e)
     if args.copy_probe:
-        n = 1 << 28
-        a = torch.empty(n, device="cuda")
+        # a plain elementwise kernel of known size (reads 4n bytes, writes 4n
+        # bytes): the reference that FETCH_SIZE / WRITE_SIZE are scaled by
+        n = COPY_PROBE_ELEMS
+        a = torch.ones(n, device="cuda")
         bb = torch.empty(n, device="cuda")
-        for _ in range(5):
-            bb.copy_(a)
+        for _ in range(3):
+            torch.neg(a, out=bb)
         torch.cuda.synchronize()
         extra["copy_probe_bytes_each_way"] = n * 4
     out["extra"] = extra

@@ -1,6 +1,6 @@
 // abi.cpp -- the library's C ABI (include/ssm.h): argument validation on the
 // host, before any HIP call, then dispatch to the kernel launchers.
-#include "../../include/ssm.h"
+#include "ssm.h"
 
 #include <hip/hip_runtime.h>
 

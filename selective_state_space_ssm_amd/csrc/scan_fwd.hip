@@ -38,6 +38,7 @@ namespace ssm {
 namespace {
 
 constexpr int kCPW = 16;            // channels per block
+constexpr int kNumXcd = 8;          // XCDs of an MI355X
 enum { MODE_FINAL = 0, MODE_LOCAL = 1 };
 enum { DISC_DB = 0, DISC_ZOH = 1 };
 
@@ -213,7 +214,12 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     IOT *Y = static_cast<IOT *>(p.y);
 
     const int tid = threadIdx.x;
-    const int64_t bid = blockIdx.x;
+    // XCD-aware order: the hardware deals block ids round-robin over the 8
+    // XCDs; remapping gives each XCD a contiguous range of logical blocks, so
+    // neighbouring channel groups (which share 128-byte lines of every token
+    // row) and all groups of one batch row (which share its B, C rows) meet
+    // in the same L2.
+    const int64_t bid = xcd_remap((int64_t)blockIdx.x, (int64_t)gridDim.x, kNumXcd);
     const int64_t g = bid % p.groups;
     const int64_t rest = bid / p.groups;
     const int k = (int)(rest % p.Kgrid);
