@@ -12,20 +12,25 @@
 //   gate:   dyv = dy*z*s,  dz = dy*yv*s*(1 + z*(1-s)),  s = sigmoid(z)
 //   dA_log = A * dA,  d_dt_raw = ddt * sigmoid(dt_raw + dt_bias)
 //
-// Structure.
-//  1. States at every T-token boundary come from the forward's two-level
-//     machinery (local chunk scans + carry walk), fully parallel over time.
-//  2. scan_bwd_kernel: one 256-thread block per (batch, 64 channels) walks
-//     the tiles from last to first.  For each tile it re-runs the forward for
-//     T tokens from the boundary state, keeping h and the decays in
-//     registers, then sweeps the tile backwards.  Four lanes own a channel
-//     exactly as in the forward; per-channel sums over the lane quad use DPP.
-//     dB and dC are sums over channels: each 16-lane row first adds its four
-//     channels with DPP row shifts, then the block's 16 row partials go to
-//     fixed LDS slots and are added in a fixed order, so the result is
-//     deterministic; one partial per block lands in the workspace.
-//  3. Two small kernels add the per-block partials (dB, dC) and the
-//     per-batch partials (dA_log, dDskip, d_dt_bias).
+// Work decomposition.  A workgroup of twelve wavefronts owns 48 channels of
+// one batch row (256 workgroups at batch 8, D = 1536: one per CU).  Each
+// channel is one 16-lane row; lane l of the row holds states l, l+16, ...
+// (S per lane).  Sums over a channel's states (the readout yv, the dt and u
+// gradients) stay inside a row: transposed DPP reductions leave token k's
+// sum in lane k.  Sums over channels (dB, dC) add the four rows of a
+// wavefront with lane swaps and then the twelve wavefronts in LDS, giving one
+// deterministic partial per workgroup.  Lane l also does the per-token work
+// (softplus, sigmoid, gate, stores) of token l of each 16-token tile of its
+// channel; the row reads those values back with DPP row broadcasts.
+//
+//  phase 1: the workgroup walks its sequence forward once and writes the
+//           state at every tile start (the checkpoints);
+//  phase 2: tiles from last to first: re-run the tile forward from its
+//           checkpoint (the states stay in registers, the readout yv is
+//           rebuilt for dz), then sweep it backwards, recomputing decays.
+// Each tile's inputs are loaded into registers one tile ahead and staged in
+// LDS.  Two small kernels add the per-workgroup dB, dC partials and the
+// per-batch dA_log, dDskip, d_dt_bias partials, in a fixed order.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -34,13 +39,18 @@
 namespace ssm {
 namespace {
 
-constexpr int kLPC = 4;
-constexpr int kCPB = 64;        // channels per block (4 wavefronts)
-constexpr int kSlots = 16;      // 16-lane rows per block
+constexpr int kCPB = 48;                 // channels per workgroup
+constexpr int kWaves = kCPB / 4;         // four channels (rows) per wavefront
+constexpr int kThreads = kWaves * 64;
 enum { DISC_DB = 0, DISC_ZOH = 1 };
 
-template <int SPL>
-constexpr int tile_for() { return SPL <= 4 ? 16 : (SPL == 8 ? 8 : 4); }
+// S states per lane (16 lanes per channel), T tokens per tile.
+template <int S>
+struct BGeo {
+    static constexpr int NP = 16 * S;
+    static constexpr int T = 16 / S;
+    static constexpr int TP = (T + 15) / 16;   // tokens per lane in the per-token work
+};
 
 struct BwdParams {
     const void *u, *dt;
@@ -49,24 +59,77 @@ struct BwdParams {
     const float *Dskip;
     const void *z;
     const void *dy;
-    const float *dhT;
-    const float *ckpt;       // [B, K, D, N] states at tile starts
+    const float *h0, *dhT;
+    float *ckpt;             // [B, K, D, N] states at tile starts
     void *du, *ddt, *dz;
     float *dh0;
-    float *pB, *pC;          // [G, B, L, N] per-block channel partials
+    float *pB, *pC;          // [G, B, L, N] per-workgroup channel partials
     float *pA;               // [B, D, N]   dLoss/dA summed over time
     float *pD, *pT;          // [B, D]      dDskip, d_dt_bias summed over time
     int64_t B, L, D, N;
     int K;                   // tiles along time
-    int G;                   // channel blocks
+    int G;                   // channel workgroups per batch row
 };
 
-template <typename IOT, int SPL, int DISC>
-__global__ __launch_bounds__(256) void scan_bwd_kernel(BwdParams p) {
-    constexpr int T = tile_for<SPL>();
-    constexpr int NP = kLPC * SPL;
-    __shared__ float redB[kSlots][T][NP];
-    __shared__ float redC[kSlots][T][NP];
+constexpr int kRowMirror = 0x140;       // lane l <- 15 - l within each row
+constexpr int kRowHalfMirror = 0x141;   // lane l <- l ^ 7 within each half row
+
+// Lane K of the row, broadcast to the whole 16-lane row.
+template <int K>
+__device__ __forceinline__ float row_bcast(float v) {
+    return dpp_f<0x150 + K>(v);
+}
+
+// Transposed row reduction: p[k] is this lane's partial for token k; lane l
+// receives the sum over its 16-lane row of p[l].  Pairings: l^15 (row
+// mirror), l^7 (half-row mirror), l^2, l^1; each lane keeps the half of the
+// tokens named by its own lane bit, so token bits end equal to lane bits.
+__device__ __forceinline__ float row_transpose_sum(const float (&p)[16], int l) {
+    float v8[8], v4[4], v2[2];
+    const bool b3 = (l & 8) != 0, b2 = (l & 4) != 0, b1 = (l & 2) != 0, b0 = (l & 1) != 0;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const float mine = b3 ? p[k + 8] : p[k];
+        const float send = b3 ? p[k] : p[k + 8];
+        v8[k] = mine + dpp_f<kRowMirror>(send);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float mine = b2 ? v8[k + 4] : v8[k];
+        const float send = b2 ? v8[k] : v8[k + 4];
+        v4[k] = mine + dpp_f<kRowHalfMirror>(send);
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const float mine = b1 ? v4[k + 2] : v4[k];
+        const float send = b1 ? v4[k] : v4[k + 2];
+        v2[k] = mine + dpp_f<kDppQuadSwap2>(send);
+    }
+    const float mine = b0 ? v2[1] : v2[0];
+    const float send = b0 ? v2[0] : v2[1];
+    return mine + dpp_f<kDppQuadSwap1>(send);
+}
+
+// Sum over the four 16-lane rows of the wavefront, in every lane, as
+// (row0 + row1) + (row2 + row3), through the gfx950 lane swaps.
+__device__ __forceinline__ float sum_rows(float v) {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float p = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+}
+
+template <typename IOT, int S, int DISC>
+__global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
+    using Gm = BGeo<S>;
+    constexpr int NP = Gm::NP, T = Gm::T, TP = Gm::TP;
+    constexpr int XE = T * kCPB;          // elements of one [T][48] tile
+    constexpr int BE = T * NP;            // elements of one [T][NP] tile
+    constexpr int XL = (XE + kThreads - 1) / kThreads;   // staged per thread
+    constexpr int BL = (BE + kThreads - 1) / kThreads;
+    __shared__ float s_u[XE], s_dt[XE], s_z[XE], s_dy[XE];
+    __shared__ float s_B[BE], s_C[BE];
+    __shared__ float s_rB[T][kWaves][NP], s_rC[T][kWaves][NP];
 
     const IOT *U = static_cast<const IOT *>(p.u);
     const IOT *DT = static_cast<const IOT *>(p.dt);
@@ -80,193 +143,356 @@ __global__ __launch_bounds__(256) void scan_bwd_kernel(BwdParams p) {
 
     const int tid = threadIdx.x;
     const int wv = tid >> 6, lane = tid & 63;
-    const int ch = lane / kLPC, q = lane % kLPC;
-    const int row = lane >> 4;
-    const int64_t gblk = blockIdx.x % p.G;
+    const int rw = lane >> 4, l = lane & 15;
+    const int cl = wv * 4 + rw;                 // channel within the workgroup
+    const int64_t grp = blockIdx.x % p.G;
     const int64_t b = blockIdx.x / p.G;
-    const int64_t d = gblk * kCPB + wv * 16 + ch;
-    const bool dvalid = d < p.D;
-    const int64_t dc = dvalid ? d : (p.D - 1);
     const int64_t N = p.N, D = p.D, L = p.L;
-    const int n0 = q * SPL;
-    const int nvalid = max(0, min(SPL, (int)(N - n0)));
-    const bool vecN = (N % 4) == 0;
+    const int64_t d0 = grp * kCPB;
+    const int64_t d = d0 + cl;
+    const bool dvalid = d < D;
+    const int64_t dc = dvalid ? d : (D - 1);
     const bool gate = Z != nullptr;
-    const float vmask = dvalid ? 1.0f : 0.0f;
+    const int K = p.K;
 
-    float A2[SPL], An[SPL], Ainv[SPL];
+    // this lane's states n = l + 16 s
+    float A2[S], An[S], Ainv[S];
+    bool sv[S];
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) {
-        const bool v = j < nvalid;
-        const float A = neg_exp_f(v ? p.A_log[dc * N + n0 + j] : 0.0f);
-        A2[j] = v ? A * kLog2e : 0.0f;
-        An[j] = A;
-        Ainv[j] = 1.0f / A;
+    for (int s = 0; s < S; ++s) {
+        const int n = l + 16 * s;
+        sv[s] = n < N;
+        const float A = neg_exp_f(sv[s] ? p.A_log[dc * N + n] : 0.0f);
+        A2[s] = sv[s] ? A * kLog2e : 0.0f;
+        An[s] = A;
+        Ainv[s] = 1.0f / A;
     }
     const float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
     const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
 
-    float gad[SPL], dAt[SPL];
+    // ---- tile staging: registers one tile ahead, then LDS.  Values out of
+    // range (tokens past L, channels past D, states past N) stage as zeros.
+    float ru[XL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL];
+    auto fetch = [&](int k, bool bwd) {
+        const int64_t ts = (int64_t)k * T;
 #pragma unroll
-    for (int j = 0; j < SPL; ++j) { gad[j] = 0.0f; dAt[j] = 0.0f; }
-    if (p.dhT != nullptr && dvalid && nvalid > 0)
-        load_k_guard<SPL>(p.dhT + (b * D + d) * N + n0, gad, nvalid, vecN);
-    float dDt = 0.0f, dTt = 0.0f;
+        for (int q = 0; q < XL; ++q) {
+            const int e = q * kThreads + tid;
+            const int tt = e / kCPB, cc = e % kCPB;
+            const bool v = e < XE && ts + tt < L && d0 + cc < D;
+            const int64_t o = (b * L + ts + tt) * D + d0 + cc;
+            ru[q] = v ? to_f32(U[o]) : 0.0f;
+            rdt[q] = v ? to_f32(DT[o]) : 0.0f;
+            if (bwd) {
+                rz[q] = (v && gate) ? to_f32(Z[o]) : 0.0f;
+                rdy[q] = v ? to_f32(DY[o]) : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < BL; ++q) {
+            const int e = q * kThreads + tid;
+            const int tt = e / NP, n = e % NP;
+            const bool v = e < BE && ts + tt < L && n < N;
+            const int64_t o = (b * L + ts + tt) * N + n;
+            rB[q] = v ? to_f32(Bp[o]) : 0.0f;
+            if (bwd) rC[q] = v ? to_f32(Cp[o]) : 0.0f;
+        }
+    };
+    auto stage = [&](bool bwd) {
+#pragma unroll
+        for (int q = 0; q < XL; ++q) {
+            const int e = q * kThreads + tid;
+            if (e < XE) {
+                s_u[e] = ru[q];
+                s_dt[e] = rdt[q];
+                if (bwd) {
+                    s_z[e] = rz[q];
+                    s_dy[e] = rdy[q];
+                }
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < BL; ++q) {
+            const int e = q * kThreads + tid;
+            if (e < BE) {
+                s_B[e] = rB[q];
+                if (bwd) s_C[e] = rC[q];
+            }
+        }
+    };
 
-    for (int c = p.K - 1; c >= 0; --c) {
-        const int64_t t0 = (int64_t)c * T;
-        const int len = (int)min((int64_t)T, L - t0);
-        float hs[T + 1][SPL], as[T][SPL], yv[T];
-        load_k_guard<SPL>(p.ckpt + ((b * p.K + c) * D + dc) * N + n0, hs[0], nvalid, vecN);
+    // per-token quantities of this lane's tokens tt = l + 16 jj of the tile;
+    // tokens past L get dt = u = 0, which leaves the state unchanged
+    float tk_dl[TP], tk_du[TP], tk_u[TP];
+    auto transform_fwd = [&](int64_t ts) {
+#pragma unroll
+        for (int jj = 0; jj < TP; ++jj) {
+            const int tt = l + 16 * jj;
+            const bool v = tt < T && ts + tt < L;
+            const int e = min(tt, T - 1) * kCPB + cl;
+            const float uu = v ? s_u[e] : 0.0f;
+            const float dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
+            tk_dl[jj] = dl;
+            tk_u[jj] = uu;
+            tk_du[jj] = (DISC == DISC_DB) ? dl * uu : uu;
+        }
+    };
+    // token i's per-token value, broadcast across the row from lane i mod 16
+    auto tokv = [&](const float (&v)[TP], int i) -> float {
+        const float src = v[i >> 4];
+        switch (i & 15) {
+            case 0: return row_bcast<0>(src);
+            case 1: return row_bcast<1>(src);
+            case 2: return row_bcast<2>(src);
+            case 3: return row_bcast<3>(src);
+            case 4: return row_bcast<4>(src);
+            case 5: return row_bcast<5>(src);
+            case 6: return row_bcast<6>(src);
+            case 7: return row_bcast<7>(src);
+            case 8: return row_bcast<8>(src);
+            case 9: return row_bcast<9>(src);
+            case 10: return row_bcast<10>(src);
+            case 11: return row_bcast<11>(src);
+            case 12: return row_bcast<12>(src);
+            case 13: return row_bcast<13>(src);
+            case 14: return row_bcast<14>(src);
+            default: return row_bcast<15>(src);
+        }
+    };
 
-        // forward re-run of the tile
+    // ================= phase 1: checkpoints at every tile start
+    float h[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        h[s] = (p.h0 != nullptr && sv[s]) ? p.h0[(b * D + dc) * N + l + 16 * s] : 0.0f;
+    if (K > 1) fetch(0, false);
+    for (int k = 0; k < K; ++k) {
+        if (dvalid) {
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                if (sv[s]) p.ckpt[((b * K + k) * D + d) * N + l + 16 * s] = h[s];
+        }
+        if (k + 1 == K) break;   // the last tile's end state is not needed
+        __syncthreads();
+        stage(false);
+        __syncthreads();
+        if (k + 2 < K) fetch(k + 1, false);
+        transform_fwd((int64_t)k * T);
 #pragma unroll
         for (int i = 0; i < T; ++i) {
-            if (i < len) {
-                const int64_t t = t0 + i;
-                const int64_t e = (b * L + t) * D + dc;
-                const float uu = to_f32(U[e]);
-                const float dl = softplus_f(to_f32(DT[e]) + dtb);
-                const float du = dl * uu;
-                float Bq[SPL], Cq[SPL];
-                load_k_guard<SPL>(Bp + (b * L + t) * N + n0, Bq, nvalid, vecN);
-                if (gate) load_k_guard<SPL>(Cp + (b * L + t) * N + n0, Cq, nvalid, vecN);
-                float yacc = 0.0f;
+            const float dli = tokv(tk_dl, i), dui = tokv(tk_du, i);
 #pragma unroll
-                for (int j = 0; j < SPL; ++j) {
-                    const float a = hw_exp2(dl * A2[j]);
-                    float w;
-                    if constexpr (DISC == DISC_DB)
-                        w = du * Bq[j];
-                    else
-                        w = expm1f(dl * An[j]) * Ainv[j] * Bq[j] * uu;
-                    hs[i + 1][j] = fmaf(a, hs[i][j], w);
-                    as[i][j] = a;
-                    if (gate) yacc = fmaf(Cq[j], hs[i + 1][j], yacc);
-                }
-                if (gate) yv[i] = fmaf(Dd, uu, group_sum<kLPC>(yacc));
+            for (int s = 0; s < S; ++s) {
+                const float bq = s_B[i * NP + l + 16 * s];
+                const float a = hw_exp2(dli * A2[s]);
+                float w;
+                if constexpr (DISC == DISC_DB)
+                    w = dui * bq;
+                else
+                    w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
+                h[s] = fmaf(a, h[s], w);
+            }
+        }
+    }
+    // the checkpoints are read back by lanes of this workgroup only
+    __threadfence_block();
+
+    // ================= phase 2: tiles from last to first
+    float g[S], dA[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        g[s] = (p.dhT != nullptr && dvalid && sv[s]) ? p.dhT[(b * D + d) * N + l + 16 * s] : 0.0f;
+        dA[s] = 0.0f;
+    }
+    float accD = 0.0f, accT = 0.0f;   // over this lane's tokens: dyv*u and d_dt_raw
+    if (K > 0) fetch(K - 1, true);
+    for (int k = K - 1; k >= 0; --k) {
+        const int64_t ts = (int64_t)k * T;
+        __syncthreads();
+        stage(true);
+        __syncthreads();
+        if (k > 0) fetch(k - 1, true);
+
+        // per-token work of this lane's tokens
+        transform_fwd(ts);
+        float tk_sg[TP], tk_dyv[TP], tk_dy[TP], tk_z[TP], tk_s[TP];
+        bool tk_v[TP];
+#pragma unroll
+        for (int jj = 0; jj < TP; ++jj) {
+            const int tt = l + 16 * jj;
+            const bool v = tt < T && ts + tt < L && dvalid;
+            const int e = min(tt, T - 1) * kCPB + cl;
+            tk_v[jj] = v;
+            tk_sg[jj] = sigmoid_f(s_dt[e] + dtb);
+            const float dyr = v ? s_dy[e] : 0.0f;
+            tk_dy[jj] = dyr;
+            if (gate) {
+                const float zz = s_z[e];
+                const float sz = sigmoid_f(zz);
+                tk_z[jj] = zz;
+                tk_s[jj] = sz;
+                tk_dyv[jj] = dyr * zz * sz;
+            } else {
+                tk_z[jj] = 0.0f;
+                tk_s[jj] = 0.0f;
+                tk_dyv[jj] = dyr;
             }
         }
 
-        float dAc[SPL];
+        // forward re-run of the tile from its checkpoint; with the gate, the
+        // readout yv of each 16-token half feeds dz
+        float hs[T + 1][S];
 #pragma unroll
-        for (int j = 0; j < SPL; ++j) dAc[j] = 0.0f;
-        float dDc = 0.0f, dTc = 0.0f;
-
-        // reverse sweep of the tile
+        for (int s = 0; s < S; ++s) hs[0][s] = sv[s] ? p.ckpt[((b * K + k) * D + dc) * N + l + 16 * s] : 0.0f;
 #pragma unroll
-        for (int i = T - 1; i >= 0; --i) {
-            if (i < len) {
-                const int64_t t = t0 + i;
-                const int64_t e = (b * L + t) * D + dc;
-                const float uu = to_f32(U[e]);
-                const float r = to_f32(DT[e]) + dtb;
-                const float dl = softplus_f(r);
-                const float sg = sigmoid_f(r);
-                const float dyr = to_f32(DY[e]) * vmask;
-                float dyv, dzv = 0.0f;
-                if (gate) {
-                    const float zz = to_f32(Z[e]);
-                    const float s = sigmoid_f(zz);
-                    dyv = dyr * zz * s;
-                    dzv = dyr * yv[i] * s * (1.0f + zz * (1.0f - s));
-                } else {
-                    dyv = dyr;
-                }
-                dDc = fmaf(dyv, uu, dDc);
-                float Bq[SPL], Cq[SPL];
-                load_k_guard<SPL>(Bp + (b * L + t) * N + n0, Bq, nvalid, vecN);
-                load_k_guard<SPL>(Cp + (b * L + t) * N + n0, Cq, nvalid, vecN);
-                const float du = dl * uu;
-                float ddt_p = 0.0f, du_p = 0.0f;
-                float bpart[SPL], cpart[SPL];
+        for (int jj = 0; jj < TP; ++jj) {
+            float yp[16];
 #pragma unroll
-                for (int j = 0; j < SPL; ++j) {
-                    const float gj = fmaf(Cq[j], dyv, gad[j]);
-                    cpart[j] = hs[i + 1][j] * dyv;
-                    const float a = as[i][j];
-                    const float daa = gj * hs[i][j] * a;
-                    if constexpr (DISC == DISC_DB) {
-                        const float gB = gj * Bq[j];
-                        ddt_p = fmaf(daa, An[j], ddt_p);
-                        ddt_p = fmaf(gB, uu, ddt_p);
-                        du_p += gB;
-                        bpart[j] = gj * du;
-                        dAc[j] = fmaf(daa, dl, dAc[j]);
-                    } else {
-                        const float em1 = expm1f(dl * An[j]);
-                        const float cz = em1 * Ainv[j];
-                        const float gBu = gj * Bq[j] * uu;
-                        ddt_p = fmaf(daa, An[j], ddt_p);
-                        ddt_p = fmaf(gBu, a, ddt_p);
-                        du_p = fmaf(gj * cz, Bq[j], du_p);
-                        bpart[j] = gj * cz * uu;
-                        dAc[j] = fmaf(daa, dl, dAc[j]);
-                        dAc[j] = fmaf(gBu * (dl * a * An[j] - em1), Ainv[j] * Ainv[j], dAc[j]);
+            for (int kk = 0; kk < 16; ++kk) {
+                const int i = 16 * jj + kk;
+                yp[kk] = 0.0f;
+                if (i < T) {
+                    const float dli = tokv(tk_dl, i), dui = tokv(tk_du, i);
+                    float yacc = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        const float bq = s_B[i * NP + l + 16 * s];
+                        const float a = hw_exp2(dli * A2[s]);
+                        float w;
+                        if constexpr (DISC == DISC_DB)
+                            w = dui * bq;
+                        else
+                            w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
+                        hs[i + 1][s] = fmaf(a, hs[i][s], w);
+                        if (gate) yacc = fmaf(s_C[i * NP + l + 16 * s], hs[i + 1][s], yacc);
                     }
-                    gad[j] = a * gj;
+                    yp[kk] = yacc;
                 }
-                const float ddt = group_sum<kLPC>(ddt_p);
-                const float dup = group_sum<kLPC>(du_p);
+            }
+            if (gate) {
+                const float yv = fmaf(Dd, tk_u[jj], row_transpose_sum(yp, l));
+                if (tk_v[jj] && DZ != nullptr) {
+                    const float sz = tk_s[jj];
+                    store_io(DZ + (b * L + ts + l + 16 * jj) * D + d,
+                             tk_dy[jj] * yv * sz * (1.0f + tk_z[jj] * (1.0f - sz)));
+                }
+            }
+        }
+
+        // reverse sweep, in halves of 16 tokens for the per-token reductions
+#pragma unroll
+        for (int jj = TP - 1; jj >= 0; --jj) {
+            float pdt[16], pdu[16];
+#pragma unroll
+            for (int kk = 15; kk >= 0; --kk) {
+                const int i = 16 * jj + kk;
+                pdt[kk] = 0.0f;
+                pdu[kk] = 0.0f;
+                if (i < T) {
+                    const float dyv = tokv(tk_dyv, i);
+                    const float dli = tokv(tk_dl, i);
+                    const float uu = tokv(tk_u, i);
+                    const float dui = (DISC == DISC_DB) ? tokv(tk_du, i) : uu;
+                    float pt = 0.0f, pu = 0.0f;
+#pragma unroll
+                    for (int s = 0; s < S; ++s) {
+                        const float bq = s_B[i * NP + l + 16 * s];
+                        const float cq = s_C[i * NP + l + 16 * s];
+                        const float gj = fmaf(cq, dyv, g[s]);
+                        const float a = hw_exp2(dli * A2[s]);   // recomputed: registers hold h only
+                        const float daa = gj * hs[i][s] * a;
+                        float bpart;
+                        if constexpr (DISC == DISC_DB) {
+                            const float gB = gj * bq;
+                            pt = fmaf(daa, An[s], pt);
+                            pt = fmaf(gB, uu, pt);
+                            pu += gB;
+                            bpart = gj * dui;
+                            dA[s] = fmaf(daa, dli, dA[s]);
+                        } else {
+                            const float em1 = expm1f(dli * An[s]);
+                            const float cz = em1 * Ainv[s];
+                            const float gBu = gj * bq * uu;
+                            pt = fmaf(daa, An[s], pt);
+                            pt = fmaf(gBu, a, pt);
+                            pu = fmaf(gj * cz, bq, pu);
+                            bpart = gj * cz * uu;
+                            dA[s] = fmaf(daa, dli, dA[s]);
+                            dA[s] = fmaf(gBu * (dli * a * An[s] - em1), Ainv[s] * Ainv[s], dA[s]);
+                        }
+                        const float cpart = hs[i + 1][s] * dyv;
+                        g[s] = a * gj;
+                        // dB, dC: the wavefront's four channels, then LDS
+                        const float sb = sum_rows(bpart);
+                        const float sc = sum_rows(cpart);
+                        if (rw == 0) {
+                            s_rB[i][wv][l + 16 * s] = sb;
+                            s_rC[i][wv][l + 16 * s] = sc;
+                        }
+                    }
+                    pdt[kk] = pt;
+                    pdu[kk] = pu;
+                }
+            }
+            // lane l finishes token l + 16 jj
+            const float ddt = row_transpose_sum(pdt, l);
+            const float dup = row_transpose_sum(pdu, l);
+            if (tk_v[jj]) {
+                const int tt = l + 16 * jj;
+                const float dyv = tk_dyv[jj];
                 float duv;
                 if constexpr (DISC == DISC_DB)
-                    duv = fmaf(dl, dup, Dd * dyv);
+                    duv = fmaf(tk_dl[jj], dup, Dd * dyv);
                 else
                     duv = fmaf(Dd, dyv, dup);
-                const float ddr = ddt * sg;
-                dTc += ddr;
-                if (q == 0 && dvalid) {
-                    const int64_t eo = (b * L + t) * D + d;
-                    if (DU) store_io(DU + eo, duv);
-                    if (DDT) store_io(DDT + eo, ddr);
-                    if (DZ && gate) store_io(DZ + eo, dzv);
-                }
-                // channel sums for dB, dC: four channels of each 16-lane row
-#pragma unroll
-                for (int j = 0; j < SPL; ++j) {
-                    bpart[j] = row_stride4_sum(bpart[j]);
-                    cpart[j] = row_stride4_sum(cpart[j]);
-                }
-                if ((lane & 15) >= 12) {
-                    const int slot = wv * 4 + row;
-#pragma unroll
-                    for (int j = 0; j < SPL; ++j) {
-                        redB[slot][i][n0 + j] = bpart[j];
-                        redC[slot][i][n0 + j] = cpart[j];
-                    }
-                }
+                const float ddr = ddt * tk_sg[jj];
+                accD = fmaf(dyv, tk_u[jj], accD);
+                accT += ddr;
+                const int64_t eo = (b * L + ts + tt) * D + d;
+                if (DU) store_io(DU + eo, duv);
+                if (DDT) store_io(DDT + eo, ddr);
             }
         }
         __syncthreads();
-        for (int e2 = tid; e2 < T * NP; e2 += 256) {
-            const int i = e2 / NP, n = e2 % NP;
-            if (i < len && n < N) {
+        // dB, dC partials of this workgroup: the twelve wavefronts in order
+        for (int e = tid; e < T * NP; e += kThreads) {
+            const int i = e / NP, n = e % NP;
+            if (n < N && ts + i < L) {
                 float sb = 0.0f, sc = 0.0f;
 #pragma unroll
-                for (int s2 = 0; s2 < kSlots; ++s2) {
-                    sb += redB[s2][i][n];
-                    sc += redC[s2][i][n];
+                for (int w = 0; w < kWaves; ++w) {
+                    sb += s_rB[i][w][n];
+                    sc += s_rC[i][w][n];
                 }
-                const int64_t o = ((gblk * p.B + b) * L + t0 + i) * N + n;
+                const int64_t o = ((grp * p.B + b) * L + ts + i) * N + n;
                 p.pB[o] = sb;
                 p.pC[o] = sc;
             }
         }
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < SPL; ++j) dAt[j] += dAc[j];
-        dDt += dDc;
-        dTt += dTc;
     }
 
+    // per-channel sums over the row's lanes (each holds its own tokens'),
+    // in a fixed order: lane 0 of the row receives the total
+    float pD[16], pT[16];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+        pD[kk] = kk == 0 ? accD : 0.0f;
+        pT[kk] = kk == 0 ? accT : 0.0f;
+    }
+    const float sD = row_transpose_sum(pD, l);
+    const float sT = row_transpose_sum(pT, l);
     if (dvalid) {
-        if (nvalid > 0) {
-            if (p.dh0 != nullptr) store_k<SPL>(p.dh0 + (b * D + d) * N + n0, gad, nvalid, vecN);
-            store_k<SPL>(p.pA + (b * D + d) * N + n0, dAt, nvalid, vecN);
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            if (sv[s]) {
+                const int64_t o = (b * D + d) * N + l + 16 * s;
+                if (p.dh0 != nullptr) p.dh0[o] = g[s];
+                p.pA[o] = dA[s];
+            }
         }
-        if (q == 0) {
-            p.pD[b * D + d] = dDt;
-            p.pT[b * D + d] = dTt;
+        if (l == 0) {
+            p.pD[b * D + d] = sD;
+            p.pT[b * D + d] = sT;
         }
     }
 }
@@ -306,7 +532,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_params(const float *A_log, con
 }
 
 struct BwdWs {
-    float *ckpt, *aggs, *pB, *pC, *pA, *pD, *pT;
+    float *ckpt, *pB, *pC, *pA, *pD, *pT;
 };
 
 int tile_len(int64_t N) { return N <= 16 ? 16 : (N <= 32 ? 8 : 4); }
@@ -324,7 +550,6 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, size_t *total)
         return ptr;
     };
     r.ckpt = take((size_t)(B * K * D * N));
-    r.aggs = take((size_t)(B * K * D));
     r.pB = take((size_t)(G * B * L * N));
     r.pC = take((size_t)(G * B * L * N));
     r.pA = take((size_t)(B * D * N));
@@ -334,23 +559,24 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, size_t *total)
     return r;
 }
 
-template <typename IOT, int SPL>
+template <typename IOT, int S>
 hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s) {
     BwdParams p{};
     p.u = a.u; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
-    p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z; p.dy = a.dy; p.dhT = a.dhT;
+    p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z; p.dy = a.dy;
+    p.h0 = a.h0; p.dhT = a.dhT;
     p.ckpt = w.ckpt;
     p.du = a.du; p.ddt = a.ddt; p.dz = a.dz; p.dh0 = a.dh0;
     p.pB = w.pB; p.pC = w.pC; p.pA = w.pA; p.pD = w.pD; p.pT = w.pT;
     p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N;
-    constexpr int T = tile_for<SPL>();
-    p.K = (int)std::max<int64_t>(1, (a.L + T - 1) / T);
+    constexpr int T = BGeo<S>::T;
+    p.K = (int)((a.L + T - 1) / T);
     p.G = (int)((a.D + kCPB - 1) / kCPB);
     const int64_t blocks = (int64_t)p.G * a.B;
     if (a.disc == DISC_ZOH)
-        hipLaunchKernelGGL((scan_bwd_kernel<IOT, SPL, DISC_ZOH>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((scan_bwd_kernel<IOT, SPL, DISC_DB>), dim3((unsigned)blocks), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = a.B * a.L * a.N;
@@ -367,12 +593,10 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
 }
 
 template <typename IOT>
-hipError_t launch_bwd_spl(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s) {
-    if (a.N <= 4) return launch_bwd_typed<IOT, 1>(a, w, s);
-    if (a.N <= 8) return launch_bwd_typed<IOT, 2>(a, w, s);
-    if (a.N <= 16) return launch_bwd_typed<IOT, 4>(a, w, s);
-    if (a.N <= 32) return launch_bwd_typed<IOT, 8>(a, w, s);
-    return launch_bwd_typed<IOT, 16>(a, w, s);
+hipError_t launch_bwd_s(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s) {
+    if (a.N <= 16) return launch_bwd_typed<IOT, 1>(a, w, s);
+    if (a.N <= 32) return launch_bwd_typed<IOT, 2>(a, w, s);
+    return launch_bwd_typed<IOT, 4>(a, w, s);
 }
 
 }  // namespace
@@ -385,14 +609,8 @@ size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
 
 hipError_t launch_scan_bwd(const ScanBwdArgs &a, hipStream_t s) {
     BwdWs w = carve(a.ws, a.B, a.L, a.D, a.N, nullptr);
-    ScanFwdArgs f{};
-    f.B = a.B; f.L = a.L; f.D = a.D; f.N = a.N; f.W = 0; f.bf16 = a.bf16; f.disc = a.disc;
-    f.x = a.u; f.dt = a.dt; f.dt_bias = a.dt_bias; f.A_log = a.A_log; f.Bm = a.Bm; f.Cm = a.Cm;
-    f.h0 = a.h0;
-    hipError_t e = launch_scan_checkpoints(f, tile_len(a.N), w.ckpt, w.aggs, s);
-    if (e != hipSuccess) return e;
-    if (a.bf16) return launch_bwd_spl<bf16_t>(a, w, s);
-    return launch_bwd_spl<float>(a, w, s);
+    if (a.bf16) return launch_bwd_s<bf16_t>(a, w, s);
+    return launch_bwd_s<float>(a, w, s);
 }
 
 }  // namespace ssm
