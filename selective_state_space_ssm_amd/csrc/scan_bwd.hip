@@ -71,45 +71,6 @@ struct BwdParams {
     int G;                   // channel workgroups per batch row
 };
 
-constexpr int kRowMirror = 0x140;       // lane l <- 15 - l within each row
-constexpr int kRowHalfMirror = 0x141;   // lane l <- l ^ 7 within each half row
-
-// Lane K of the row, broadcast to the whole 16-lane row.
-template <int K>
-__device__ __forceinline__ float row_bcast(float v) {
-    return dpp_f<0x150 + K>(v);
-}
-
-// Transposed row reduction: p[k] is this lane's partial for token k; lane l
-// receives the sum over its 16-lane row of p[l].  Pairings: l^15 (row
-// mirror), l^7 (half-row mirror), l^2, l^1; each lane keeps the half of the
-// tokens named by its own lane bit, so token bits end equal to lane bits.
-__device__ __forceinline__ float row_transpose_sum(const float (&p)[16], int l) {
-    float v8[8], v4[4], v2[2];
-    const bool b3 = (l & 8) != 0, b2 = (l & 4) != 0, b1 = (l & 2) != 0, b0 = (l & 1) != 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float mine = b3 ? p[k + 8] : p[k];
-        const float send = b3 ? p[k] : p[k + 8];
-        v8[k] = mine + dpp_f<kRowMirror>(send);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float mine = b2 ? v8[k + 4] : v8[k];
-        const float send = b2 ? v8[k] : v8[k + 4];
-        v4[k] = mine + dpp_f<kRowHalfMirror>(send);
-    }
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {
-        const float mine = b1 ? v4[k + 2] : v4[k];
-        const float send = b1 ? v4[k] : v4[k + 2];
-        v2[k] = mine + dpp_f<kDppQuadSwap2>(send);
-    }
-    const float mine = b0 ? v2[1] : v2[0];
-    const float send = b0 ? v2[0] : v2[1];
-    return mine + dpp_f<kDppQuadSwap1>(send);
-}
-
 // Sum over the four 16-lane rows of the wavefront, in every lane, as
 // (row0 + row1) + (row2 + row3), through the gfx950 lane swaps.
 __device__ __forceinline__ float sum_rows(float v) {
