@@ -43,11 +43,6 @@ int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N);
 size_t scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int W,
                                 int64_t chunk_len);
 hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s);
-// States at the start of every `chunk`-token chunk ([B, K, D, N], K =
-// ceil(L / chunk)), from h0; agg_s is [B, K, D] scratch.  No conv (x is u).
-hipError_t launch_scan_checkpoints(const ScanFwdArgs &a, int64_t chunk, float *ckpt, float *agg_s,
-                                   hipStream_t s);
-
 struct ScanBwdArgs {
     int64_t B, L, D, N;
     int bf16;

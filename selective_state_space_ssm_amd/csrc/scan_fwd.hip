@@ -619,28 +619,4 @@ hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s) {
     return dispatch(p, a.bf16, a.disc, conv, MODE_FINAL, s);
 }
 
-hipError_t launch_scan_checkpoints(const ScanFwdArgs &a, int64_t chunk, float *ckpt, float *agg_s,
-                                   hipStream_t s) {
-    // States at the start of every chunk of `chunk` tokens: local scans of
-    // chunks 0 .. K-2, then the carry walk writes the exact starting states.
-    FwdParams p{};
-    p.x = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
-    p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip;
-    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N; p.W = 0;
-    p.groups = (int)((a.D + kCPW - 1) / kCPW);
-    const int64_t K = num_chunks(a.L, chunk);
-    p.chunk = chunk;
-    p.K = (int)K;
-    p.agg_h = ckpt; p.agg_s = agg_s;
-    if (K > 1) {
-        p.Kgrid = (int)K - 1;
-        hipError_t e = dispatch(p, a.bf16, a.disc, false, MODE_LOCAL, s);
-        if (e != hipSuccess) return e;
-    }
-    const int64_t total = a.B * a.D * a.N;
-    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.A_log,
-                       a.h0, ckpt, agg_s, a.B, a.D, a.N, (int)K, nullptr, nullptr, (int64_t)0);
-    return hipGetLastError();
-}
-
 }  // namespace ssm
