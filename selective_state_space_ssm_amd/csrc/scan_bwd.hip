@@ -17,17 +17,17 @@
 // channel is one 16-lane row; lane l of the row holds states l, l+16, ...
 // (S per lane).  Sums over a channel's states (the readout yv, the dt and u
 // gradients) stay inside a row: transposed DPP reductions leave token k's
-// sum in lane k.  Sums over channels (dB, dC) add the four rows of a
-// wavefront with lane swaps and then the twelve wavefronts in LDS, giving one
-// deterministic partial per workgroup.  Lane l also does the per-token work
+// sum in lane k.  Sums over channels (dB, dC): every lane leaves its terms in
+// LDS and the workgroup adds its 48 channels per (token, state) in a fixed
+// order, one deterministic partial per workgroup.  Lane l also does the per-token work
 // (softplus, sigmoid, gate, stores) of token l of each 16-token tile of its
 // channel; the row reads those values back with DPP row broadcasts.
 //
 //  phase 1: the workgroup walks its sequence forward once and writes the
 //           state at every tile start (the checkpoints);
 //  phase 2: tiles from last to first: re-run the tile forward from its
-//           checkpoint (the states stay in registers, the readout yv is
-//           rebuilt for dz), then sweep it backwards, recomputing decays.
+//           checkpoint (states and decays stay in registers, the readout yv
+//           is rebuilt for dz), then sweep it backwards.
 // Each tile's inputs are loaded into registers one tile ahead and staged in
 // LDS.  Two small kernels add the per-workgroup dB, dC partials and the
 // per-batch dA_log, dDskip, d_dt_bias partials, in a fixed order.
@@ -71,15 +71,6 @@ struct BwdParams {
     int G;                   // channel workgroups per batch row
 };
 
-// Sum over the four 16-lane rows of the wavefront, in every lane, as
-// (row0 + row1) + (row2 + row3), through the gfx950 lane swaps.
-__device__ __forceinline__ float sum_rows(float v) {
-    const auto s16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float p = __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
-    const auto s32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
-    return __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
-}
-
 template <typename IOT, int S, int DISC>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     using Gm = BGeo<S>;
@@ -90,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     constexpr int BL = (BE + kThreads - 1) / kThreads;
     __shared__ float s_u[XE], s_dt[XE], s_z[XE], s_dy[XE];
     __shared__ float s_B[BE], s_C[BE];
-    __shared__ float s_rB[T][kWaves][NP], s_rC[T][kWaves][NP];
+    __shared__ float s_rB[T][kCPB][NP], s_rC[T][kCPB][NP];   // per-channel dB, dC terms
 
     const IOT *U = static_cast<const IOT *>(p.u);
     const IOT *DT = static_cast<const IOT *>(p.dt);
@@ -302,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 
         // forward re-run of the tile from its checkpoint; with the gate, the
         // readout yv of each 16-token half feeds dz
-        float hs[T + 1][S];
+        float hs[T + 1][S], as[T][S];
 #pragma unroll
         for (int s = 0; s < S; ++s) hs[0][s] = sv[s] ? p.ckpt[((b * K + k) * D + dc) * N + l + 16 * s] : 0.0f;
 #pragma unroll
@@ -325,6 +316,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                         else
                             w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
                         hs[i + 1][s] = fmaf(a, hs[i][s], w);
+                        as[i][s] = a;
                         if (gate) yacc = fmaf(s_C[i * NP + l + 16 * s], hs[i + 1][s], yacc);
                     }
                     yp[kk] = yacc;
@@ -360,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                         const float bq = s_B[i * NP + l + 16 * s];
                         const float cq = s_C[i * NP + l + 16 * s];
                         const float gj = fmaf(cq, dyv, g[s]);
-                        const float a = hw_exp2(dli * A2[s]);   // recomputed: registers hold h only
+                        const float a = as[i][s];
                         const float daa = gj * hs[i][s] * a;
                         float bpart;
                         if constexpr (DISC == DISC_DB) {
@@ -383,13 +375,9 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                         }
                         const float cpart = hs[i + 1][s] * dyv;
                         g[s] = a * gj;
-                        // dB, dC: the wavefront's four channels, then LDS
-                        const float sb = sum_rows(bpart);
-                        const float sc = sum_rows(cpart);
-                        if (rw == 0) {
-                            s_rB[i][wv][l + 16 * s] = sb;
-                            s_rC[i][wv][l + 16 * s] = sc;
-                        }
+                        // dB, dC terms of this channel; summed over channels below
+                        s_rB[i][cl][l + 16 * s] = bpart;
+                        s_rC[i][cl][l + 16 * s] = cpart;
                     }
                     pdt[kk] = pt;
                     pdu[kk] = pu;
@@ -415,15 +403,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             }
         }
         __syncthreads();
-        // dB, dC partials of this workgroup: the twelve wavefronts in order
+        // dB, dC partials of this workgroup: its 48 channels in order
         for (int e = tid; e < T * NP; e += kThreads) {
             const int i = e / NP, n = e % NP;
             if (n < N && ts + i < L) {
                 float sb = 0.0f, sc = 0.0f;
-#pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
-                    sb += s_rB[i][w][n];
-                    sc += s_rC[i][w][n];
+#pragma unroll 8
+                for (int c2 = 0; c2 < kCPB; ++c2) {
+                    sb += s_rB[i][c2][n];
+                    sc += s_rC[i][c2][n];
                 }
                 const int64_t o = ((grp * p.B + b) * L + ts + i) * N + n;
                 p.pB[o] = sb;

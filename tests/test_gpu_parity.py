@@ -316,8 +316,10 @@ def test_step_loop_equals_forward(ssm, disc):
                                Dskip=dev(p["Dskip"])[None], disc=disc)[0])
     torch.cuda.synchronize()
     ys = torch.stack(ys, 1)
-    assert rel_linf(ys, y) <= 1e-6
-    assert rel_linf(h[0], hT) <= 1e-6
+    # the step kernel replays the sequence kernel's operation order, readout
+    # tree included, so the decode is bit-identical
+    assert torch.equal(ys, y)
+    assert torch.equal(h[0], hT)
     assert torch.equal(cs[0], cso)
 
 
