@@ -66,7 +66,8 @@ struct FwdParams {
 };
 
 constexpr int kTile = 64;           // tokens staged per tile
-constexpr int kXS = 17;             // padded LDS row stride (16 channels + 1)
+constexpr int kXS = 20;             // LDS row stride: 16 channels + 4, so the two row groups a
+                                    // half-wavefront touches land on disjoint banks
 constexpr int kThreads = 256;       // four wavefronts per block
 constexpr int kRows = kTile / 16;   // tile rows per thread in the transform role
 
