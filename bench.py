@@ -93,7 +93,8 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=40,
+                    help="untimed launches first; the GPU needs ~10 ms of work to reach steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle's CPU timing")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
     ap.add_argument("--copy-probe", action="store_true",

@@ -8,16 +8,18 @@
 // output.
 //
 // The step is bound by memory traffic on the state (4 B read + 4 B written
-// per state coordinate against a handful of VALU ops).  One lane owns a
-// channel's 16 states (LPC = 2 or 4 lanes for N up to 32 or 64), so a
-// wavefront covers 64 consecutive channels of one stream: x, z, y and each
-// history slot move as 256-byte rows, the state as 64-byte runs per lane.
+// per state coordinate against a handful of VALU ops).  LPC lanes share a
+// channel and each holds 4 consecutive states (LPC = 4 up to N = 16), so one
+// 16-byte access per lane makes every load and store of the state and of
+// A_log one contiguous kilobyte per wavefront (16 channels x 64 B).  The
+// per-channel work (conv, softplus, gate) is repeated in the LPC lanes, which
+// compute identical values; lane 0 of the channel stores y and the history.
 // Every load of a lane is issued before any arithmetic.
 //
 // Arithmetic follows the sequence kernel operation by operation: the same
 // conv tap order, softplus, decay 2^(dt*A*log2 e) with A = -exp(A_log), and
-// the same readout tree -- per-lane partials over the sequence kernel's
-// states per lane, pairwise within lane quads, then pairwise across the four
+// the same readout tree -- chains over the sequence kernel's states per
+// lane, then pairwise within its lane quads, then pairwise across its four
 // wavefronts -- so a token-by-token decode reproduces the full forward bit
 // for bit.
 #include <algorithm>
@@ -28,11 +30,11 @@
 namespace ssm {
 namespace {
 
-constexpr int kSPL = 16;   // states per lane
+constexpr int kSPL = 4;    // states per lane
 enum { DISC_DB = 0, DISC_ZOH = 1 };
 
-// LPC lanes per channel, 16 states per lane; VL = states per lane of the
-// sequence kernel (readout leaves); MAXW = widest conv carried.
+// LPC lanes per channel, 4 states per lane; VL = states per lane of the
+// sequence kernel (its readout chains); MAXW = widest conv carried.
 template <typename IOT, int LPC, int VL, int DISC, bool CONV, int MAXW>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     const IOT *X = static_cast<const IOT *>(a.x);
@@ -119,19 +121,17 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
         part[j / VL] = fmaf(Cq[j], hq[j], part[j / VL]);
     }
     if (active && nvalid > 0) store_k<kSPL>(hp, hq, nvalid, vecN);
-    // the sequence kernel's tree: quads of leaves, then quads pairwise
-    constexpr int NQ = kSPL / VL / 4;
-    float Q[NQ];
-#pragma unroll
-    for (int qi = 0; qi < NQ; ++qi)
-        Q[qi] = (part[4 * qi] + part[4 * qi + 1]) + (part[4 * qi + 2] + part[4 * qi + 3]);
+    // the sequence kernel's tree: its chains of VL states, four chains per
+    // lane quad ((c0 + c1) + (c2 + c3)), then its four wavefronts the same
+    // way; here the lane's four states hold 4/VL chains and the rest of the
+    // tree is the pairwise reduction over the channel's LPC lanes
     float ysum;
-    if constexpr (NQ == 4)
-        ysum = (Q[0] + Q[1]) + (Q[2] + Q[3]);
-    else if constexpr (NQ == 2)
-        ysum = Q[0] + Q[1];
+    if constexpr (VL == 1)
+        ysum = (part[0] + part[1]) + (part[2] + part[3]);
+    else if constexpr (VL == 2)
+        ysum = part[0] + part[1];
     else
-        ysum = Q[0];
+        ysum = part[0];
     ysum = group_sum<LPC>(ysum);
     // readout in the sequence kernel's order: (sum_n C h + Dskip*u) * SiLU(z)
     float yv = ysum + Dd * uu;
@@ -171,10 +171,10 @@ hipError_t launch_g(const StepArgs &a, hipStream_t s) {
 
 template <typename IOT>
 hipError_t launch_io(const StepArgs &a, hipStream_t s) {
-    // one lane per 16 states; readout leaves = the sequence kernel's states per lane
-    if (a.N <= 16) return launch_g<IOT, 1, 1>(a, s);
-    if (a.N <= 32) return launch_g<IOT, 2, 2>(a, s);
-    return launch_g<IOT, 4, 4>(a, s);
+    // four states per lane; readout chains = the sequence kernel's states per lane
+    if (a.N <= 16) return launch_g<IOT, 4, 1>(a, s);
+    if (a.N <= 32) return launch_g<IOT, 8, 2>(a, s);
+    return launch_g<IOT, 16, 4>(a, s);
 }
 
 }  // namespace
