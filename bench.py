@@ -337,7 +337,8 @@ def bench_extras(torch, np, si, ssm, dev, args):
 def cpu_baseline(np, si):
     """The float64 oracle, as it stands, on the host cores: the whole
     headline forward (conv, then the scan with the gate) over all 8 batch
-    rows, five times; the mean is reported."""
+    rows with every host thread, five times (the mean is reported), and
+    batch row 0 alone on one thread."""
     import oracle
     oracle.build(force=False)
     Bs, L, D, N, W = 8, 2048, 1536, 16, 4
@@ -345,18 +346,30 @@ def cpu_baseline(np, si):
     f = lambda k: np.ascontiguousarray(p[k], np.float64)
     args = {k: f(k) for k in ("x", "dt_raw", "B", "C", "z", "dt_bias", "A_log", "Dskip", "conv_w", "conv_b")}
     del p
+
+    def run(rows):
+        sl = lambda k: args[k][rows] if args[k].ndim == 3 else args[k]
+        u, _ = oracle.conv1d_causal(sl("x"), args["conv_w"], args["conv_b"], want_state=False)
+        oracle.scan_fwd(u, sl("dt_raw"), args["A_log"], sl("B"), sl("C"), dt_bias=args["dt_bias"],
+                        Dskip=args["Dskip"], z=sl("z"))
+
+    cores = oracle.num_threads()
     reps, times = 5, []
     for _ in range(reps):
         t0 = time.perf_counter()
-        u, _ = oracle.conv1d_causal(args["x"], args["conv_w"], args["conv_b"], want_state=False)
-        oracle.scan_fwd(u, args["dt_raw"], args["A_log"], args["B"], args["C"], dt_bias=args["dt_bias"],
-                        Dskip=args["Dskip"], z=args["z"])
+        run(slice(0, Bs))
         times.append(time.perf_counter() - t0)
-        del u
     dt = sum(times) / reps
-    return {"value": Bs * L * D * N / dt, "unit": "elements/s", "cores": oracle.num_threads(), "kind": "oracle",
+    oracle.set_num_threads(1)
+    t0 = time.perf_counter()
+    run(slice(0, 1))
+    dt1 = time.perf_counter() - t0
+    oracle.set_num_threads(cores)
+    return {"value": Bs * L * D * N / dt, "unit": "elements/s", "cores": cores, "kind": "oracle",
             "sample": "the whole forward workload (conv + scan + gate, B=8, L=2048, D=1536, N=16, float64), "
-                      "%d runs, mean %.3f s per run" % (reps, dt)}
+                      "%d runs, mean %.3f s per run" % (reps, dt),
+            "single_thread": {"value": L * D * N / dt1, "unit": "elements/s", "cores": 1,
+                              "sample": "batch row 0 of the same workload, %.2f s" % dt1}}
 
 if __name__ == "__main__":
     main()

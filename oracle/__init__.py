@@ -49,6 +49,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         i64, i32, p = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
         lib.orc_num_threads.restype = ctypes.c_int
+        lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_num_threads.restype = None
         lib.orc_conv1d_causal.argtypes = [i64, i64, i64, i32, p, p, p, p, p, i32, p]
         lib.orc_scan_core.argtypes = [i64, i64, i64, i64, i32] + [p] * 13
         lib.orc_delta.argtypes = [i64, i64, i64, p, p, p]
@@ -64,6 +66,11 @@ def _load():
 
 def num_threads() -> int:
     return int(_load().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads used by the following oracle calls."""
+    _load().orc_set_num_threads(int(n))
 
 
 def _f64(a):

@@ -77,6 +77,17 @@ int orc_num_threads(void)
 #endif
 }
 
+/* Threads used by later calls (n >= 1); a no-op without OpenMP. */
+void orc_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Causal depthwise convolution ("mamba, live": xc = SiLU(depthwise_conv4(xin)),
  * 4-tap causal, per channel; TensorViz manifest step "local": left padded,

@@ -323,6 +323,46 @@ def test_step_loop_equals_forward(ssm, disc):
     assert torch.equal(cs[0], cso)
 
 
+def test_step_graph_replay(ssm):
+    """Streaming steps captured in a HIP graph (as the decode benchmark runs
+    them): every replay, with eager work and synchronisation in between,
+    reproduces the same steps run eagerly, bit for bit."""
+    S, D, N, W, steps = 8, 128, 16, 4, 4
+    p = _rand(17, S, steps, D, N, W)
+    tok = {k: dev(np.ascontiguousarray(p[k].transpose(1, 0, 2))) for k in ("x", "dt_raw", "B", "C", "z")}
+    prm = {k: dev(p[k])[None].contiguous() for k in ("A_log", "conv_w", "conv_b", "dt_bias", "Dskip")}
+    h0 = dev(p["h0"])[None].contiguous()
+    cs0 = dev(p["conv_state"])[None].contiguous()
+
+    def run(h, cs, ys):
+        for t in range(steps):
+            ssm.ssm_step(h, tok["x"][t][None], tok["dt_raw"][t][None], prm["A_log"], tok["B"][t][None],
+                         tok["C"][t][None], conv_state=cs, z=tok["z"][t][None], conv_w=prm["conv_w"],
+                         conv_b=prm["conv_b"], dt_bias=prm["dt_bias"], Dskip=prm["Dskip"], y=ys[t])
+
+    h_e, cs_e = h0.clone(), cs0.clone()
+    ys_e = torch.empty(steps, 1, S, D, device="cuda")
+    run(h_e, cs_e, ys_e)
+    torch.cuda.synchronize()
+    h_g, cs_g = h0.clone(), cs0.clone()
+    ys_g = torch.empty(steps, 1, S, D, device="cuda")
+    run(h_g, cs_g, ys_g)            # warm-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(h_g, cs_g, ys_g)
+    for _ in range(3):
+        h_g.copy_(h0)
+        cs_g.copy_(cs0)
+        ys_g.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(ys_g, ys_e)
+        assert torch.equal(h_g, h_e)
+        assert torch.equal(cs_g, cs_e)
+
+
 def test_step_bf16(ssm):
     p = _rand(16, 4, 6, 32, 16, 4, bf16=True)
     y_ref, h_ref, _ = _step_oracle_loop(p, 6)
