@@ -52,12 +52,13 @@ def _load():
         lib.orc_set_num_threads.argtypes = [ctypes.c_int]
         lib.orc_set_num_threads.restype = None
         lib.orc_conv1d_causal.argtypes = [i64, i64, i64, i32, p, p, p, p, p, i32, p]
+        lib.orc_conv1d_causal_bwd.argtypes = [i64, i64, i64, i32, p, p, p, p, i32, p, p, p, p, p]
         lib.orc_scan_core.argtypes = [i64, i64, i64, i64, i32] + [p] * 13
         lib.orc_delta.argtypes = [i64, i64, i64, p, p, p]
         lib.orc_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 12
         lib.orc_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 21
         lib.orc_step.argtypes = [i64, i64, i64, i32, i32] + [p] * 13
-        for f in (lib.orc_conv1d_causal, lib.orc_scan_core, lib.orc_delta,
+        for f in (lib.orc_conv1d_causal, lib.orc_conv1d_causal_bwd, lib.orc_scan_core, lib.orc_delta,
                   lib.orc_scan_fwd, lib.orc_scan_bwd, lib.orc_step):
             f.restype = ctypes.c_int
         _lib = lib
@@ -102,6 +103,22 @@ def conv1d_causal(x, w, bias=None, state_in=None, silu=True, want_state=True):
                                      _ptr(state_in), _ptr(so), int(bool(silu)),
                                      _ptr(y)), "conv1d_causal")
     return y, so
+
+
+def conv1d_causal_bwd(x, w, dy, bias=None, state_in=None, silu=True):
+    """orc_conv1d_causal_bwd: gradients of conv1d_causal's output (given
+    dy [B,L,D]) w.r.t. x, w [D,W], bias [D] and the history [B,W-1,D]."""
+    x, w, dy, bias, state_in = _f64(x), _f64(w), _f64(dy), _f64(bias), _f64(state_in)
+    Bn, L, D = x.shape
+    W = w.shape[1]
+    dx = np.empty((Bn, L, D))
+    dw = np.empty((D, W))
+    db = np.empty(D)
+    ds = np.empty((Bn, W - 1, D))
+    _check(_load().orc_conv1d_causal_bwd(Bn, L, D, W, _ptr(x), _ptr(w), _ptr(bias), _ptr(state_in),
+                                         int(bool(silu)), _ptr(dy), _ptr(dx), _ptr(dw), _ptr(db),
+                                         _ptr(ds)), "conv1d_causal_bwd")
+    return {"dx": dx, "dw": dw, "db": db, "dstate": ds}
 
 
 def delta(dt_raw, dt_bias=None):

@@ -137,6 +137,86 @@ int orc_conv1d_causal(int64_t B, int64_t L, int64_t D, int32_t W,
     return 0;
 }
 
+/* Backward of orc_conv1d_causal (reverse mode, written from the forward's
+ * definition).  dy is dLoss/d(output).  With silu the output is SiLU(xc), so
+ *   dxc[t] = dy[t] * s * (1 + xc[t] * (1 - s)),   s = sigmoid(xc[t]);
+ * without it dxc = dy.  From xc[t] = bias + sum_k w[k] * xt[t-(W-1)+k]:
+ *   d xt[i] = sum over (t, k) with t-(W-1)+k = i of w[k] * dxc[t]
+ *           -> dx[i] for i >= 0, dstate[W-1+i] (the history slot) for i < 0;
+ *   dw[k]   = sum over b, t of dxc[t] * xt[t-(W-1)+k];   dbias = sum dxc.
+ * dw and dbias are summed over batch rows in row order after the parallel
+ * loop, so the result does not depend on the thread count. */
+int orc_conv1d_causal_bwd(int64_t B, int64_t L, int64_t D, int32_t W,
+                          const double *x, const double *w, const double *bias,
+                          const double *state_in, int32_t silu, const double *dy,
+                          double *dx, double *dw, double *dbias, double *dstate)
+{
+    if (B < 0 || L < 0 || D < 0 || W < 1 || !w || (L > 0 && (!x || !dy)))
+        return -1;
+    int64_t rows = B * D;
+    double *pw = (double *)calloc((size_t)(rows > 0 ? rows : 1) * (size_t)W, sizeof(double));
+    double *pb = (double *)calloc((size_t)(rows > 0 ? rows : 1), sizeof(double));
+    double *dxc_all = (double *)calloc((size_t)(rows > 0 ? rows : 1) * (size_t)(L > 0 ? L : 1), sizeof(double));
+    int fail = (!pw || !pb || !dxc_all);
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        if (fail)
+            continue;
+        int64_t b = r / D, d = r % D;
+        double *dxc = dxc_all + r * (L > 0 ? L : 1);
+        for (int64_t t = 0; t < L; ++t) {
+            double acc = bias ? bias[d] : 0.0;
+            for (int32_t k = 0; k < W; ++k)
+                acc += w[d * W + k] *
+                       orc_conv_input(x, state_in, L, D, W, b, d, t - (W - 1) + k);
+            double g = dy[(b * L + t) * D + d];
+            if (silu) {
+                double sg = orc_sigmoid(acc);
+                g *= sg * (1.0 + acc * (1.0 - sg));
+            }
+            dxc[t] = g;
+            pb[r] += g;
+            for (int32_t k = 0; k < W; ++k)
+                pw[r * W + k] += g * orc_conv_input(x, state_in, L, D, W, b, d, t - (W - 1) + k);
+        }
+        /* input positions i = -(W-1) .. L-1 */
+        for (int64_t i = -(int64_t)(W - 1); i < L; ++i) {
+            double v = 0.0;
+            for (int32_t k = 0; k < W; ++k) {
+                int64_t t = i + (W - 1) - k;
+                if (t >= 0 && t < L)
+                    v += w[d * W + k] * dxc[t];
+            }
+            if (i >= 0) {
+                if (dx)
+                    dx[(b * L + i) * D + d] = v;
+            } else if (dstate) {
+                dstate[(b * (int64_t)(W - 1) + (W - 1) + i) * D + d] = v;
+            }
+        }
+    }
+    if (!fail) {
+        for (int64_t d = 0; d < D; ++d) {
+            for (int32_t k = 0; k < W; ++k) {
+                double sw = 0.0;
+                for (int64_t b = 0; b < B; ++b)
+                    sw += pw[(b * D + d) * W + k];
+                if (dw)
+                    dw[d * W + k] = sw;
+            }
+            double sb = 0.0;
+            for (int64_t b = 0; b < B; ++b)
+                sb += pb[b * D + d];
+            if (dbias)
+                dbias[d] = sb;
+        }
+    }
+    free(pw);
+    free(pb);
+    free(dxc_all);
+    return fail ? -2 : 0;
+}
+
 /* ------------------------------------------------------------------------ */
 /* Discretised input coefficient for one state coordinate.
  *  - dt*B form ("mamba, live" pseudocode; "the s6 cell"): coef = dt.

@@ -38,6 +38,8 @@ MUTANTS = {
     "bwd_dC_uses_previous_state": ("gC[t * N + n] += hh[t * N + n] * dyv;", "gC[t * N + n] += hprev * dyv;"),
     "bwd_zoh_dA_sign": ("(dt * a * An - em1)", "(dt * a * An + em1)"),
     "bwd_adjoint_not_decayed": ("                            g[n] *= a;\n", ""),
+    "conv_bwd_silu_derivative": ("g *= sg * (1.0 + acc * (1.0 - sg));", "g *= sg;"),
+    "conv_bwd_taps_reversed": ("int64_t t = i + (W - 1) - k;", "int64_t t = i + k;"),
 }
 
 

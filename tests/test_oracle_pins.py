@@ -450,3 +450,57 @@ def test_backward_without_gate_and_state(oracle_lib):
     for k in names:
         np.testing.assert_allclose(g[_GRAD_OF[k]], ts[k].grad.numpy(), rtol=1e-10, atol=1e-12,
                                    err_msg=k)
+
+
+# ------------------------------------------------------------ conv backward
+def _conv_loss(x, w, b, st, dy, silu):
+    y, _ = oracle.conv1d_causal(x, w, b, st, silu=silu, want_state=False)
+    return float(np.sum(y * dy))
+
+
+@pytest.mark.parametrize("silu", [True, False])
+def test_conv_backward_against_finite_differences(oracle_lib, silu):
+    """dx, dw, dbias and the history gradient of the conv prologue match
+    central finite differences of the oracle's own forward (float64)."""
+    r = np.random.default_rng(31)
+    x, w, b = r.standard_normal((2, 7, 3)), r.standard_normal((3, 4)), r.standard_normal(3)
+    st, dy = r.standard_normal((2, 3, 3)), r.standard_normal((2, 7, 3))
+    g = oracle.conv1d_causal_bwd(x, w, dy, bias=b, state_in=st, silu=silu)
+    args = {"dx": x, "dw": w, "db": b, "dstate": st}
+    eps = 1e-6
+    for gname, arr in args.items():
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + eps
+            lp = _conv_loss(x, w, b, st, dy, silu)
+            arr[idx] = keep - eps
+            lm = _conv_loss(x, w, b, st, dy, silu)
+            arr[idx] = keep
+            fd[idx] = (lp - lm) / (2 * eps)
+        err = np.max(np.abs(g[gname] - fd)) / max(np.max(np.abs(fd)), 1e-3)
+        assert err < 2e-7, (gname, err)
+        assert np.any(g[gname] != 0), gname
+
+
+@pytest.mark.parametrize("silu", [True, False])
+@pytest.mark.parametrize("W", [1, 4, 6])
+def test_conv_backward_against_torch_autograd(oracle_lib, silu, W):
+    """The same gradients from float64 torch autograd of
+    torch.nn.functional.conv1d (depthwise, history prepended), then SiLU."""
+    r = np.random.default_rng(32 + W)
+    Bn, L, D = 2, 9, 5
+    x, w, b = r.standard_normal((Bn, L, D)), r.standard_normal((D, W)), r.standard_normal(D)
+    st, dy = r.standard_normal((Bn, W - 1, D)), r.standard_normal((Bn, L, D))
+    tx, tw, tb, ts = (torch.tensor(a, dtype=torch.float64, requires_grad=True) for a in (x, w, b, st))
+    full = torch.cat([ts, tx], dim=1).permute(0, 2, 1)            # [B, D, W-1+L]
+    y = torch.nn.functional.conv1d(full, tw[:, None, :], tb, groups=D).permute(0, 2, 1)
+    if silu:
+        y = torch.nn.functional.silu(y)
+    (y * torch.from_numpy(dy)).sum().backward()
+    g = oracle.conv1d_causal_bwd(x, w, dy, bias=b, state_in=st if W > 1 else None, silu=silu)
+    np.testing.assert_allclose(g["dx"], tx.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g["dw"], tw.grad.numpy(), rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(g["db"], tb.grad.numpy(), rtol=1e-12, atol=1e-13)
+    if W > 1:
+        np.testing.assert_allclose(g["dstate"], ts.grad.numpy(), rtol=1e-12, atol=1e-13)
