@@ -62,10 +62,12 @@ def fwd_bytes(B, L, D, N, W, es, gate=True, conv=True):
     return per_tok + bc + params
 
 
-def bwd_bytes(B, L, D, N, es, gate=True):
-    reads = B * L * D * es * (3 + (1 if gate else 0)) + 2 * B * L * N * es   # u, dt, dy (+z), B, C
-    writes = B * L * D * es * (2 + (1 if gate else 0)) + 2 * B * L * N * es  # du, ddt (+dz), dB, dC
+def bwd_bytes(B, L, D, N, es, gate=True, W=0):
+    reads = B * L * D * es * (3 + (1 if gate else 0)) + 2 * B * L * N * es   # x, dt, dy (+z), B, C
+    writes = B * L * D * es * (2 + (1 if gate else 0)) + 2 * B * L * N * es  # dx, ddt (+dz), dB, dC
     params = 4 * (3 * D + D * N) + 4 * (3 * D + D * N)                        # read + grads written
+    if W:
+        params += 2 * 4 * (D * W + D)                                          # conv taps, bias and grads
     return reads + writes + params
 
 
@@ -226,6 +228,27 @@ def bench_extras(torch, np, si, ssm, dev, args):
                                "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": nb}
     log("backward: %.1f us" % (ms * 1e3))
 
+    # the same backward through the fused conv prologue (x in, dx, dconv_w, dconv_b out)
+    outc = {}
+
+    def bwd_conv():
+        ssm.ssm_scan_bwd(P["x"], P["dt_raw"], P["A_log"], P["B"], P["C"], P["dy"], dt_bias=P["dt_bias"],
+                         Dskip=P["Dskip"], z=P["z"], conv_w=P["conv_w"], conv_b=P["conv_b"], out=outc,
+                         workspace=ws)
+
+    for _ in range(2):
+        bwd_conv()
+    tm = EventTimer(torch)
+    for _ in range(reps):
+        tm.run(bwd_conv)
+    ms = tm.mean_ms()
+    nb = bwd_bytes(B, L, D, N, 4, W=4)
+    ex["backward_conv_fused_B8_L2048"] = {"us_per_call": round(ms * 1e3, 2),
+                                          "elements_per_s": B * L * D * N / (ms * 1e-3),
+                                          "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                          "algorithmic_bytes": nb}
+    log("backward with the conv prologue: %.1f us" % (ms * 1e3))
+
     # conv alone and the L=256 block
     tm = EventTimer(torch)
     for _ in range(reps):
@@ -233,7 +256,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
     ms = tm.mean_ms()
     nb = 2 * B * L * D * 4 + 4 * D * 5
     ex["conv1d_B8_L2048"] = {"us_per_call": round(ms * 1e3, 2), "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
-    del P, u, out, ws
+    del P, u, out, outc, ws
     torch.cuda.empty_cache()
 
     B2, L2 = 8, 256

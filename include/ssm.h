@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef int32_t ssm_status;
 #define SSM_OK 0
@@ -177,27 +177,43 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
 ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes);
 
 /*
- * ssm_scan_bwd -- gradients of ssm_scan_fwd (conv_width must be 0: u is the
- * scan input) for the loss sum(y * dy) + sum(hT * dhT).  The pages state that
- * the selection maps receive gradients (TensorViz explorer, numerical checks)
- * but give no backward; this is the reverse-mode adjoint of the recurrence:
- * with g = dLoss/dh_t, g_{t-1} = exp(dt_t*A) * g_t + C_{t-1} * dyv_{t-1}.
- *   u, dt_raw, B, C, z, dy    io  as in ssm_scan_fwd (dy [B, L, D] required)
+ * ssm_scan_bwd -- gradients of ssm_scan_fwd for the loss
+ * sum(y * dy) + sum(hT * dhT).  The pages state that the selection maps
+ * receive gradients (TensorViz explorer, numerical checks) but give no
+ * backward; this is the reverse-mode adjoint of the recurrence: with
+ * g = dLoss/dh_t, g_{t-1} = exp(dt_t*A) * g_t + C_{t-1} * dyv_{t-1}.  With
+ * conv_width > 0 the conv + SiLU prologue ("mamba, live": the 4-tap causal
+ * conv before the scan; TensorViz manifest step "local") is differentiated
+ * in the same pass: u is recomputed from x, and the gradient of u flows on
+ * through SiLU and the taps to x, conv_w, conv_b and conv_state_in.
+ *   x, dt_raw, B, C, z, dy    io  as in ssm_scan_fwd (dy [B, L, D] required)
  *   dt_bias, A_log, Dskip, h0 f32 as in ssm_scan_fwd
+ *   conv_w, conv_b, conv_state_in  f32 as in ssm_scan_fwd (conv_w required
+ *                             when conv_width > 0; all ignored when it is 0)
  *   dhT        f32 [B, D, N]  optional upstream gradient of hT
- *   du, d_dt_raw, dz   io [B, L, D]  optional outputs (dz needs z)
+ *   dx, d_dt_raw, dz   io [B, L, D]  optional outputs (dx is dLoss/dx: the
+ *                                    scan input u when conv_width is 0; dz
+ *                                    needs z)
  *   dB, dC             io [B, L, N]  optional outputs (summed over channels)
  *   d_dt_bias, dDskip  f32 [D]       optional outputs (summed over batch and time)
  *   dA_log             f32 [D, N]    optional output (summed over batch and time)
  *   dh0                f32 [B, D, N] optional output
+ *   dconv_w   f32 [D, W]      optional output (summed over batch and time)
+ *   dconv_b   f32 [D]         optional output (summed over batch and time)
+ *   dconv_state_in f32 [B, W-1, D]  optional output, the gradient of the
+ *                             carried history (written whether or not
+ *                             conv_state_in was given)
+ *   The three conv outputs must be NULL when conv_width is 0.
  *   workspace  device memory of ssm_scan_bwd_workspace_size bytes (required)
  */
-ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void *dt_raw,
+ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt_raw,
                         const float *dt_bias, const float *A_log, const void *B,
                         const void *C, const float *Dskip, const void *z,
+                        const float *conv_w, const float *conv_b, const float *conv_state_in,
                         const float *h0, const void *dy, const float *dhT,
-                        void *du, void *d_dt_raw, float *d_dt_bias, float *dA_log,
+                        void *dx, void *d_dt_raw, float *d_dt_bias, float *dA_log,
                         void *dB, void *dC, float *dDskip, void *dz, float *dh0,
+                        float *dconv_w, float *dconv_b, float *dconv_state_in,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*

@@ -88,7 +88,7 @@ def lib():
         L.ssm_scan_bwd_workspace_size.restype = i32
         L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ssm_scan_desc), ctypes.POINTER(sz)]
         L.ssm_scan_bwd.restype = i32
-        L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ssm_scan_desc)] + [p] * 21 + [sz, p]
+        L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ssm_scan_desc)] + [p] * 27 + [sz, p]
         L.ssm_step.restype = i32
         L.ssm_step.argtypes = [ctypes.POINTER(ssm_step_desc)] + [p] * 14
         _lib = L
@@ -207,36 +207,47 @@ def ssm_scan_fwd(x, dt_raw, A_log, B, C, dt_bias=None, Dskip=None, z=None, conv_
     return y
 
 
-def ssm_scan_bwd(u, dt_raw, A_log, B, C, dy, dt_bias=None, Dskip=None, z=None, h0=None, dhT=None,
-                 disc=SSM_DISC_DELTA_B, want=("du", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dD", "dz", "dh0"),
+def ssm_scan_bwd(x, dt_raw, A_log, B, C, dy, dt_bias=None, Dskip=None, z=None, conv_w=None, conv_b=None,
+                 conv_state_in=None, h0=None, dhT=None, disc=SSM_DISC_DELTA_B,
+                 want=("dx", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dD", "dz", "dh0",
+                       "dconv_w", "dconv_b", "dconv_state"),
                  out=None, workspace=None, stream=None):
     """Gradients of ssm_scan_fwd for the loss sum(y*dy) + sum(hT*dhT).
-    Returns a dict of the requested gradients (allocated unless given in
-    `out`)."""
-    Bn, L, D = u.shape
+    x is u, or the conv input when conv_w is given (then dx flows through
+    the conv + SiLU prologue).  Returns a dict of the requested gradients
+    (allocated unless given in `out`); the conv ones only with conv_w, dz only
+    with z."""
+    Bn, L, D = x.shape
     N = A_log.shape[1]
-    desc = _scan_desc(u, N, 0, disc, 0)
-    t = u.dtype
+    W = conv_w.shape[1] if conv_w is not None else 0
+    desc = _scan_desc(x, N, W, disc, 0)
+    t = x.dtype
     out = dict(out or {})
-    shapes = dict(du=((Bn, L, D), t), d_dt_raw=((Bn, L, D), t), d_dt_bias=((D,), torch.float32),
-                  dA_log=((D, N), torch.float32), dB=((Bn, L, N), t), dC=((Bn, L, N), t),
-                  dD=((D,), torch.float32), dz=((Bn, L, D), t), dh0=((Bn, D, N), torch.float32))
+    f32 = torch.float32
+    shapes = dict(dx=((Bn, L, D), t), d_dt_raw=((Bn, L, D), t), d_dt_bias=((D,), f32),
+                  dA_log=((D, N), f32), dB=((Bn, L, N), t), dC=((Bn, L, N), t),
+                  dD=((D,), f32), dz=((Bn, L, D), t), dh0=((Bn, D, N), f32),
+                  dconv_w=((D, W), f32), dconv_b=((D,), f32), dconv_state=((Bn, max(W - 1, 0), D), f32))
     for k in want:
         if k == "dz" and z is None:
             continue
+        if k.startswith("dconv") and W == 0:
+            continue
         if k not in out:
             shp, dt_ = shapes[k]
-            out[k] = torch.empty(shp, dtype=dt_, device=u.device)
-    ws = _workspace(ssm_scan_bwd_workspace_size(desc), workspace, u.device)
+            out[k] = torch.empty(shp, dtype=dt_, device=x.device)
+    ws = _workspace(ssm_scan_bwd_workspace_size(desc), workspace, x.device)
     g = out.get
     _check("ssm_scan_bwd", lib().ssm_scan_bwd(
-        ctypes.byref(desc), _ptr(u, t, "u"), _ptr(dt_raw, t, "dt_raw"), _f32(dt_bias, "dt_bias"),
+        ctypes.byref(desc), _ptr(x, t, "x"), _ptr(dt_raw, t, "dt_raw"), _f32(dt_bias, "dt_bias"),
         _f32(A_log, "A_log"), _ptr(B, t, "B"), _ptr(C, t, "C"), _f32(Dskip, "Dskip"), _ptr(z, t, "z"),
-        _f32(h0, "h0"), _ptr(dy, t, "dy"), _f32(dhT, "dhT"), _ptr(g("du"), t, "du"),
+        _f32(conv_w, "conv_w"), _f32(conv_b, "conv_b"), _f32(conv_state_in, "conv_state_in"),
+        _f32(h0, "h0"), _ptr(dy, t, "dy"), _f32(dhT, "dhT"), _ptr(g("dx"), t, "dx"),
         _ptr(g("d_dt_raw"), t, "d_dt_raw"), _f32(g("d_dt_bias"), "d_dt_bias"), _f32(g("dA_log"), "dA_log"),
         _ptr(g("dB"), t, "dB"), _ptr(g("dC"), t, "dC"), _f32(g("dD"), "dD"), _ptr(g("dz"), t, "dz"),
-        _f32(g("dh0"), "dh0"), _ptr(ws, None, "workspace"), ctypes.c_size_t(ws.numel()),
-        _stream(stream)))
+        _f32(g("dh0"), "dh0"), _f32(g("dconv_w"), "dconv_w"), _f32(g("dconv_b"), "dconv_b"),
+        _f32(g("dconv_state") if W > 1 else None, "dconv_state"),
+        _ptr(ws, None, "workspace"), ctypes.c_size_t(ws.numel()), _stream(stream)))
     return out
 
 

@@ -204,39 +204,53 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes)
     ssm_status st = check_scan_desc(desc);
     if (st != SSM_OK) return st;
     if (!bytes) return SSM_ERR_NULL_ARG;
-    if (desc->conv_width != 0) return SSM_ERR_UNSUPPORTED;
     *bytes = ssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim, desc->dstate);
     return SSM_OK;
 }
 
-ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void *dt_raw, const float *dt_bias,
+ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt_raw, const float *dt_bias,
                         const float *A_log, const void *B, const void *C, const float *Dskip, const void *z,
-                        const float *h0, const void *dy, const float *dhT, void *du, void *d_dt_raw,
-                        float *d_dt_bias, float *dA_log, void *dB, void *dC, float *dDskip, void *dz,
-                        float *dh0, void *workspace, size_t workspace_bytes, void *stream) {
+                        const float *conv_w, const float *conv_b, const float *conv_state_in, const float *h0,
+                        const void *dy, const float *dhT, void *dx, void *d_dt_raw, float *d_dt_bias,
+                        float *dA_log, void *dB, void *dC, float *dDskip, void *dz, float *dh0, float *dconv_w,
+                        float *dconv_b, float *dconv_state_in, void *workspace, size_t workspace_bytes,
+                        void *stream) {
     ssm_status st = check_scan_desc(desc);
     if (st != SSM_OK) return st;
-    if (desc->conv_width != 0) return SSM_ERR_UNSUPPORTED;
     const int64_t Bn = desc->batch, L = desc->seqlen, D = desc->dim, N = desc->dstate;
-    if (!A_log || (L > 0 && (!u || !dt_raw || !B || !C || !dy))) return SSM_ERR_NULL_ARG;
+    const int W = desc->conv_width;
+    if (!A_log || (L > 0 && (!x || !dt_raw || !B || !C || !dy)) || (W > 0 && !conv_w)) return SSM_ERR_NULL_ARG;
     if (dz && !z) return SSM_ERR_NULL_ARG;
-    for (const void *p : {(const void *)u, (const void *)dt_raw, (const void *)dt_bias, (const void *)A_log,
+    if (W == 0 && (dconv_w || dconv_b || dconv_state_in)) return SSM_ERR_BAD_SHAPE;
+    for (const void *p : {(const void *)x, (const void *)dt_raw, (const void *)dt_bias, (const void *)A_log,
                           (const void *)B, (const void *)C, (const void *)Dskip, (const void *)z,
-                          (const void *)h0, (const void *)dy, (const void *)dhT, (const void *)du,
+                          (const void *)conv_w, (const void *)conv_b, (const void *)conv_state_in,
+                          (const void *)h0, (const void *)dy, (const void *)dhT, (const void *)dx,
                           (const void *)d_dt_raw, (const void *)d_dt_bias, (const void *)dA_log,
                           (const void *)dB, (const void *)dC, (const void *)dDskip, (const void *)dz,
-                          (const void *)dh0, (const void *)workspace})
+                          (const void *)dh0, (const void *)dconv_w, (const void *)dconv_b,
+                          (const void *)dconv_state_in, (const void *)workspace})
         if (!aligned16(p)) return SSM_ERR_ALIGNMENT;
     const size_t need = ssm::scan_bwd_workspace_bytes(Bn, L, D, N);
     if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
     const int64_t es = io_size(desc->io_dtype);
-    const int64_t nbld = Bn * L * D, nbln = Bn * L * N, nbdn = Bn * D * N;
+    const int64_t nbld = Bn * L * D, nbln = Bn * L * N, nbdn = Bn * D * N, nst = Bn * (W > 0 ? W - 1 : 0) * D;
     AliasCheck ac;
-    ac.ins = {{u, nbld * es},          {dt_raw, nbld * es},          {dt_bias, dt_bias ? D * 4 : 0},
-              {A_log, D * N * 4},      {B, nbln * es},               {C, nbln * es},
-              {Dskip, Dskip ? D * 4 : 0}, {z, z ? nbld * es : 0},    {h0, h0 ? nbdn * 4 : 0},
-              {dy, nbld * es},         {dhT, dhT ? nbdn * 4 : 0}};
-    ac.outs = {{du, du ? nbld * es : 0},
+    ac.ins = {{x, nbld * es},
+              {dt_raw, nbld * es},
+              {dt_bias, dt_bias ? D * 4 : 0},
+              {A_log, D * N * 4},
+              {B, nbln * es},
+              {C, nbln * es},
+              {Dskip, Dskip ? D * 4 : 0},
+              {z, z ? nbld * es : 0},
+              {conv_w, W > 0 ? D * W * 4 : 0},
+              {conv_b, (W > 0 && conv_b) ? D * 4 : 0},
+              {conv_state_in, (W > 0 && conv_state_in) ? nst * 4 : 0},
+              {h0, h0 ? nbdn * 4 : 0},
+              {dy, nbld * es},
+              {dhT, dhT ? nbdn * 4 : 0}};
+    ac.outs = {{dx, dx ? nbld * es : 0},
                {d_dt_raw, d_dt_raw ? nbld * es : 0},
                {d_dt_bias, d_dt_bias ? D * 4 : 0},
                {dA_log, dA_log ? D * N * 4 : 0},
@@ -245,14 +259,20 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *u, const void *dt
                {dDskip, dDskip ? D * 4 : 0},
                {dz, dz ? nbld * es : 0},
                {dh0, dh0 ? nbdn * 4 : 0},
+               {dconv_w, dconv_w ? D * W * 4 : 0},
+               {dconv_b, dconv_b ? D * 4 : 0},
+               {dconv_state_in, dconv_state_in ? nst * 4 : 0},
                {workspace, (int64_t)need}};
     if (!ac.ok()) return SSM_ERR_ALIAS;
     ssm::ScanBwdArgs a{};
-    a.B = Bn; a.L = L; a.D = D; a.N = N; a.bf16 = desc->io_dtype == SSM_BF16; a.disc = desc->disc;
-    a.u = u; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.Bm = B; a.Cm = C; a.Dskip = Dskip;
+    a.B = Bn; a.L = L; a.D = D; a.N = N; a.W = W; a.bf16 = desc->io_dtype == SSM_BF16; a.disc = desc->disc;
+    a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.Bm = B; a.Cm = C; a.Dskip = Dskip;
     a.z = z; a.h0 = h0; a.dy = dy; a.dhT = dhT;
-    a.du = du; a.ddt = d_dt_raw; a.ddt_bias = d_dt_bias; a.dA_log = dA_log; a.dB = dB; a.dC = dC;
-    a.dD = dDskip; a.dz = dz; a.dh0 = dh0; a.ws = workspace;
+    a.conv_w = W > 0 ? conv_w : nullptr; a.conv_b = W > 0 ? conv_b : nullptr;
+    a.conv_state_in = W > 0 ? conv_state_in : nullptr;
+    a.dx = dx; a.ddt = d_dt_raw; a.ddt_bias = d_dt_bias; a.dA_log = dA_log; a.dB = dB; a.dC = dC;
+    a.dD = dDskip; a.dz = dz; a.dh0 = dh0;
+    a.dconv_w = dconv_w; a.dconv_b = dconv_b; a.dconv_state_in = dconv_state_in; a.ws = workspace;
     return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -45,22 +45,25 @@ size_t scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int 
 hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s);
 struct ScanBwdArgs {
     int64_t B, L, D, N;
+    int W;                   // conv width, 0 = no conv prologue
     int bf16;
     int disc;
-    const void *u, *dt;
+    const void *x, *dt;      // x is u when W == 0
     const float *dt_bias, *A_log;
     const void *Bm, *Cm;
     const float *Dskip;
     const void *z;
+    const float *conv_w, *conv_b, *conv_state_in;
     const float *h0;
     const void *dy;
     const float *dhT;
-    void *du, *ddt;
+    void *dx, *ddt;
     float *ddt_bias, *dA_log;
     void *dB, *dC;
     float *dD;
     void *dz;
     float *dh0;
+    float *dconv_w, *dconv_b, *dconv_state_in;
     void *ws;
 };
 size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N);

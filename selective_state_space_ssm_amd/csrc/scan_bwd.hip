@@ -11,6 +11,10 @@
 //           dA += da*a*dt + g*B*u*(dt*a*A - expm1(dt*A))/A^2
 //   gate:   dyv = dy*z*s,  dz = dy*yv*s*(1 + z*(1-s)),  s = sigmoid(z)
 //   dA_log = A * dA,  d_dt_raw = ddt * sigmoid(dt_raw + dt_bias)
+//   conv:   u = SiLU(xc),  xc_t = cb + sum_k w_k x_{t-(W-1)+k}  ("mamba, live", the
+//           causal conv before the scan): gx_t = du_t * s(1 + xc(1-s)), s = sigmoid(xc);
+//           dx_t = sum_k w_k gx_{t+(W-1)-k},  dw_k += gx_t x_{t-(W-1)+k},  dcb += gx_t;
+//           inputs before t = 0 come from the carried history, which gets dx too
 //
 // Work decomposition.  A workgroup of twelve wavefronts owns 48 channels of
 // one batch row (256 workgroups at batch 8, D = 1536: one per CU).  Each
@@ -30,7 +34,16 @@
 //           is rebuilt for dz), then sweep it backwards.
 // Each tile's inputs are loaded into registers one tile ahead and staged in
 // LDS.  Two small kernels add the per-workgroup dB, dC partials and the
-// per-batch dA_log, dDskip, d_dt_bias partials, in a fixed order.
+// per-batch dA_log, dDskip, d_dt_bias (and conv tap and bias) partials, in a
+// fixed order.
+//
+// With the conv prologue the raw input x is staged with 7 rows of history
+// in front of the tile and u is recomputed from it in both phases, with the
+// forward kernel's operation order (right-aligned 8-tap window).  gx, the
+// gradient at the conv output, goes to an LDS ring indexed by absolute token
+// mod 32: when tile k is finished, the first 7 tokens of tile k+1 (processed
+// before it) are still in the ring, so dx of every token of tile k is read
+// from there.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -52,36 +65,48 @@ struct BGeo {
     static constexpr int TP = (T + 15) / 16;   // tokens per lane in the per-token work
 };
 
+constexpr int kRing = 32;                // rows of the conv-output gradient ring
+
 struct BwdParams {
-    const void *u, *dt;
+    const void *u, *dt;      // u: the conv input x when the conv prologue is on
     const float *dt_bias, *A_log;
     const void *Bm, *Cm;
     const float *Dskip;
     const void *z;
     const void *dy;
     const float *h0, *dhT;
+    const float *conv_w, *conv_b, *conv_hist;   // [D, W], [D], [B, W-1, D]
+    float *dhist;            // [B, W-1, D] gradient of the carried history
     float *ckpt;             // [B, K, D, N] states at tile starts
     void *du, *ddt, *dz;
     float *dh0;
     float *pB, *pC;          // [G, B, L, N] per-workgroup channel partials
     float *pA;               // [B, D, N]   dLoss/dA summed over time
     float *pD, *pT;          // [B, D]      dDskip, d_dt_bias summed over time
+    float *pW, *pCb;         // [B, D, 8] (taps right-aligned), [B, D]: conv taps, bias
     int64_t B, L, D, N;
+    int W;
     int K;                   // tiles along time
     int G;                   // channel workgroups per batch row
 };
 
-template <typename IOT, int S, int DISC>
+template <typename IOT, int S, int DISC, bool CONV>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     using Gm = BGeo<S>;
     constexpr int NP = Gm::NP, T = Gm::T, TP = Gm::TP;
     constexpr int XE = T * kCPB;          // elements of one [T][48] tile
+    constexpr int XH = CONV ? 7 : 0;      // history rows staged in front of the first input
+    constexpr int XUE = (T + XH) * kCPB;
     constexpr int BE = T * NP;            // elements of one [T][NP] tile
     constexpr int XL = (XE + kThreads - 1) / kThreads;   // staged per thread
+    constexpr int XUL = (XUE + kThreads - 1) / kThreads;
     constexpr int BL = (BE + kThreads - 1) / kThreads;
-    __shared__ float s_u[XE], s_dt[XE], s_z[XE], s_dy[XE];
+    static_assert(T + 7 <= kRing, "ring too short");
+    __shared__ float s_u[XUE], s_dt[XE], s_z[XE], s_dy[XE];
     __shared__ float s_B[BE], s_C[BE];
     __shared__ float s_rB[T][kCPB][NP], s_rC[T][kCPB][NP];   // per-channel dB, dC terms
+    __shared__ float s_gx[CONV ? kRing * kCPB : 1];         // conv-output gradient by token mod 32
+    __shared__ float s_wk[CONV ? kCPB * 8 : 1];              // conv taps, right-aligned in 8 slots
 
     const IOT *U = static_cast<const IOT *>(p.u);
     const IOT *DT = static_cast<const IOT *>(p.dt);
@@ -121,19 +146,47 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     }
     const float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
     const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
+    // conv taps right-aligned in an 8-tap window (slot 7 multiplies the
+    // current input), kept in LDS; first read after the tile loop's barriers
+    const int W = p.W;
+    float cb = 0.0f;
+    if constexpr (CONV) {
+        if (tid < kCPB * 8) {
+            const int kk = (tid & 7) - (8 - W);
+            const int64_t dd = (d0 + (tid >> 3) < D) ? d0 + (tid >> 3) : D - 1;
+            s_wk[tid] = (kk >= 0) ? p.conv_w[dd * W + kk] : 0.0f;
+        }
+        cb = p.conv_b ? p.conv_b[dc] : 0.0f;
+    }
+    const float *wk = s_wk + cl * 8;
 
     // ---- tile staging: registers one tile ahead, then LDS.  Values out of
     // range (tokens past L, channels past D, states past N) stage as zeros.
-    float ru[XL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL];
+    float ru[XUL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL];
     auto fetch = [&](int k, bool bwd) {
         const int64_t ts = (int64_t)k * T;
+#pragma unroll
+        for (int q = 0; q < XUL; ++q) {
+            // row r of the first input holds token ts + r - XH; with the conv,
+            // tokens before 0 come from the carried history (or are zero)
+            const int e = q * kThreads + tid;
+            const int rr = e / kCPB, cc = e % kCPB;
+            const int64_t t = ts + rr - XH;
+            float v = 0.0f;
+            if (e < XUE && t < L && d0 + cc < D) {
+                if (!CONV || t >= 0)
+                    v = to_f32(U[(b * L + t) * D + d0 + cc]);
+                else if (p.conv_hist != nullptr && t >= -(int64_t)(W - 1))
+                    v = p.conv_hist[(b * (W - 1) + (W - 1) + t) * D + d0 + cc];
+            }
+            ru[q] = v;
+        }
 #pragma unroll
         for (int q = 0; q < XL; ++q) {
             const int e = q * kThreads + tid;
             const int tt = e / kCPB, cc = e % kCPB;
             const bool v = e < XE && ts + tt < L && d0 + cc < D;
             const int64_t o = (b * L + ts + tt) * D + d0 + cc;
-            ru[q] = v ? to_f32(U[o]) : 0.0f;
             rdt[q] = v ? to_f32(DT[o]) : 0.0f;
             if (bwd) {
                 rz[q] = (v && gate) ? to_f32(Z[o]) : 0.0f;
@@ -152,10 +205,14 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     };
     auto stage = [&](bool bwd) {
 #pragma unroll
+        for (int q = 0; q < XUL; ++q) {
+            const int e = q * kThreads + tid;
+            if (e < XUE) s_u[e] = ru[q];
+        }
+#pragma unroll
         for (int q = 0; q < XL; ++q) {
             const int e = q * kThreads + tid;
             if (e < XE) {
-                s_u[e] = ru[q];
                 s_dt[e] = rdt[q];
                 if (bwd) {
                     s_z[e] = rz[q];
@@ -175,14 +232,25 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 
     // per-token quantities of this lane's tokens tt = l + 16 jj of the tile;
     // tokens past L get dt = u = 0, which leaves the state unchanged
-    float tk_dl[TP], tk_du[TP], tk_u[TP];
+    float tk_dl[TP], tk_du[TP], tk_u[TP], tk_xc[TP];
     auto transform_fwd = [&](int64_t ts) {
 #pragma unroll
         for (int jj = 0; jj < TP; ++jj) {
             const int tt = l + 16 * jj;
             const bool v = tt < T && ts + tt < L;
-            const int e = min(tt, T - 1) * kCPB + cl;
-            const float uu = v ? s_u[e] : 0.0f;
+            const int tc = min(tt, T - 1);
+            const int e = tc * kCPB + cl;
+            float uu;
+            if constexpr (CONV) {
+                float acc = cb;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], s_u[(tc + i) * kCPB + cl], acc);
+                tk_xc[jj] = acc;
+                uu = v ? silu_f(acc) : 0.0f;
+            } else {
+                tk_xc[jj] = 0.0f;
+                uu = v ? s_u[e] : 0.0f;
+            }
             const float dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
             tk_dl[jj] = dl;
             tk_u[jj] = uu;
@@ -257,6 +325,13 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         dA[s] = 0.0f;
     }
     float accD = 0.0f, accT = 0.0f;   // over this lane's tokens: dyv*u and d_dt_raw
+    // conv: lane l sums tap slot l & 7 over half of each tile's tokens; the
+    // bias over its own tokens; lane j < W-1 holds history input j's gradient
+    float accW = 0.0f, accCb = 0.0f, dhist = 0.0f;
+    if constexpr (CONV) {
+        // tokens past the last tile have no gradient
+        for (int e = tid; e < kRing * kCPB; e += kThreads) s_gx[e] = 0.0f;
+    }
     if (K > 0) fetch(K - 1, true);
     for (int k = K - 1; k >= 0; --k) {
         const int64_t ts = (int64_t)k * T;
@@ -333,6 +408,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         }
 
         // reverse sweep, in halves of 16 tokens for the per-token reductions
+        float tk_gx[TP];
 #pragma unroll
         for (int jj = TP - 1; jj >= 0; --jj) {
             float pdt[16], pdu[16];
@@ -386,6 +462,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             // lane l finishes token l + 16 jj
             const float ddt = row_transpose_sum(pdt, l);
             const float dup = row_transpose_sum(pdu, l);
+            tk_gx[jj] = 0.0f;
             if (tk_v[jj]) {
                 const int tt = l + 16 * jj;
                 const float dyv = tk_dyv[jj];
@@ -398,11 +475,55 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 accD = fmaf(dyv, tk_u[jj], accD);
                 accT += ddr;
                 const int64_t eo = (b * L + ts + tt) * D + d;
-                if (DU) store_io(DU + eo, duv);
+                if constexpr (CONV) {
+                    const float xc = tk_xc[jj];
+                    const float sx = sigmoid_f(xc);
+                    tk_gx[jj] = duv * (sx * (1.0f + xc * (1.0f - sx)));
+                } else if (DU) {
+                    store_io(DU + eo, duv);
+                }
                 if (DDT) store_io(DDT + eo, ddr);
+            }
+            if constexpr (CONV) {
+                if (l + 16 * jj < T) s_gx[((ts + l + 16 * jj) & (kRing - 1)) * kCPB + cl] = tk_gx[jj];
             }
         }
         __syncthreads();
+        if constexpr (CONV) {
+            // dx of this lane's tokens from the ring; tap and bias sums
+#pragma unroll
+            for (int jj = 0; jj < TP; ++jj) {
+                const int tt = l + 16 * jj;
+                if (tk_v[jj]) {
+                    const int64_t t = ts + tt;
+                    float acc = 0.0f;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        acc = fmaf(wk[i], s_gx[((t + 7 - i) & (kRing - 1)) * kCPB + cl], acc);
+                    if (DU) store_io(DU + (b * L + t) * D + d, acc);
+                    accCb += tk_gx[jj];
+                }
+            }
+            {
+                constexpr int TH = T / 2;
+                const int i = l & 7, t0 = (l >> 3) * TH;
+#pragma unroll
+                for (int j = 0; j < TH; ++j)
+                    accW = fmaf(s_gx[((ts + t0 + j) & (kRing - 1)) * kCPB + cl], s_u[(t0 + j + i) * kCPB + cl],
+                                accW);
+            }
+            // gradient of history input j (token j - (W-1)): lane j of the row
+            if (k == 0 && l < W - 1) {
+                const int t = l - (W - 1);
+                float acc = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int r = t + 7 - i;
+                    if (r >= 0) acc = fmaf(wk[i], s_gx[r * kCPB + cl], acc);
+                }
+                dhist = acc;
+            }
+        }
         // dB, dC partials of this workgroup: its 48 channels in order
         for (int e = tid; e < T * NP; e += kThreads) {
             const int i = e / NP, n = e % NP;
@@ -421,15 +542,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     }
 
     // per-channel sums over the row's lanes (each holds its own tokens'),
-    // in a fixed order: lane 0 of the row receives the total
-    float pD[16], pT[16];
+    // in a fixed order: lane j of the row receives the total of slot j
+    // (slots 0..7 conv taps, 8 conv bias, 9 dDskip, 10 d_dt_bias)
+    float pr[16];
 #pragma unroll
-    for (int kk = 0; kk < 16; ++kk) {
-        pD[kk] = kk == 0 ? accD : 0.0f;
-        pT[kk] = kk == 0 ? accT : 0.0f;
-    }
-    const float sD = row_transpose_sum(pD, l);
-    const float sT = row_transpose_sum(pT, l);
+    for (int kk = 0; kk < 16; ++kk) pr[kk] = (kk < 8 && (l & 7) == kk) ? accW : 0.0f;
+    pr[8] = accCb;
+    pr[9] = accD;
+    pr[10] = accT;
+    const float sr = row_transpose_sum(pr, l);
     if (dvalid) {
 #pragma unroll
         for (int s = 0; s < S; ++s) {
@@ -439,9 +560,12 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 p.pA[o] = dA[s];
             }
         }
-        if (l == 0) {
-            p.pD[b * D + d] = sD;
-            p.pT[b * D + d] = sT;
+        if (l == 9) p.pD[b * D + d] = sr;
+        if (l == 10) p.pT[b * D + d] = sr;
+        if constexpr (CONV) {
+            if (l < 8) p.pW[(b * D + d) * 8 + l] = sr;
+            if (l == 8) p.pCb[b * D + d] = sr;
+            if (l < W - 1 && p.dhist != nullptr) p.dhist[(b * (W - 1) + l) * D + d] = dhist;
         }
     }
 }
@@ -461,9 +585,22 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float *pB, const floa
 }
 
 __global__ __launch_bounds__(256) void bwd_reduce_params(const float *A_log, const float *pA, const float *pD,
-                                                         const float *pT, int64_t B, int64_t D, int64_t N,
-                                                         float *dA_log, float *dD, float *ddtb) {
+                                                         const float *pT, const float *pW, const float *pCb,
+                                                         int64_t B, int64_t D, int64_t N, int W,
+                                                         float *dA_log, float *dD, float *ddtb, float *dw,
+                                                         float *dcb) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < D * W && dw) {
+        const int64_t dd = i / W, kk = i % W;
+        float s = 0.0f;
+        for (int64_t b = 0; b < B; ++b) s += pW[(b * D + dd) * 8 + kk + (8 - W)];
+        dw[i] = s;
+    }
+    if (i < D && dcb) {
+        float s = 0.0f;
+        for (int64_t b = 0; b < B; ++b) s += pCb[b * D + i];
+        dcb[i] = s;
+    }
     if (i < D * N && dA_log) {
         float s = 0.0f;
         for (int64_t b = 0; b < B; ++b) s += pA[b * D * N + i];
@@ -481,7 +618,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_params(const float *A_log, con
 }
 
 struct BwdWs {
-    float *ckpt, *pB, *pC, *pA, *pD, *pT;
+    float *ckpt, *pB, *pC, *pA, *pD, *pT, *pW, *pCb;
 };
 
 int tile_len(int64_t N) { return N <= 16 ? 16 : (N <= 32 ? 8 : 4); }
@@ -504,6 +641,8 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, size_t *total)
     r.pA = take((size_t)(B * D * N));
     r.pD = take((size_t)(B * D));
     r.pT = take((size_t)(B * D));
+    r.pW = take((size_t)(B * D * 8));
+    r.pCb = take((size_t)(B * D));
     if (total) *total = off;
     return r;
 }
@@ -511,21 +650,30 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, size_t *total)
 template <typename IOT, int S>
 hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s) {
     BwdParams p{};
-    p.u = a.u; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
+    p.u = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
     p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z; p.dy = a.dy;
     p.h0 = a.h0; p.dhT = a.dhT;
+    p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_hist = a.conv_state_in; p.dhist = a.dconv_state_in;
     p.ckpt = w.ckpt;
-    p.du = a.du; p.ddt = a.ddt; p.dz = a.dz; p.dh0 = a.dh0;
-    p.pB = w.pB; p.pC = w.pC; p.pA = w.pA; p.pD = w.pD; p.pT = w.pT;
-    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N;
+    p.du = a.dx; p.ddt = a.ddt; p.dz = a.dz; p.dh0 = a.dh0;
+    p.pB = w.pB; p.pC = w.pC; p.pA = w.pA; p.pD = w.pD; p.pT = w.pT; p.pW = w.pW; p.pCb = w.pCb;
+    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N; p.W = a.W;
     constexpr int T = BGeo<S>::T;
     p.K = (int)((a.L + T - 1) / T);
     p.G = (int)((a.D + kCPB - 1) / kCPB);
     const int64_t blocks = (int64_t)p.G * a.B;
-    if (a.disc == DISC_ZOH)
-        hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB>), dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    const dim3 grid((unsigned)blocks), block(kThreads);
+    if (a.disc == DISC_ZOH) {
+        if (a.W > 0)
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH, false>), grid, block, 0, s, p);
+    } else {
+        if (a.W > 0)
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB, false>), grid, block, 0, s, p);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = a.B * a.L * a.N;
@@ -535,9 +683,10 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t pn = std::max(a.D * a.N, a.D);
+    const int64_t pn = std::max(std::max(a.D * a.N, a.D), a.D * a.W);
     hipLaunchKernelGGL(bwd_reduce_params, dim3((unsigned)((pn + 255) / 256)), dim3(256), 0, s, a.A_log, w.pA,
-                       w.pD, w.pT, a.B, a.D, a.N, a.dA_log, a.dD, a.ddt_bias);
+                       w.pD, w.pT, w.pW, w.pCb, a.B, a.D, a.N, a.W, a.dA_log, a.dD, a.ddt_bias,
+                       a.W > 0 ? a.dconv_w : nullptr, a.W > 0 ? a.dconv_b : nullptr);
     return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol(ssm):
 
 
 def test_version_and_status_strings(ssm):
-    assert ssm.ssm_version() // 100 == 1
+    assert ssm.ssm_version() // 100 == 2
     for code in range(0, 8):
         s = ssm.ssm_status_string(code)
         assert isinstance(s, str) and len(s) > 3
@@ -130,30 +130,47 @@ def test_scan_fwd_workspace_zero_without_split(ssm):
     assert ssm.ssm_scan_fwd_workspace_size(_desc(ssm, L=64, chunk=1000)) == 0
 
 
-def test_scan_bwd_rejects_fused_conv(ssm):
-    with pytest.raises(ssm.SSMError) as e:
-        ssm.ssm_scan_bwd_workspace_size(_desc(ssm, W=4))
-    assert e.value.code == ssm.SSM_ERR_UNSUPPORTED
+_BWD = ["x", "dt_raw", "dt_bias", "A_log", "B", "C", "Dskip", "z", "conv_w", "conv_b", "conv_state_in",
+        "h0", "dy", "dhT", "dx", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dDskip", "dz", "dh0",
+        "dconv_w", "dconv_b", "dconv_state_in"]
+_BWD_OPTIONAL_ABSENT = ["dt_bias", "Dskip", "z", "conv_w", "conv_b", "conv_state_in", "h0", "dhT", "dz",
+                        "dconv_w", "dconv_b", "dconv_state_in"]
+
+
+def _bwd(ssm, desc, ws=None, ws_bytes=0, **over):
+    args = {k: _addr(i) for i, k in enumerate(_BWD)}
+    for k in _BWD_OPTIONAL_ABSENT:
+        args[k] = None
+    args.update(over)
+    return ssm.lib().ssm_scan_bwd(ctypes.byref(desc), *[args[k] for k in _BWD], ws, ctypes.c_size_t(ws_bytes),
+                                  None)
 
 
 def test_scan_bwd_workspace_and_nulls(ssm):
     d = _desc(ssm)
     n = ssm.ssm_scan_bwd_workspace_size(d)
     assert n > 0
-    args = [_addr(i) for i in range(21)]
-    # optional inputs absent
-    for i in (2, 6, 7, 8, 10, 18):
-        args[i] = None
-    rc = ssm.lib().ssm_scan_bwd(ctypes.byref(d), *args[:20], None, ctypes.c_size_t(0), None)
-    assert rc == ssm.SSM_ERR_WORKSPACE
-    args2 = list(args)
-    args2[9] = None  # dy
-    rc = ssm.lib().ssm_scan_bwd(ctypes.byref(d), *args2[:20], _addr(50), ctypes.c_size_t(n), None)
-    assert rc == ssm.SSM_ERR_NULL_ARG
-    args3 = list(args)
-    args3[18] = _addr(1)  # dz without z
-    rc = ssm.lib().ssm_scan_bwd(ctypes.byref(d), *args3[:20], _addr(50), ctypes.c_size_t(n), None)
-    assert rc == ssm.SSM_ERR_NULL_ARG
+    assert _bwd(ssm, d) == ssm.SSM_ERR_WORKSPACE
+    assert _bwd(ssm, d, _addr(50), n - 1) == ssm.SSM_ERR_WORKSPACE
+    assert _bwd(ssm, d, _addr(50), n, dy=None) == ssm.SSM_ERR_NULL_ARG
+    assert _bwd(ssm, d, _addr(50), n, dz=_addr(30)) == ssm.SSM_ERR_NULL_ARG   # dz without z
+
+
+def test_scan_bwd_conv_arguments(ssm):
+    d0, d4 = _desc(ssm), _desc(ssm, W=4)
+    n = ssm.ssm_scan_bwd_workspace_size(d4)
+    assert n == ssm.ssm_scan_bwd_workspace_size(d0)
+    # conv width 4 needs the taps
+    assert _bwd(ssm, d4, _addr(50), n) == ssm.SSM_ERR_NULL_ARG
+    # conv gradients without a conv
+    for k in ("dconv_w", "dconv_b", "dconv_state_in"):
+        assert _bwd(ssm, d0, _addr(50), n, **{k: _addr(40)}) == ssm.SSM_ERR_BAD_SHAPE
+    # conv inputs and outputs are alignment- and alias-checked
+    assert _bwd(ssm, d4, _addr(50), n, conv_w=_addr(40, 4)) == ssm.SSM_ERR_ALIGNMENT
+    assert _bwd(ssm, d4, _addr(50), n, conv_w=_addr(40), dconv_b=_addr(41, 8)) == ssm.SSM_ERR_ALIGNMENT
+    assert _bwd(ssm, d4, _addr(50), n, conv_w=_addr(40), dconv_w=_addr(40, 16)) == ssm.SSM_ERR_ALIAS
+    assert _bwd(ssm, d4, _addr(50), n, conv_w=_addr(40), conv_state_in=_addr(41),
+                dconv_state_in=_addr(41)) == ssm.SSM_ERR_ALIAS
 
 
 def test_step_validation(ssm):

@@ -416,21 +416,36 @@ def test_streaming_decode_six_blocks(ssm):
 
 # --------------------------------------------------------------------------- backward
 
-_GRADS = ["du", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dD", "dz", "dh0"]
+_GRADS = ["dx", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dD", "dz", "dh0"]
+_CONV_GRADS = ["dconv_w", "dconv_b", "dconv_state"]
 
 
-def _bwd_check(ssm, p, dtype, disc, gate=True, h0=True, dhT=True, tolerance=None):
+def _bwd_check(ssm, p, dtype, disc, gate=True, h0=True, dhT=True, conv=False, state=False, tolerance=None):
+    """ssm_scan_bwd against the oracle.  With conv, x is the conv input and
+    the expected gradients come from the oracle's conv, its scan backward on
+    the conv output, and its conv backward on that dLoss/du."""
     Bn, L, D = p["x"].shape
+    W = p["conv_w"].shape[1]
+    st = p["conv_state"] if (conv and state and W > 1) else None
     g = ssm.ssm_scan_bwd(dev(p["x"], dtype), dev(p["dt_raw"], dtype), dev(p["A_log"]), dev(p["B"], dtype),
                          dev(p["C"], dtype), dev(p["dy"], dtype), dt_bias=dev(p["dt_bias"]),
                          Dskip=dev(p["Dskip"]), z=dev(p["z"], dtype) if gate else None,
+                         conv_w=dev(p["conv_w"]) if conv else None, conv_b=dev(p["conv_b"]) if conv else None,
+                         conv_state_in=dev(st) if st is not None else None,
                          h0=dev(p["h0"]) if h0 else None, dhT=dev(p["dhT"]) if dhT else None, disc=disc)
     torch.cuda.synchronize()
-    r = oracle.scan_bwd(p["x"], p["dt_raw"], p["A_log"], p["B"], p["C"], p["dy"], dt_bias=p["dt_bias"],
+    u = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"], st)[0] if conv else p["x"]
+    r = oracle.scan_bwd(u, p["dt_raw"], p["A_log"], p["B"], p["C"], p["dy"], dt_bias=p["dt_bias"],
                         Dskip=p["Dskip"], z=p["z"] if gate else None, h0=p["h0"] if h0 else None,
                         dhT=p["dhT"] if dhT else None, disc=disc)
+    r["dx"] = r["du"]
+    keys = list(_GRADS)
+    if conv:
+        rc = oracle.conv1d_causal_bwd(p["x"], p["conv_w"], r["du"], bias=p["conv_b"], state_in=st)
+        r.update(dx=rc["dx"], dconv_w=rc["dw"], dconv_b=rc["db"], dconv_state=rc["dstate"])
+        keys += ["dconv_w", "dconv_b"] + (["dconv_state"] if W > 1 else [])
     errs = {}
-    for k in _GRADS:
+    for k in keys:
         if k == "dz" and not gate:
             continue
         errs[k] = rel_linf(g[k], r[k])
@@ -475,11 +490,58 @@ def test_bwd_deterministic(ssm):
 
 
 def test_bwd_forward_backward_workload(ssm):
-    """Forward plus backward at batch 8, L=2,048, D_inner=1536, N=16, fp32:
-    gradients w.r.t. u, dt (as d_dt_raw and d_dt_bias), A_log, B, C, Dskip,
-    z and h0 against the oracle.  u = SiLU(conv4(x)) from the oracle's conv."""
+    """Forward plus backward at batch 8, L=2,048, D_inner=1536, N=16, fp32,
+    through the fused conv prologue: gradients w.r.t. x, conv_w, conv_b, dt
+    (as d_dt_raw and d_dt_bias), A_log, B, C, Dskip and z against the oracle's
+    conv, scan backward and conv backward."""
     p = si.mamba_block(8, 2048, 1536, 16, 4, workload=si.WL_FWDBWD, with_dy=True)
-    u, _ = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"])
-    q = dict(p, x=u.astype(np.float32), h0=np.zeros((8, 1536, 16), np.float32),
-             dhT=np.zeros((8, 1536, 16), np.float32))
-    _bwd_check(ssm, q, torch.float32, DB, h0=False, dhT=False)
+    q = dict(p, h0=np.zeros((8, 1536, 16), np.float32), dhT=np.zeros((8, 1536, 16), np.float32))
+    _bwd_check(ssm, q, torch.float32, DB, h0=False, dhT=False, conv=True)
+
+
+# --------------------------------------------------------------------------- backward with the conv prologue
+
+@pytest.mark.parametrize("Bn,L,D,N,W,state", [
+    (2, 100, 40, 16, 4, True),     # ragged L and D, carried history
+    (1, 37, 24, 3, 3, False),
+    (2, 21, 16, 8, 1, False),      # one tap: no history
+    (1, 50, 70, 33, 8, True),      # 8 tokens per tile
+    (1, 9, 16, 64, 8, True),       # 4 tokens per tile: the 7-token halo spans two tiles
+    (2, 5, 16, 16, 8, True),       # L < W - 1: history gradient reaches past the sequence
+    (1, 1, 1, 16, 4, True),
+])
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_bwd_conv_shapes(ssm, Bn, L, D, N, W, state, disc):
+    p = _rand(23, Bn, L, D, N, W)
+    _bwd_check(ssm, p, torch.float32, disc, conv=True, state=state)
+
+
+def test_bwd_conv_empty_sequence(ssm):
+    """L = 0: nothing flows; the tap, bias and history gradients are zero and
+    dh0 equals dhT."""
+    p = _rand(24, 2, 0, 32, 16, 4)
+    g = ssm.ssm_scan_bwd(dev(p["x"]), dev(p["dt_raw"]), dev(p["A_log"]), dev(p["B"]), dev(p["C"]),
+                         dev(p["dy"]), conv_w=dev(p["conv_w"]), conv_b=dev(p["conv_b"]),
+                         conv_state_in=dev(p["conv_state"]), dhT=dev(p["dhT"]))
+    torch.cuda.synchronize()
+    for k in ("dconv_w", "dconv_b", "dconv_state", "dD", "d_dt_bias", "dA_log"):
+        assert not host(g[k]).any(), k
+    np.testing.assert_array_equal(host(g["dh0"]), p["dhT"])
+
+
+def test_bwd_conv_bf16(ssm):
+    p = _rand(25, 2, 80, 48, 16, 4, bf16=True)
+    _bwd_check(ssm, p, torch.bfloat16, DB, conv=True, state=True)
+
+
+def test_bwd_conv_no_gate_no_state(ssm):
+    p = _rand(26, 2, 64, 32, 16, 4)
+    _bwd_check(ssm, p, torch.float32, DB, gate=False, h0=False, dhT=False, conv=True)
+
+
+def test_bwd_conv_deterministic(ssm):
+    p = _rand(27, 2, 96, 128, 16, 4)
+    a = _bwd_check(ssm, p, torch.float32, DB, conv=True, state=True)
+    b = _bwd_check(ssm, p, torch.float32, DB, conv=True, state=True)
+    for k in _GRADS + _CONV_GRADS:
+        assert torch.equal(a[k], b[k]), k

@@ -28,7 +28,9 @@ MUTANTS = {
     "gate_sigmoid_not_silu": ("y[i] = z ? yv * orc_silu(z[i]) : yv;", "y[i] = z ? yv * orc_sigmoid(z[i]) : yv;"),
     "h0_ignored": ("h[n] = h0 ? h0[(b * D + d) * N + n] : 0.0;", "h[n] = 0.0;"),
     "dt_bias_ignored": ("(dt_bias ? dt_bias[i % D] : 0.0)", "0.0"),
-    "conv_taps_reversed": ("acc += w[d * W + k] *", "acc += w[d * W + (W - 1 - k)] *"),
+    # the forward conv's window read backwards (= taps reversed)
+    "conv_taps_reversed": ("t - (W - 1) + k);\n            y[(b * L + t) * D + d] = silu",
+                           "t - k);\n            y[(b * L + t) * D + d] = silu"),
     "conv_state_out_off_by_one": ("int64_t i = L - (W - 1) + j;", "int64_t i = L - W + j;"),
     "step_history_not_shifted": ("conv_state[(s * (int64_t)(W - 1) + k + 1) * D + d];",
                                  "conv_state[(s * (int64_t)(W - 1) + k) * D + d];"),
