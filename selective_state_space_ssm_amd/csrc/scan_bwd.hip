@@ -40,10 +40,9 @@
 // With the conv prologue the raw input x is staged with 7 rows of history
 // in front of the tile and u is recomputed from it in both phases, with the
 // forward kernel's operation order (right-aligned 8-tap window).  gx, the
-// gradient at the conv output, goes to an LDS ring indexed by absolute token
-// mod 32: when tile k is finished, the first 7 tokens of tile k+1 (processed
-// before it) are still in the ring, so dx of every token of tile k is read
-// from there.
+// gradient at the conv output, goes to LDS rows 0..T-1; rows T..T+6 hold the
+// first 7 tokens of the following tile (finished before it), so the dx of
+// every token of the tile reads its 8 gx values from there.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -65,7 +64,11 @@ struct BGeo {
     static constexpr int TP = (T + 15) / 16;   // tokens per lane in the per-token work
 };
 
-constexpr int kRing = 32;                // rows of the conv-output gradient ring
+// LDS row stride of the [token][channel] tiles.  The per-token work has the
+// 16 lanes of a row on 16 consecutive tokens of one channel; with 50 words
+// per row those 16 addresses fall on 16 distinct even banks (50 r mod 32), and
+// the two channels a half-wavefront covers fill the odd/even pairs.
+constexpr int kXR = 50;
 
 struct BwdParams {
     const void *u, *dt;      // u: the conv input x when the conv prologue is on
@@ -97,16 +100,19 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     constexpr int XE = T * kCPB;          // elements of one [T][48] tile
     constexpr int XH = CONV ? 7 : 0;      // history rows staged in front of the first input
     constexpr int XUE = (T + XH) * kCPB;
+    constexpr int XEP = T * kXR, XUEP = (T + XH) * kXR;   // padded LDS sizes
     constexpr int BE = T * NP;            // elements of one [T][NP] tile
     constexpr int XL = (XE + kThreads - 1) / kThreads;   // staged per thread
     constexpr int XUL = (XUE + kThreads - 1) / kThreads;
     constexpr int BL = (BE + kThreads - 1) / kThreads;
-    static_assert(T + 7 <= kRing, "ring too short");
-    __shared__ float s_u[XUE], s_dt[XE], s_z[XE], s_dy[XE];
+    __shared__ float s_u[XUEP], s_dt[XEP], s_z[XEP], s_dy[XEP];
     __shared__ float s_B[BE], s_C[BE];
     __shared__ float s_rB[T][kCPB][NP], s_rC[T][kCPB][NP];   // per-channel dB, dC terms
-    __shared__ float s_gx[CONV ? kRing * kCPB : 1];         // conv-output gradient by token mod 32
+    __shared__ float s_gx[CONV ? (T + 7) * kXR : 1];       // conv-output gradient, tile + 7 following
     __shared__ float s_wk[CONV ? kCPB * 8 : 1];              // conv taps, right-aligned in 8 slots
+    // outputs of the finished tile, written to memory one tile later (below)
+    __shared__ float s_odx[XEP], s_oddt[XEP], s_odz[XEP];
+    __shared__ float s_oB[BE], s_oC[BE];
 
     const IOT *U = static_cast<const IOT *>(p.u);
     const IOT *DT = static_cast<const IOT *>(p.dt);
@@ -162,9 +168,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 
     // ---- tile staging: registers one tile ahead, then LDS.  Values out of
     // range (tokens past L, channels past D, states past N) stage as zeros.
-    float ru[XUL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL];
+    float ru[XUL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL], rck[S];
     auto fetch = [&](int k, bool bwd) {
         const int64_t ts = (int64_t)k * T;
+        if (bwd) {
+            // this lane's own checkpoint of the tile (written in phase 1)
+#pragma unroll
+            for (int s = 0; s < S; ++s)
+                rck[s] = sv[s] ? p.ckpt[((b * K + k) * D + dc) * N + l + 16 * s] : 0.0f;
+        }
 #pragma unroll
         for (int q = 0; q < XUL; ++q) {
             // row r of the first input holds token ts + r - XH; with the conv,
@@ -207,16 +219,17 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int q = 0; q < XUL; ++q) {
             const int e = q * kThreads + tid;
-            if (e < XUE) s_u[e] = ru[q];
+            if (e < XUE) s_u[(e / kCPB) * kXR + e % kCPB] = ru[q];
         }
 #pragma unroll
         for (int q = 0; q < XL; ++q) {
             const int e = q * kThreads + tid;
             if (e < XE) {
-                s_dt[e] = rdt[q];
+                const int ep = (e / kCPB) * kXR + e % kCPB;
+                s_dt[ep] = rdt[q];
                 if (bwd) {
-                    s_z[e] = rz[q];
-                    s_dy[e] = rdy[q];
+                    s_z[ep] = rz[q];
+                    s_dy[ep] = rdy[q];
                 }
             }
         }
@@ -239,12 +252,12 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             const int tt = l + 16 * jj;
             const bool v = tt < T && ts + tt < L;
             const int tc = min(tt, T - 1);
-            const int e = tc * kCPB + cl;
+            const int e = tc * kXR + cl;
             float uu;
             if constexpr (CONV) {
                 float acc = cb;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], s_u[(tc + i) * kCPB + cl], acc);
+                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], s_u[(tc + i) * kXR + cl], acc);
                 tk_xc[jj] = acc;
                 uu = v ? silu_f(acc) : 0.0f;
             } else {
@@ -285,17 +298,26 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
         h[s] = (p.h0 != nullptr && sv[s]) ? p.h0[(b * D + dc) * N + l + 16 * s] : 0.0f;
-    if (K > 1) fetch(0, false);
-    for (int k = 0; k < K; ++k) {
+    // A wait for loaded data also waits for every store still in flight, so
+    // each store is issued right after a wait and has a whole tile of work
+    // to complete before the next one.
+    auto store_ckpt = [&](int k) {
         if (dvalid) {
 #pragma unroll
             for (int s = 0; s < S; ++s)
                 if (sv[s]) p.ckpt[((b * K + k) * D + d) * N + l + 16 * s] = h[s];
         }
-        if (k + 1 == K) break;   // the last tile's end state is not needed
+    };
+    if (K > 1) fetch(0, false);
+    for (int k = 0; k < K; ++k) {
+        if (k + 1 == K) {   // the last tile's end state is not needed
+            store_ckpt(k);
+            break;
+        }
         __syncthreads();
         stage(false);
         __syncthreads();
+        store_ckpt(k);
         if (k + 2 < K) fetch(k + 1, false);
         transform_fwd((int64_t)k * T);
 #pragma unroll
@@ -327,17 +349,69 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     float accD = 0.0f, accT = 0.0f;   // over this lane's tokens: dyv*u and d_dt_raw
     // conv: lane l sums tap slot l & 7 over half of each tile's tokens; the
     // bias over its own tokens; lane j < W-1 holds history input j's gradient
-    float accW = 0.0f, accCb = 0.0f, dhist = 0.0f;
+    float accW = 0.0f, accCb = 0.0f, dhist = 0.0f, gshift = 0.0f;
     if constexpr (CONV) {
         // tokens past the last tile have no gradient
-        for (int e = tid; e < kRing * kCPB; e += kThreads) s_gx[e] = 0.0f;
+        for (int e = tid; e < (T + 7) * kXR; e += kThreads) s_gx[e] = 0.0f;
     }
+    // The finished tile's outputs wait in LDS and go to memory, in whole
+    // 48-channel rows, after the next tile is staged.
+    float odx[XL], oddt[XL], odz[XL], oB[BL], oC[BL];
+    auto read_out = [&]() {
+#pragma unroll
+        for (int q = 0; q < XL; ++q) {
+            const int e = q * kThreads + tid;
+            const int ep = (min(e, XE - 1) / kCPB) * kXR + min(e, XE - 1) % kCPB;
+            odx[q] = s_odx[ep];
+            oddt[q] = s_oddt[ep];
+            odz[q] = s_odz[ep];
+        }
+#pragma unroll
+        for (int q = 0; q < BL; ++q) {
+            const int e = min(q * kThreads + tid, BE - 1);
+            oB[q] = s_oB[e];
+            oC[q] = s_oC[e];
+        }
+    };
+    auto store_out = [&](int k) {
+        const int64_t ts = (int64_t)k * T;
+#pragma unroll
+        for (int q = 0; q < XL; ++q) {
+            const int e = q * kThreads + tid;
+            const int tt = e / kCPB, cc = e % kCPB;
+            if (e < XE && ts + tt < L && d0 + cc < D) {
+                const int64_t o = (b * L + ts + tt) * D + d0 + cc;
+                if (DU) store_io(DU + o, odx[q]);
+                if (DDT) store_io(DDT + o, oddt[q]);
+                if (DZ) store_io(DZ + o, odz[q]);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < BL; ++q) {
+            const int e = q * kThreads + tid;
+            const int i = e / NP, n = e % NP;
+            if (e < BE && n < N && ts + i < L) {
+                const int64_t o = ((grp * p.B + b) * L + ts + i) * N + n;
+                p.pB[o] = oB[q];
+                p.pC[o] = oC[q];
+            }
+        }
+    };
+
     if (K > 0) fetch(K - 1, true);
     for (int k = K - 1; k >= 0; --k) {
         const int64_t ts = (int64_t)k * T;
         __syncthreads();
         stage(true);
+        float hck[S];
+#pragma unroll
+        for (int s = 0; s < S; ++s) hck[s] = rck[s];
+        if (k + 1 < K) read_out();
+        if constexpr (CONV) {
+            if (k + 1 < K && tid < 7 * kCPB) s_gx[(T + tid / kCPB) * kXR + tid % kCPB] = gshift;
+        }
         __syncthreads();
+        if (k + 1 < K) store_out(k + 1);
         if (k > 0) fetch(k - 1, true);
 
         // per-token work of this lane's tokens
@@ -348,7 +422,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         for (int jj = 0; jj < TP; ++jj) {
             const int tt = l + 16 * jj;
             const bool v = tt < T && ts + tt < L && dvalid;
-            const int e = min(tt, T - 1) * kCPB + cl;
+            const int e = min(tt, T - 1) * kXR + cl;
             tk_v[jj] = v;
             tk_sg[jj] = sigmoid_f(s_dt[e] + dtb);
             const float dyr = v ? s_dy[e] : 0.0f;
@@ -370,7 +444,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         // readout yv of each 16-token half feeds dz
         float hs[T + 1][S], as[T][S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) hs[0][s] = sv[s] ? p.ckpt[((b * K + k) * D + dc) * N + l + 16 * s] : 0.0f;
+        for (int s = 0; s < S; ++s) hs[0][s] = hck[s];
 #pragma unroll
         for (int jj = 0; jj < TP; ++jj) {
             float yp[16];
@@ -399,10 +473,9 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             }
             if (gate) {
                 const float yv = fmaf(Dd, tk_u[jj], row_transpose_sum(yp, l));
-                if (tk_v[jj] && DZ != nullptr) {
+                if (l + 16 * jj < T) {
                     const float sz = tk_s[jj];
-                    store_io(DZ + (b * L + ts + l + 16 * jj) * D + d,
-                             tk_dy[jj] * yv * sz * (1.0f + tk_z[jj] * (1.0f - sz)));
+                    s_odz[(l + 16 * jj) * kXR + cl] = tk_dy[jj] * yv * sz * (1.0f + tk_z[jj] * (1.0f - sz));
                 }
             }
         }
@@ -474,18 +547,17 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 const float ddr = ddt * tk_sg[jj];
                 accD = fmaf(dyv, tk_u[jj], accD);
                 accT += ddr;
-                const int64_t eo = (b * L + ts + tt) * D + d;
                 if constexpr (CONV) {
                     const float xc = tk_xc[jj];
                     const float sx = sigmoid_f(xc);
                     tk_gx[jj] = duv * (sx * (1.0f + xc * (1.0f - sx)));
-                } else if (DU) {
-                    store_io(DU + eo, duv);
+                } else {
+                    s_odx[tt * kXR + cl] = duv;
                 }
-                if (DDT) store_io(DDT + eo, ddr);
+                s_oddt[tt * kXR + cl] = ddr;
             }
             if constexpr (CONV) {
-                if (l + 16 * jj < T) s_gx[((ts + l + 16 * jj) & (kRing - 1)) * kCPB + cl] = tk_gx[jj];
+                if (l + 16 * jj < T) s_gx[(l + 16 * jj) * kXR + cl] = tk_gx[jj];
             }
         }
         __syncthreads();
@@ -495,12 +567,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             for (int jj = 0; jj < TP; ++jj) {
                 const int tt = l + 16 * jj;
                 if (tk_v[jj]) {
-                    const int64_t t = ts + tt;
                     float acc = 0.0f;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        acc = fmaf(wk[i], s_gx[((t + 7 - i) & (kRing - 1)) * kCPB + cl], acc);
-                    if (DU) store_io(DU + (b * L + t) * D + d, acc);
+                    for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], s_gx[(tt + 7 - i) * kXR + cl], acc);
+                    s_odx[tt * kXR + cl] = acc;
                     accCb += tk_gx[jj];
                 }
             }
@@ -509,20 +579,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 const int i = l & 7, t0 = (l >> 3) * TH;
 #pragma unroll
                 for (int j = 0; j < TH; ++j)
-                    accW = fmaf(s_gx[((ts + t0 + j) & (kRing - 1)) * kCPB + cl], s_u[(t0 + j + i) * kCPB + cl],
-                                accW);
+                    accW = fmaf(s_gx[(t0 + j) * kXR + cl], s_u[(t0 + j + i) * kXR + cl], accW);
             }
-            // gradient of history input j (token j - (W-1)): lane j of the row
-            if (k == 0 && l < W - 1) {
-                const int t = l - (W - 1);
-                float acc = 0.0f;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const int r = t + 7 - i;
-                    if (r >= 0) acc = fmaf(wk[i], s_gx[r * kCPB + cl], acc);
-                }
-                dhist = acc;
-            }
+            // rows 0..6 become the following rows of the next (earlier) tile;
+            // written after the next barrier, when nobody reads rows T..T+6
+            gshift = (tid < 7 * kCPB) ? s_gx[(tid / kCPB) * kXR + tid % kCPB] : 0.0f;
         }
         // dB, dC partials of this workgroup: its 48 channels in order
         for (int e = tid; e < T * NP; e += kThreads) {
@@ -534,9 +595,24 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                     sb += s_rB[i][c2][n];
                     sc += s_rC[i][c2][n];
                 }
-                const int64_t o = ((grp * p.B + b) * L + ts + i) * N + n;
-                p.pB[o] = sb;
-                p.pC[o] = sc;
+                s_oB[e] = sb;
+                s_oC[e] = sc;
+            }
+        }
+    }
+    if (K > 0) {
+        __syncthreads();
+        read_out();
+        store_out(0);
+    }
+    if constexpr (CONV) {
+        // gradient of history input j (token j - (W-1)): lane j of the row,
+        // from the first tile's rows (zeros when L = 0)
+        if (l < W - 1) {
+            const int t = l - (W - 1);
+            for (int i = 0; i < 8; ++i) {
+                const int r = t + 7 - i;
+                if (r >= 0) dhist = fmaf(wk[i], s_gx[r * kXR + cl], dhist);
             }
         }
     }
