@@ -69,6 +69,9 @@ struct BGeo {
 // per row those 16 addresses fall on 16 distinct even banks (50 r mod 32), and
 // the two channels a half-wavefront covers fill the odd/even pairs.
 constexpr int kXR = 50;
+// s_waitcnt immediate for "all vector memory operations done" (vmcnt 0,
+// expcnt and lgkmcnt left at their maxima)
+constexpr int kWaitVm0 = 0x0F70;
 
 struct BwdParams {
     const void *u, *dt;      // u: the conv input x when the conv prologue is on
@@ -150,8 +153,8 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         An[s] = A;
         Ainv[s] = 1.0f / A;
     }
-    const float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
-    const float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
+    float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
     // conv taps right-aligned in an 8-tap window (slot 7 multiplies the
     // current input), kept in LDS; first read after the tile loop's barriers
     const int W = p.W;
@@ -216,6 +219,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         }
     };
     auto stage = [&](bool bwd) {
+        // One unconditional wait for the fetched tile: the staging writes
+        // below are lane-masked, and a wait inside a masked block would not
+        // count for the code after it.
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
 #pragma unroll
         for (int q = 0; q < XUL; ++q) {
             const int e = q * kThreads + tid;
@@ -308,6 +315,13 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 if (sv[s]) p.ckpt[((b * K + k) * D + d) * N + l + 16 * s] = h[s];
         }
     };
+    // Values loaded before the tile loops and first used inside them are
+    // consumed here, before any tile is requested: left pending, they would
+    // make the compiler wait for every load in flight at their first use in
+    // the loop, on every tile.
+#pragma unroll
+    for (int s = 0; s < S; ++s) asm volatile("" : "+v"(h[s]));
+    asm volatile("" : "+v"(dtb), "+v"(Dd), "+v"(cb));
     if (K > 1) fetch(0, false);
     for (int k = 0; k < K; ++k) {
         if (k + 1 == K) {   // the last tile's end state is not needed

@@ -73,87 +73,61 @@ constexpr int kRows = kTile / 16;   // tile rows per thread in the transform rol
 
 // Raw loads of one tile, held in registers while the previous tile is
 // scanned.  Transform role: thread -> channel tc = tid & 15 and rows
-// kRows*rp .. kRows*rp + kRows-1 with rp = tid >> 4.  B and C: 4-wide
-// chunks (vector path) or single elements (guarded path) dealt over the
-// block's threads, B first then C.
+// kRows*rp .. kRows*rp + kRows-1 with rp = tid >> 4.  B and C: the [64][NP]
+// element tiles dealt over the block's threads in order, B first then C
+// (consecutive threads read consecutive elements).
 template <int NP>
 struct RawTile {
-    static constexpr int NCH = kTile * NP / 4;                      // chunks per tensor
-    static constexpr int BCV = 4 * ((2 * NCH + kThreads - 1) / kThreads);
-    static constexpr int BCS = (2 * kTile * NP + kThreads - 1) / kThreads;
-    static constexpr int BCE = BCV > BCS ? BCV : BCS;
+    static constexpr int TE = kTile * NP;                 // elements per tensor tile
+    static_assert(TE % kThreads == 0, "tile elements");
+    static constexpr int BCS = 2 * TE / kThreads;
     float x[kRows], dt[kRows], z[kRows];
-    float bc[BCE];
+    float bc[BCS];
 };
 
+// Every load here is unconditional, from a clamped (valid) address: rows
+// past the tile's end are never read back, states past N are zeroed when
+// staged.  Branch-free fetching keeps the compiler from waiting on these
+// loads (or on anything issued before them) until the data is staged.
 template <typename IOT, int NP, bool WANT_C>
 __device__ __forceinline__ void load_raw(RawTile<NP> &r, const IOT *X, const IOT *DT, const IOT *Z,
                                          const IOT *Bp, const IOT *Cp, int64_t b, int64_t L, int64_t D,
-                                         int64_t N, int64_t ts, int nv, int64_t tdc, bool tvalid, int rp,
-                                         int tid, bool vecBC) {
+                                         int64_t N, int64_t ts, int nv, int64_t tdc, int rp, int tid) {
+    constexpr int TE = RawTile<NP>::TE;
+#pragma unroll
+    for (int i = 0; i < RawTile<NP>::BCS; ++i) {
+        constexpr int per = TE / kThreads;                // loads per tensor per thread
+        const int tens = i / per;                         // 0: B, 1: C (compile time)
+        const int ec = (i % per) * kThreads + tid;
+        const int row = min(ec / NP, nv - 1);
+        const int n = min(ec % NP, (int)N - 1);
+        r.bc[i] = (tens < (WANT_C ? 2 : 1)) ? to_f32((tens == 0 ? Bp : Cp)[(b * L + ts + row) * N + n]) : 0.0f;
+    }
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-        const int row = rp * kRows + i;
-        const bool v = tvalid && row < nv;
+        const int row = min(rp * kRows + i, nv - 1);
         const int64_t e = (b * L + ts + row) * D + tdc;
-        r.x[i] = v ? to_f32(X[e]) : 0.0f;
-        r.dt[i] = v ? to_f32(DT[e]) : 0.0f;
-        r.z[i] = (v && Z != nullptr) ? to_f32(Z[e]) : 0.0f;
-    }
-    constexpr int NCH = RawTile<NP>::NCH;
-    const int ntens = WANT_C ? 2 : 1;
-    if (vecBC) {
-#pragma unroll
-        for (int i = 0; i < RawTile<NP>::BCV / 4; ++i) {
-            const int f = tid + kThreads * i;
-            const int tens = f / NCH, fc = f % NCH;
-            const int row = fc / (NP / 4), c4 = (fc % (NP / 4)) * 4;
-            float t4[4] = {0.f, 0.f, 0.f, 0.f};
-            if (tens < ntens && row < nv)
-                load_k<4>((tens == 0 ? Bp : Cp) + (b * L + ts + row) * N + c4, t4, true);
-#pragma unroll
-            for (int k = 0; k < 4; ++k) r.bc[4 * i + k] = t4[k];
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < RawTile<NP>::BCS; ++i) {
-            const int e = tid + kThreads * i;
-            const int tens = e / (kTile * NP), ec = e % (kTile * NP);
-            const int row = ec / NP, n = ec % NP;
-            const bool v = tens < ntens && row < nv && n < N;
-            r.bc[i] = v ? to_f32((tens == 0 ? Bp : Cp)[(b * L + ts + row) * N + n]) : 0.0f;
-        }
+        r.x[i] = to_f32(X[e]);
+        r.dt[i] = to_f32(DT[e]);
+        r.z[i] = (Z != nullptr) ? to_f32(Z[e]) : 0.0f;
     }
 }
 
 // B and C go to LDS transposed, [state][token] with a padded row of
 // kTile + 4 floats, so that a lane reads four consecutive tokens of its
-// state with one 16-byte access.
+// state with one 16-byte access.  States past N are staged as zeros.
 constexpr int kTS = kTile + 4;
 
 template <int NP, bool WANT_C>
-__device__ __forceinline__ void store_bc(const RawTile<NP> &r, float *sB, float *sC, int tid, bool vecBC) {
-    constexpr int NCH = RawTile<NP>::NCH;
-    const int ntens = WANT_C ? 2 : 1;
-    if (vecBC) {
+__device__ __forceinline__ void store_bc(const RawTile<NP> &r, float *sB, float *sC, int tid, int64_t N) {
+    constexpr int TE = RawTile<NP>::TE;
 #pragma unroll
-        for (int i = 0; i < RawTile<NP>::BCV / 4; ++i) {
-            const int f = tid + kThreads * i;
-            const int tens = f / NCH, fc = f % NCH;
-            if (tens < ntens) {
-                const int row = fc / (NP / 4), c4 = (fc % (NP / 4)) * 4;
-                float *dst = (tens == 0 ? sB : sC);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) dst[(c4 + k) * kTS + row] = r.bc[4 * i + k];
-            }
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < RawTile<NP>::BCS; ++i) {
-            const int e = tid + kThreads * i;
-            const int tens = e / (kTile * NP), ec = e % (kTile * NP);
-            if (tens < ntens) (tens == 0 ? sB : sC)[(ec % NP) * kTS + ec / NP] = r.bc[i];
-        }
+    for (int i = 0; i < RawTile<NP>::BCS; ++i) {
+        constexpr int per = TE / kThreads;
+        const int tens = i / per;
+        const int ec = (i % per) * kThreads + tid;
+        const int row = ec / NP, n = ec % NP;
+        if (tens < (WANT_C ? 2 : 1)) (tens == 0 ? sB : sC)[n * kTS + row] = (n < N) ? r.bc[i] : 0.0f;
     }
 }
 
@@ -245,9 +219,18 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     const int64_t td = d0 + tc;
     const bool tvalid = td < D;
     const int64_t tdc = tvalid ? td : (D - 1);
-    const bool vecBC = (N == NP) && (N % 4 == 0);
 
     float A2[SPL], An[SPL], Ainv[SPL], h[SPL];
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) h[s] = 0.0f;
+    // The starting state is requested first, so the wait for A_log below
+    // (issued after it) also covers it; it is then pinned, so that the
+    // compiler sees it complete before the loop.  Left pending, it would
+    // make the compiler wait for every load in flight at its first use in
+    // the loop, on every tile.
+    if (p.init != nullptr && nvalid > 0)
+        load_k_guard<SPL>(p.init + b * p.init_bstride + (int64_t)k * p.init_kstride + dc * N + n0, h, nvalid,
+                          vecN && (SPL % 4 == 0));
 #pragma unroll
     for (int s = 0; s < SPL; ++s) {
         const bool v = s < nvalid;
@@ -255,11 +238,9 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
         A2[s] = v ? A * kLog2e : 0.0f;
         An[s] = A;
         Ainv[s] = 1.0f / A;
-        h[s] = 0.0f;
     }
-    if (p.init != nullptr && nvalid > 0)
-        load_k_guard<SPL>(p.init + b * p.init_bstride + (int64_t)k * p.init_kstride + dc * N + n0, h, nvalid,
-                          vecN && (SPL % 4 == 0));
+#pragma unroll
+    for (int s = 0; s < SPL; ++s) asm volatile("" : "+v"(h[s]) : "v"(A2[s]));
 
     const float dtb = p.dt_bias ? p.dt_bias[tdc] : 0.0f;
     const float Dd = p.Dskip ? p.Dskip[tdc] : 0.0f;
@@ -282,7 +263,6 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     };
 
     RawTile<NP> raw;
-    float xh[kRows];   // raw conv input of the previous tile (threads holding its last 8 rows)
 
     // Per-(token, channel) quantities, once per tile element.
     auto transform = [&](int nv) {
@@ -320,18 +300,16 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
 #pragma unroll
             for (int i = 0; i < kRows; ++i) s_x[(8 + rp * kRows + i) * kXS + tc] = raw.x[i];
         }
-        store_bc<NP, FINAL>(raw, s_B, s_C, tid, vecBC);
+        store_bc<NP, FINAL>(raw, s_B, s_C, tid, N);
         __syncthreads();
         transform(nv);
-#pragma unroll
-        for (int i = 0; i < kRows; ++i) xh[i] = raw.x[i];
         __syncthreads();
     };
 
     auto fetch = [&](int it) {
         const int64_t ts = t0 + (int64_t)it * T;
         const int nv = (int)min((int64_t)T, t1 - ts);
-        load_raw<IOT, NP, FINAL>(raw, X, DT, Z, Bp, Cp, b, L, D, N, ts, nv, tdc, tvalid, rp, tid, vecBC);
+        load_raw<IOT, NP, FINAL>(raw, X, DT, Z, Bp, Cp, b, L, D, N, ts, nv, tdc, rp, tid);
     };
 
     float ssum = 0.0f;
@@ -418,30 +396,48 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             for (; t < nv; ++t) scan_step(t);
         }
         __syncthreads();
+        // readout: ((w0 + w1) + (w2 + w3)) + Dskip*u, then the gate
+        float yo[kRows];
         if constexpr (FINAL) {
-            // readout: ((w0 + w1) + (w2 + w3)) + Dskip*u, then the gate
-            if (tvalid) {
 #pragma unroll
-                for (int i = 0; i < kRows; ++i) {
-                    const int row = rp * kRows + i;
-                    if (row < nv) {
-                        const float2 gd = s_gd[tc][row];
-                        const float ys = (s_yp[0][tc][row] + s_yp[1][tc][row]) +
-                                         (s_yp[2][tc][row] + s_yp[3][tc][row]);
-                        store_io(Y + (b * L + ts + row) * D + td, (ys + gd.y) * gd.x);
+            for (int i = 0; i < kRows; ++i) {
+                const int row = rp * kRows + i;
+                const float2 gd = s_gd[tc][row];
+                const float ys = (s_yp[0][tc][row] + s_yp[1][tc][row]) + (s_yp[2][tc][row] + s_yp[3][tc][row]);
+                yo[i] = (ys + gd.y) * gd.x;
+            }
+        }
+        // A wait for loaded data also waits for every store in flight, so y
+        // is stored after the next tile is staged and the one after it is
+        // requested (whose waits would otherwise hold for these stores), and
+        // has a whole tile of scanning to drain.
+        auto store_y = [&]() {
+            if constexpr (FINAL) {
+                if (tvalid) {
+#pragma unroll
+                    for (int i = 0; i < kRows; ++i) {
+                        const int row = rp * kRows + i;
+                        if (row < nv) store_io(Y + (b * L + ts + row) * D + td, yo[i]);
                     }
                 }
             }
-        }
+        };
         if (it + 1 < ntiles) {
             if constexpr (CONV) {
+                // the last 8 rows become the next tile's history rows; each
+                // thread moves the rows it staged itself (no other thread
+                // touches them before the next barrier)
                 if (rp >= kHaloRp) {
 #pragma unroll
-                    for (int i = 0; i < kRows; ++i) s_x[(rp * kRows + i - (T - 8)) * kXS + tc] = xh[i];
+                    for (int i = 0; i < kRows; ++i)
+                        s_x[(rp * kRows + i - (T - 8)) * kXS + tc] = s_x[(8 + rp * kRows + i) * kXS + tc];
                 }
             }
             stage(it + 1);
             if (it + 2 < ntiles) fetch(it + 2);
+            store_y();
+        } else {
+            store_y();
         }
     }
 
