@@ -85,31 +85,52 @@ struct RawTile {
     float bc[BCS];
 };
 
-// Every load here is unconditional, from a clamped (valid) address: rows
-// past the tile's end are never read back, states past N are zeroed when
-// staged.  Branch-free fetching keeps the compiler from waiting on these
-// loads (or on anything issued before them) until the data is staged.
+// Per-thread byte offsets of the fetch inside a tile, the same for every
+// tile.  x, dt_raw, z: rows rp*kRows + i of channel tdc; B, C: chunk i of the
+// [64][NP] tile, i.e. element ec = (i % per) * kThreads + tid at row ec / NP,
+// state ec % NP.
+struct FetchOff {
+    uint32_t x0, xrow;     // row rp*kRows, and the byte stride of one row
+    uint32_t bc0, bcstep;  // chunk 0, and the byte stride between chunks
+};
+
+// Loads of one tile through buffer descriptors whose range ends at the end
+// of the sequence: rows past L read 0, rows past the tile's end (a chunk
+// boundary) are read but never used, states past N are zeroed at staging.
+// Every load is unconditional, so the compiler never waits on one (or on
+// anything issued before it) until the data is staged.
 template <typename IOT, int NP, bool WANT_C>
-__device__ __forceinline__ void load_raw(RawTile<NP> &r, const IOT *X, const IOT *DT, const IOT *Z,
-                                         const IOT *Bp, const IOT *Cp, int64_t b, int64_t L, int64_t D,
-                                         int64_t N, int64_t ts, int nv, int64_t tdc, int rp, int tid) {
+__device__ __forceinline__ void load_raw(RawTile<NP> &r, const FetchOff &fo, const IOT *X, const IOT *DT,
+                                         const IOT *Z, const IOT *Bp, const IOT *Cp, int64_t b, int64_t L,
+                                         int64_t D, int64_t N, int64_t ts) {
     constexpr int TE = RawTile<NP>::TE;
+    constexpr int per = TE / kThreads;                    // loads per tensor per thread
+    const uint64_t es = sizeof(IOT);
+    const int64_t left = L - ts;                          // tokens from ts to the end
+    const buf_t rB = make_buf(Bp + (b * L + ts) * N, (uint64_t)(left * N) * es);
+    const buf_t rC = make_buf(Cp + (b * L + ts) * N, (uint64_t)(left * N) * es);
 #pragma unroll
     for (int i = 0; i < RawTile<NP>::BCS; ++i) {
-        constexpr int per = TE / kThreads;                // loads per tensor per thread
         const int tens = i / per;                         // 0: B, 1: C (compile time)
-        const int ec = (i % per) * kThreads + tid;
-        const int row = min(ec / NP, nv - 1);
-        const int n = min(ec % NP, (int)N - 1);
-        r.bc[i] = (tens < (WANT_C ? 2 : 1)) ? to_f32((tens == 0 ? Bp : Cp)[(b * L + ts + row) * N + n]) : 0.0f;
+        const uint32_t off = fo.bc0 + (uint32_t)(i % per) * fo.bcstep;
+        r.bc[i] = (tens < (WANT_C ? 2 : 1)) ? buf_ld(tens == 0 ? rB : rC, off, Bp) : 0.0f;
     }
+    const uint64_t tb = (uint64_t)(left * D) * es;
+    const buf_t rX = make_buf(X + (b * L + ts) * D, tb);
+    const buf_t rD = make_buf(DT + (b * L + ts) * D, tb);
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
-        const int row = min(rp * kRows + i, nv - 1);
-        const int64_t e = (b * L + ts + row) * D + tdc;
-        r.x[i] = to_f32(X[e]);
-        r.dt[i] = to_f32(DT[e]);
-        r.z[i] = (Z != nullptr) ? to_f32(Z[e]) : 0.0f;
+        const uint32_t off = fo.x0 + (uint32_t)i * fo.xrow;
+        r.x[i] = buf_ld(rX, off, X);
+        r.dt[i] = buf_ld(rD, off, DT);
+    }
+    if (Z != nullptr) {
+        const buf_t rZ = make_buf(Z + (b * L + ts) * D, tb);
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) r.z[i] = buf_ld(rZ, fo.x0 + (uint32_t)i * fo.xrow, Z);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) r.z[i] = 0.0f;
     }
 }
 
@@ -263,6 +284,14 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     };
 
     RawTile<NP> raw;
+    FetchOff fo;
+    {
+        const uint32_t es = sizeof(IOT);
+        fo.x0 = (uint32_t)((rp * kRows) * (int)D + (int)tdc) * es;
+        fo.xrow = (uint32_t)D * es;
+        fo.bc0 = (uint32_t)((tid / NP) * (int)N + tid % NP) * es;
+        fo.bcstep = (uint32_t)((kThreads / NP) * (int)N) * es;
+    }
 
     // Per-(token, channel) quantities, once per tile element.
     auto transform = [&](int nv) {
@@ -308,8 +337,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
 
     auto fetch = [&](int it) {
         const int64_t ts = t0 + (int64_t)it * T;
-        const int nv = (int)min((int64_t)T, t1 - ts);
-        load_raw<IOT, NP, FINAL>(raw, X, DT, Z, Bp, Cp, b, L, D, N, ts, nv, tdc, rp, tid);
+        load_raw<IOT, NP, FINAL>(raw, fo, X, DT, Z, Bp, Cp, b, L, D, N, ts);
     };
 
     float ssum = 0.0f;
@@ -411,14 +439,14 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
         // is stored after the next tile is staged and the one after it is
         // requested (whose waits would otherwise hold for these stores), and
         // has a whole tile of scanning to drain.
+        // (the descriptor's range ends at the tile's last valid row, so rows
+        // past it are dropped by the hardware)
         auto store_y = [&]() {
             if constexpr (FINAL) {
+                const buf_t rY = make_buf(Y + (b * L + ts) * D, (uint64_t)nv * D * sizeof(IOT));
                 if (tvalid) {
 #pragma unroll
-                    for (int i = 0; i < kRows; ++i) {
-                        const int row = rp * kRows + i;
-                        if (row < nv) store_io(Y + (b * L + ts + row) * D + td, yo[i]);
-                    }
+                    for (int i = 0; i < kRows; ++i) buf_st(rY, fo.x0 + (uint32_t)i * fo.xrow, Y, yo[i]);
                 }
             }
         };

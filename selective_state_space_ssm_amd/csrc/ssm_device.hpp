@@ -108,6 +108,34 @@ __device__ __forceinline__ void store_k(float *p, const float (&v)[K], int valid
         if (i < valid) p[i] = v[i];
 }
 
+// ------------------------------------------------------------ buffer access
+// Raw buffer descriptors: a uniform 48-bit base, a byte range and the gfx9
+// format word (32-bit data).  A lane's byte offset at or past the range
+// reads 0 and writes nothing, so tile tails need no per-lane clamping, and
+// loads take a 32-bit VGPR offset on a scalar base (no 64-bit address math).
+typedef __amdgpu_buffer_rsrc_t buf_t;
+constexpr int kBufFormatWord = 0x00020000;
+
+__device__ __forceinline__ buf_t make_buf(const void *base, uint64_t bytes) {
+    const uint32_t n = bytes > 0xffffffffull ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, kBufFormatWord);
+}
+__device__ __forceinline__ float buf_ld(buf_t r, uint32_t boff, const float *) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, boff, 0, 0));
+}
+__device__ __forceinline__ float buf_ld(buf_t r, uint32_t boff, const bf16_t *) {
+    return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, boff, 0, 0) << 16);
+}
+
+__device__ __forceinline__ void buf_st(buf_t r, uint32_t boff, float *, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, boff, 0, 0);
+}
+__device__ __forceinline__ void buf_st(buf_t r, uint32_t boff, bf16_t *, float v) {
+    bf16_t h;
+    store_io(&h, v);
+    __builtin_amdgcn_raw_buffer_store_b16(h, r, boff, 0, 0);
+}
+
 // ------------------------------------------------------------ fast math
 // Hardware transcendentals (v_exp_f32 = 2^x, v_log_f32 = log2, v_rcp_f32).
 __device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
