@@ -280,7 +280,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
 
     # long sequence, bf16, two-level scan
     L4 = 65536
-    r = si.mamba_block(1, L4, D, N, 4, workload=si.WL_LONG, bf16=True)
+    r = si.mamba_block(1, L4, D, N, 4, workload=si.WL_LONG, bf16=True, with_dy=True)
     bf = torch.bfloat16
     R = {k: dev(r[k], bf) for k in ("x", "dt_raw", "B", "C", "z")}
     R.update({k: dev(r[k]) for k in ("dt_bias", "A_log", "Dskip")})
@@ -299,7 +299,29 @@ def bench_extras(torch, np, si, ssm, dev, args):
     ex["forward_bf16_B1_L65536_chunked"] = {"us_per_call": round(ms * 1e3, 2),
                                             "elements_per_s": L4 * D * N / (ms * 1e-3),
                                             "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
-    del R, y4, ws4
+    del y4, ws4
+    torch.cuda.empty_cache()
+
+    # backward of the same workload, split in time by the library
+    R["dy"] = dev(r["dy"], bf)
+    del r
+    wsb = torch.empty(ssm.ssm_scan_bwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    outb = {}
+    b4 = lambda: ssm.ssm_scan_bwd(R["x"], R["dt_raw"], R["A_log"], R["B"], R["C"], R["dy"], dt_bias=R["dt_bias"],
+                                  Dskip=R["Dskip"], z=R["z"], out=outb, workspace=wsb)
+    for _ in range(2):
+        b4()
+    tm = EventTimer(torch)
+    for _ in range(max(3, reps // 2)):
+        tm.run(b4)
+    ms = tm.mean_ms()
+    nb = bwd_bytes(1, L4, D, N, 2)
+    ex["backward_bf16_B1_L65536_chunked"] = {"us_per_call": round(ms * 1e3, 2),
+                                             "elements_per_s": L4 * D * N / (ms * 1e-3),
+                                             "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1),
+                                             "algorithmic_bytes": nb}
+    log("long bf16 backward (time split): %.1f us" % (ms * 1e3))
+    del R, wsb, outb
     torch.cuda.empty_cache()
 
     # streaming decode: 6 blocks x 256 streams x 1536 channels x 16 states,

@@ -205,6 +205,13 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes)
  *                             conv_state_in was given)
  *   The three conv outputs must be NULL when conv_width is 0.
  *   workspace  device memory of ssm_scan_bwd_workspace_size bytes (required)
+ * Time chunks (desc->chunk_len: 0 the library's choice, -1 never, > 0 this
+ * length rounded up to a multiple of 64): with few channel workgroups the
+ * sequence is split in time.  The forward's chunk scan and carry give every
+ * chunk its exact start state; a reverse walk over chunk summaries gives its
+ * end adjoint (over a chunk the adjoint is affine, g_start = prod(exp(dt*A))
+ * * g_end + R); every chunk then runs the backward sweep independently.  The
+ * result equals the unsplit backward up to rounding.
  */
 ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt_raw,
                         const float *dt_bias, const float *A_log, const void *B,

@@ -208,7 +208,7 @@ def ssm_scan_fwd(x, dt_raw, A_log, B, C, dt_bias=None, Dskip=None, z=None, conv_
 
 
 def ssm_scan_bwd(x, dt_raw, A_log, B, C, dy, dt_bias=None, Dskip=None, z=None, conv_w=None, conv_b=None,
-                 conv_state_in=None, h0=None, dhT=None, disc=SSM_DISC_DELTA_B,
+                 conv_state_in=None, h0=None, dhT=None, disc=SSM_DISC_DELTA_B, chunk_len=0,
                  want=("dx", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dD", "dz", "dh0",
                        "dconv_w", "dconv_b", "dconv_state"),
                  out=None, workspace=None, stream=None):
@@ -220,7 +220,7 @@ def ssm_scan_bwd(x, dt_raw, A_log, B, C, dy, dt_bias=None, Dskip=None, z=None, c
     Bn, L, D = x.shape
     N = A_log.shape[1]
     W = conv_w.shape[1] if conv_w is not None else 0
-    desc = _scan_desc(x, N, W, disc, 0)
+    desc = _scan_desc(x, N, W, disc, chunk_len)
     t = x.dtype
     out = dict(out or {})
     f32 = torch.float32

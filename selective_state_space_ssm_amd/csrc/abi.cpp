@@ -204,7 +204,8 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes)
     ssm_status st = check_scan_desc(desc);
     if (st != SSM_OK) return st;
     if (!bytes) return SSM_ERR_NULL_ARG;
-    *bytes = ssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim, desc->dstate);
+    const int64_t chunk = ssm::scan_bwd_chunk(desc->batch, desc->seqlen, desc->dim, desc->dstate, desc->chunk_len);
+    *bytes = ssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim, desc->dstate, chunk);
     return SSM_OK;
 }
 
@@ -231,7 +232,8 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
                           (const void *)dh0, (const void *)dconv_w, (const void *)dconv_b,
                           (const void *)dconv_state_in, (const void *)workspace})
         if (!aligned16(p)) return SSM_ERR_ALIGNMENT;
-    const size_t need = ssm::scan_bwd_workspace_bytes(Bn, L, D, N);
+    const int64_t chunk = ssm::scan_bwd_chunk(Bn, L, D, N, desc->chunk_len);
+    const size_t need = ssm::scan_bwd_workspace_bytes(Bn, L, D, N, chunk);
     if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
     const int64_t es = io_size(desc->io_dtype);
     const int64_t nbld = Bn * L * D, nbln = Bn * L * N, nbdn = Bn * D * N, nst = Bn * (W > 0 ? W - 1 : 0) * D;
@@ -266,6 +268,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
     if (!ac.ok()) return SSM_ERR_ALIAS;
     ssm::ScanBwdArgs a{};
     a.B = Bn; a.L = L; a.D = D; a.N = N; a.W = W; a.bf16 = desc->io_dtype == SSM_BF16; a.disc = desc->disc;
+    a.chunk = chunk;
     a.x = x; a.dt = dt_raw; a.dt_bias = dt_bias; a.A_log = A_log; a.Bm = B; a.Cm = C; a.Dskip = Dskip;
     a.z = z; a.h0 = h0; a.dy = dy; a.dhT = dhT;
     a.conv_w = W > 0 ? conv_w : nullptr; a.conv_b = W > 0 ? conv_b : nullptr;

@@ -43,8 +43,16 @@ int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N);
 size_t scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int W,
                                 int64_t chunk_len);
 hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s);
+// The exact state at the start of every time chunk (chunks of `chunk` tokens,
+// at least two): local scans of chunks 0..K-2, then the carries.  agg_h
+// [B, K, D, N] receives the start states (chunk 0: h0), agg_s [B, K, D] the
+// sums of dt of chunks 0..K-2.  Only x, dt, dt_bias, A_log, B, the conv
+// inputs and h0 of `a` are read.
+hipError_t launch_scan_chunk_starts(const ScanFwdArgs &a, int64_t chunk, float *agg_h, float *agg_s,
+                                   hipStream_t s);
 struct ScanBwdArgs {
     int64_t B, L, D, N;
+    int64_t chunk;           // resolved time-chunk length (>= L: no split)
     int W;                   // conv width, 0 = no conv prologue
     int bf16;
     int disc;
@@ -66,7 +74,10 @@ struct ScanBwdArgs {
     float *dconv_w, *dconv_b, *dconv_state_in;
     void *ws;
 };
-size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N);
+// Time-chunk length of the backward for this shape and request (0: the
+// library's choice, -1: never split, > 0: rounded up to a multiple of 64).
+int64_t scan_bwd_chunk(int64_t B, int64_t L, int64_t D, int64_t N, int64_t requested);
+size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk);
 hipError_t launch_scan_bwd(const ScanBwdArgs &a, hipStream_t s);
 
 struct StepArgs {

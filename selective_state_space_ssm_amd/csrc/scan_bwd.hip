@@ -73,6 +73,32 @@ constexpr int kXR = 50;
 // expcnt and lgkmcnt left at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
 
+// Token i's per-token value of a 16-lane row, broadcast across the row from
+// lane i mod 16 (entry i / 16 of the lane's array).  i is a compile-time
+// constant at every call (unrolled loops), so the switch folds to one DPP.
+template <int TP>
+__device__ __forceinline__ float tok_bcast(const float (&v)[TP], int i) {
+    const float src = v[i >> 4];
+    switch (i & 15) {
+        case 0: return row_bcast<0>(src);
+        case 1: return row_bcast<1>(src);
+        case 2: return row_bcast<2>(src);
+        case 3: return row_bcast<3>(src);
+        case 4: return row_bcast<4>(src);
+        case 5: return row_bcast<5>(src);
+        case 6: return row_bcast<6>(src);
+        case 7: return row_bcast<7>(src);
+        case 8: return row_bcast<8>(src);
+        case 9: return row_bcast<9>(src);
+        case 10: return row_bcast<10>(src);
+        case 11: return row_bcast<11>(src);
+        case 12: return row_bcast<12>(src);
+        case 13: return row_bcast<13>(src);
+        case 14: return row_bcast<14>(src);
+        default: return row_bcast<15>(src);
+    }
+}
+
 struct BwdParams {
     const void *u, *dt;      // u: the conv input x when the conv prologue is on
     const float *dt_bias, *A_log;
@@ -80,19 +106,24 @@ struct BwdParams {
     const float *Dskip;
     const void *z;
     const void *dy;
-    const float *h0, *dhT;
+    const float *h0, *dhT;   // start state and end adjoint of each chunk:
+    int64_t h0_bs, h0_ks;    //   element (b, k) at b * bs + k * ks (floats)
+    int64_t dhT_bs, dhT_ks;
     const float *conv_w, *conv_b, *conv_hist;   // [D, W], [D], [B, W-1, D]
     float *dhist;            // [B, W-1, D] gradient of the carried history
-    float *ckpt;             // [B, K, D, N] states at tile starts
+    float *bnd;              // [B, KC, W-1, D] the same for chunks 1.. (their first W-1 inputs' left part)
+    float *ckpt;             // [B, Kt, D, N] states at tile starts
     void *du, *ddt, *dz;
     float *dh0;
     float *pB, *pC;          // [G, B, L, N] per-workgroup channel partials
-    float *pA;               // [B, D, N]   dLoss/dA summed over time
-    float *pD, *pT;          // [B, D]      dDskip, d_dt_bias summed over time
-    float *pW, *pCb;         // [B, D, 8] (taps right-aligned), [B, D]: conv taps, bias
+    float *pA;               // [B, KC, D, N] dLoss/dA summed over each chunk
+    float *pD, *pT;          // [B, KC, D]    dDskip, d_dt_bias summed over each chunk
+    float *pW, *pCb;         // [B, KC, D, 8] (taps right-aligned), [B, KC, D]: conv taps, bias
     int64_t B, L, D, N;
     int W;
-    int K;                   // tiles along time
+    int Kt;                  // tiles along the whole sequence
+    int64_t chunk;           // tokens per time chunk (a multiple of 64)
+    int KC;                  // time chunks
     int G;                   // channel workgroups per batch row
 };
 
@@ -132,14 +163,19 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     const int rw = lane >> 4, l = lane & 15;
     const int cl = wv * 4 + rw;                 // channel within the workgroup
     const int64_t grp = blockIdx.x % p.G;
-    const int64_t b = blockIdx.x / p.G;
+    const int64_t kc = (blockIdx.x / p.G) % p.KC;   // time chunk
+    const int64_t b = blockIdx.x / p.G / p.KC;
     const int64_t N = p.N, D = p.D, L = p.L;
+    // this workgroup's tokens [kc*chunk, Le): tiles tile0 .. tile0 + K - 1
+    const int64_t Le = min(L, (kc + 1) * p.chunk);
+    const int Kt = p.Kt;
+    const int tile0 = (int)(kc * p.chunk / T);
+    const int K = (int)((Le - kc * p.chunk + T - 1) / T);
     const int64_t d0 = grp * kCPB;
     const int64_t d = d0 + cl;
     const bool dvalid = d < D;
     const int64_t dc = dvalid ? d : (D - 1);
     const bool gate = Z != nullptr;
-    const int K = p.K;
 
     // this lane's states n = l + 16 s
     float A2[S], An[S], Ainv[S];
@@ -173,12 +209,12 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     // range (tokens past L, channels past D, states past N) stage as zeros.
     float ru[XUL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL], rck[S];
     auto fetch = [&](int k, bool bwd) {
-        const int64_t ts = (int64_t)k * T;
+        const int64_t ts = (int64_t)(tile0 + k) * T;
         if (bwd) {
             // this lane's own checkpoint of the tile (written in phase 1)
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                rck[s] = sv[s] ? p.ckpt[((b * K + k) * D + dc) * N + l + 16 * s] : 0.0f;
+                rck[s] = sv[s] ? p.ckpt[((b * Kt + tile0 + k) * D + dc) * N + l + 16 * s] : 0.0f;
         }
 #pragma unroll
         for (int q = 0; q < XUL; ++q) {
@@ -188,7 +224,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             const int rr = e / kCPB, cc = e % kCPB;
             const int64_t t = ts + rr - XH;
             float v = 0.0f;
-            if (e < XUE && t < L && d0 + cc < D) {
+            if (e < XUE && t < Le && d0 + cc < D) {
                 if (!CONV || t >= 0)
                     v = to_f32(U[(b * L + t) * D + d0 + cc]);
                 else if (p.conv_hist != nullptr && t >= -(int64_t)(W - 1))
@@ -200,7 +236,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         for (int q = 0; q < XL; ++q) {
             const int e = q * kThreads + tid;
             const int tt = e / kCPB, cc = e % kCPB;
-            const bool v = e < XE && ts + tt < L && d0 + cc < D;
+            const bool v = e < XE && ts + tt < Le && d0 + cc < D;
             const int64_t o = (b * L + ts + tt) * D + d0 + cc;
             rdt[q] = v ? to_f32(DT[o]) : 0.0f;
             if (bwd) {
@@ -212,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         for (int q = 0; q < BL; ++q) {
             const int e = q * kThreads + tid;
             const int tt = e / NP, n = e % NP;
-            const bool v = e < BE && ts + tt < L && n < N;
+            const bool v = e < BE && ts + tt < Le && n < N;
             const int64_t o = (b * L + ts + tt) * N + n;
             rB[q] = v ? to_f32(Bp[o]) : 0.0f;
             if (bwd) rC[q] = v ? to_f32(Cp[o]) : 0.0f;
@@ -257,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int jj = 0; jj < TP; ++jj) {
             const int tt = l + 16 * jj;
-            const bool v = tt < T && ts + tt < L;
+            const bool v = tt < T && ts + tt < Le;
             const int tc = min(tt, T - 1);
             const int e = tc * kXR + cl;
             float uu;
@@ -278,33 +314,13 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         }
     };
     // token i's per-token value, broadcast across the row from lane i mod 16
-    auto tokv = [&](const float (&v)[TP], int i) -> float {
-        const float src = v[i >> 4];
-        switch (i & 15) {
-            case 0: return row_bcast<0>(src);
-            case 1: return row_bcast<1>(src);
-            case 2: return row_bcast<2>(src);
-            case 3: return row_bcast<3>(src);
-            case 4: return row_bcast<4>(src);
-            case 5: return row_bcast<5>(src);
-            case 6: return row_bcast<6>(src);
-            case 7: return row_bcast<7>(src);
-            case 8: return row_bcast<8>(src);
-            case 9: return row_bcast<9>(src);
-            case 10: return row_bcast<10>(src);
-            case 11: return row_bcast<11>(src);
-            case 12: return row_bcast<12>(src);
-            case 13: return row_bcast<13>(src);
-            case 14: return row_bcast<14>(src);
-            default: return row_bcast<15>(src);
-        }
-    };
+    auto tokv = [&](const float (&v)[TP], int i) -> float { return tok_bcast<TP>(v, i); };
 
     // ================= phase 1: checkpoints at every tile start
     float h[S];
 #pragma unroll
     for (int s = 0; s < S; ++s)
-        h[s] = (p.h0 != nullptr && sv[s]) ? p.h0[(b * D + dc) * N + l + 16 * s] : 0.0f;
+        h[s] = (p.h0 != nullptr && sv[s]) ? p.h0[b * p.h0_bs + kc * p.h0_ks + dc * N + l + 16 * s] : 0.0f;
     // A wait for loaded data also waits for every store still in flight, so
     // each store is issued right after a wait and has a whole tile of work
     // to complete before the next one.
@@ -312,7 +328,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         if (dvalid) {
 #pragma unroll
             for (int s = 0; s < S; ++s)
-                if (sv[s]) p.ckpt[((b * K + k) * D + d) * N + l + 16 * s] = h[s];
+                if (sv[s]) p.ckpt[((b * Kt + tile0 + k) * D + d) * N + l + 16 * s] = h[s];
         }
     };
     // Values loaded before the tile loops and first used inside them are
@@ -333,7 +349,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         __syncthreads();
         store_ckpt(k);
         if (k + 2 < K) fetch(k + 1, false);
-        transform_fwd((int64_t)k * T);
+        transform_fwd((int64_t)(tile0 + k) * T);
 #pragma unroll
         for (int i = 0; i < T; ++i) {
             const float dli = tokv(tk_dl, i), dui = tokv(tk_du, i);
@@ -357,7 +373,8 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     float g[S], dA[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        g[s] = (p.dhT != nullptr && dvalid && sv[s]) ? p.dhT[(b * D + d) * N + l + 16 * s] : 0.0f;
+        g[s] = (p.dhT != nullptr && dvalid && sv[s]) ? p.dhT[b * p.dhT_bs + kc * p.dhT_ks + d * N + l + 16 * s]
+                                                     : 0.0f;
         dA[s] = 0.0f;
     }
     float accD = 0.0f, accT = 0.0f;   // over this lane's tokens: dyv*u and d_dt_raw
@@ -388,12 +405,12 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         }
     };
     auto store_out = [&](int k) {
-        const int64_t ts = (int64_t)k * T;
+        const int64_t ts = (int64_t)(tile0 + k) * T;
 #pragma unroll
         for (int q = 0; q < XL; ++q) {
             const int e = q * kThreads + tid;
             const int tt = e / kCPB, cc = e % kCPB;
-            if (e < XE && ts + tt < L && d0 + cc < D) {
+            if (e < XE && ts + tt < Le && d0 + cc < D) {
                 const int64_t o = (b * L + ts + tt) * D + d0 + cc;
                 if (DU) store_io(DU + o, odx[q]);
                 if (DDT) store_io(DDT + o, oddt[q]);
@@ -404,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         for (int q = 0; q < BL; ++q) {
             const int e = q * kThreads + tid;
             const int i = e / NP, n = e % NP;
-            if (e < BE && n < N && ts + i < L) {
+            if (e < BE && n < N && ts + i < Le) {
                 const int64_t o = ((grp * p.B + b) * L + ts + i) * N + n;
                 p.pB[o] = oB[q];
                 p.pC[o] = oC[q];
@@ -414,7 +431,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 
     if (K > 0) fetch(K - 1, true);
     for (int k = K - 1; k >= 0; --k) {
-        const int64_t ts = (int64_t)k * T;
+        const int64_t ts = (int64_t)(tile0 + k) * T;
         __syncthreads();
         stage(true);
         float hck[S];
@@ -435,7 +452,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int jj = 0; jj < TP; ++jj) {
             const int tt = l + 16 * jj;
-            const bool v = tt < T && ts + tt < L && dvalid;
+            const bool v = tt < T && ts + tt < Le && dvalid;
             const int e = min(tt, T - 1) * kXR + cl;
             tk_v[jj] = v;
             tk_sg[jj] = sigmoid_f(s_dt[e] + dtb);
@@ -602,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         // dB, dC partials of this workgroup: its 48 channels in order
         for (int e = tid; e < T * NP; e += kThreads) {
             const int i = e / NP, n = e % NP;
-            if (n < N && ts + i < L) {
+            if (n < N && ts + i < Le) {
                 float sb = 0.0f, sc = 0.0f;
 #pragma unroll 8
                 for (int c2 = 0; c2 < kCPB; ++c2) {
@@ -642,20 +659,29 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     pr[10] = accT;
     const float sr = row_transpose_sum(pr, l);
     if (dvalid) {
+        const int64_t bk = b * p.KC + kc;   // partials per (batch row, chunk)
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             if (sv[s]) {
-                const int64_t o = (b * D + d) * N + l + 16 * s;
-                if (p.dh0 != nullptr) p.dh0[o] = g[s];
-                p.pA[o] = dA[s];
+                if (p.dh0 != nullptr && kc == 0) p.dh0[(b * D + d) * N + l + 16 * s] = g[s];
+                p.pA[(bk * D + d) * N + l + 16 * s] = dA[s];
             }
         }
-        if (l == 9) p.pD[b * D + d] = sr;
-        if (l == 10) p.pT[b * D + d] = sr;
+        if (l == 9) p.pD[bk * D + d] = sr;
+        if (l == 10) p.pT[bk * D + d] = sr;
         if constexpr (CONV) {
-            if (l < 8) p.pW[(b * D + d) * 8 + l] = sr;
-            if (l == 8) p.pCb[b * D + d] = sr;
-            if (l < W - 1 && p.dhist != nullptr) p.dhist[(b * (W - 1) + l) * D + d] = dhist;
+            if (l < 8) p.pW[(bk * D + d) * 8 + l] = sr;
+            if (l == 8) p.pCb[bk * D + d] = sr;
+            // the first W-1 inputs before the chunk: the carried history for
+            // chunk 0, else the previous chunk's last inputs (added to its dx
+            // by bwd_conv_boundary)
+            if (l < W - 1) {
+                if (kc == 0) {
+                    if (p.dhist != nullptr) p.dhist[(b * (W - 1) + l) * D + d] = dhist;
+                } else {
+                    p.bnd[(bk * (W - 1) + l) * D + d] = dhist;
+                }
+            }
         }
     }
 }
@@ -707,19 +733,170 @@ __global__ __launch_bounds__(256) void bwd_reduce_params(const float *A_log, con
     }
 }
 
+// ---------------------------------------------------------------- time chunks
+// Long sequences with few channel workgroups split time into chunks, each
+// run by its own workgroups (the main kernel above, with the chunk's exact
+// start state and end adjoint).  The start states come from the forward's
+// chunk scan and carry.  The end adjoints follow from the backward
+// recurrence g_{t-1} = a_t (C_t dyv_t + g_t), affine in g: over a chunk,
+// g_start = Lambda * g_end + R with Lambda = prod a_t = 2^(A log2e sum dt) and
+// R the chunk's g_start from g_end = 0.  bwd_local_kernel computes R and
+// sum dt of chunks 1..KC-1; bwd_carry_kernel walks the chunks from last to
+// first: G_{KC-1} = dhT, G_{k-1} = Lambda_k G_k + R_k.
+
+struct BwdLocalParams {
+    const void *dt, *Cm, *z, *dy;
+    const float *dt_bias, *A_log;
+    float *R;                // [B, KC, D, N]
+    float *Sdt;              // [B, KC, D]
+    int64_t B, L, D, N;
+    int64_t chunk;
+    int KC;
+    int G;
+};
+
+template <typename IOT, int S>
+__global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
+    using Gm = BGeo<S>;
+    constexpr int NP = Gm::NP, T = Gm::T, TP = Gm::TP;
+    __shared__ float s_dt[T * kXR], s_z[T * kXR], s_dy[T * kXR];
+    __shared__ float s_C[T * NP];
+    const IOT *DT = static_cast<const IOT *>(p.dt);
+    const IOT *Cp = static_cast<const IOT *>(p.Cm);
+    const IOT *Z = static_cast<const IOT *>(p.z);
+    const IOT *DY = static_cast<const IOT *>(p.dy);
+
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6, lane = tid & 63;
+    const int rw = lane >> 4, l = lane & 15;
+    const int cl = wv * 4 + rw;
+    const int64_t grp = blockIdx.x % p.G;
+    const int64_t kc = 1 + (blockIdx.x / p.G) % (p.KC - 1);
+    const int64_t b = blockIdx.x / p.G / (p.KC - 1);
+    const int64_t N = p.N, D = p.D, L = p.L;
+    const int64_t t0 = kc * p.chunk, Le = min(L, t0 + p.chunk);
+    const int K = (int)((Le - t0 + T - 1) / T);
+    const int64_t d0 = grp * kCPB, d = d0 + cl;
+    const bool dvalid = d < D;
+    const int64_t dc = dvalid ? d : (D - 1);
+    const bool gate = Z != nullptr;
+
+    float A2[S], g[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int n = l + 16 * s;
+        A2[s] = n < N ? neg_exp_f(p.A_log[dc * N + n]) * kLog2e : 0.0f;
+        g[s] = 0.0f;
+    }
+    const float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    float sdl = 0.0f;   // sum of dt over this lane's tokens
+
+    for (int k = K - 1; k >= 0; --k) {
+        const int64_t ts = t0 + (int64_t)k * T;
+        __syncthreads();
+        for (int e = tid; e < T * kCPB; e += kThreads) {
+            const int tt = e / kCPB, cc = e % kCPB;
+            const bool v = ts + tt < Le && d0 + cc < D;
+            const int64_t o = (b * L + ts + tt) * D + d0 + cc;
+            s_dt[tt * kXR + cc] = v ? to_f32(DT[o]) : 0.0f;
+            s_dy[tt * kXR + cc] = v ? to_f32(DY[o]) : 0.0f;
+            s_z[tt * kXR + cc] = (v && gate) ? to_f32(Z[o]) : 0.0f;
+        }
+        for (int e = tid; e < T * NP; e += kThreads) {
+            const int tt = e / NP, n = e % NP;
+            s_C[e] = (ts + tt < Le && n < N) ? to_f32(Cp[(b * L + ts + tt) * N + n]) : 0.0f;
+        }
+        __syncthreads();
+        // per-token values of this lane's tokens; tokens past the chunk get
+        // dt = dyv = 0, which leaves g unchanged
+        float tk_dl[TP], tk_dyv[TP];
+#pragma unroll
+        for (int jj = 0; jj < TP; ++jj) {
+            const int tt = l + 16 * jj;
+            const bool v = tt < T && ts + tt < Le;
+            const int e = min(tt, T - 1) * kXR + cl;
+            const float dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
+            const float dyr = v ? s_dy[e] : 0.0f;
+            tk_dl[jj] = dl;
+            tk_dyv[jj] = gate ? dyr * silu_f(s_z[e]) : dyr;
+            sdl += dl;
+        }
+#pragma unroll
+        for (int i = T - 1; i >= 0; --i) {
+            const float dli = tok_bcast<TP>(tk_dl, i), dyv = tok_bcast<TP>(tk_dyv, i);
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const float gj = fmaf(s_C[i * NP + l + 16 * s], dyv, g[s]);
+                g[s] = hw_exp2(dli * A2[s]) * gj;
+            }
+        }
+    }
+    float pr[16];
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) pr[kk] = kk == 0 ? sdl : 0.0f;
+    const float sum = row_transpose_sum(pr, l);
+    if (dvalid) {
+        const int64_t bk = b * p.KC + kc;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+            if (l + 16 * s < N) p.R[(bk * D + d) * N + l + 16 * s] = g[s];
+        if (l == 0) p.Sdt[bk * D + d] = sum;
+    }
+}
+
+// RG holds R_k (k >= 1) on entry and the end adjoint G_k of every chunk on exit.
+__global__ __launch_bounds__(256) void bwd_carry_kernel(const float *A_log, const float *dhT, float *RG,
+                                                        const float *Sdt, int64_t B, int64_t D, int64_t N,
+                                                        int KC) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= B * D * N) return;
+    const int64_t n = i % N, d = (i / N) % D, b = i / (N * D);
+    const float A2 = neg_exp_f(A_log[d * N + n]) * kLog2e;
+    float G = dhT ? dhT[i] : 0.0f;
+    for (int k = KC - 1; k >= 0; --k) {
+        const int64_t o = ((b * KC + k) * D + d) * N + n;
+        const float Rk = k > 0 ? RG[o] : 0.0f;
+        RG[o] = G;
+        if (k > 0) G = fmaf(hw_exp2(A2 * Sdt[(b * KC + k) * D + d]), G, Rk);
+    }
+}
+
+// With the conv prologue, a chunk's last W-1 inputs also feed the next
+// chunk's first outputs; that chunk left the gradient in bnd.
+template <typename IOT>
+__global__ __launch_bounds__(256) void bwd_conv_boundary(IOT *dx, const float *bnd, int64_t B, int64_t L,
+                                                         int64_t D, int W, int KC, int64_t chunk) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t total = B * (KC - 1) * (W - 1) * D;
+    if (i >= total) return;
+    const int64_t dd = i % D, j = (i / D) % (W - 1), r = i / (D * (W - 1));
+    const int64_t kc = 1 + r % (KC - 1), b = r / (KC - 1);
+    const int64_t t = kc * chunk - (W - 1) + j;
+    if (t < 0 || t >= L) return;
+    const int64_t o = (b * L + t) * D + dd;
+    store_io(dx + o, to_f32(dx[o]) + bnd[((b * KC + kc) * (W - 1) + j) * D + dd]);
+}
+
 struct BwdWs {
     float *ckpt, *pB, *pC, *pA, *pD, *pT, *pW, *pCb;
+    float *agg_h, *agg_s, *RG, *Sdt, *bnd;   // time chunks only
 };
 
 int tile_len(int64_t N) { return N <= 16 ? 16 : (N <= 32 ? 8 : 4); }
 
-BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, size_t *total) {
+int64_t num_bwd_chunks(int64_t L, int64_t chunk) {
+    if (L <= 0 || chunk >= L) return 1;
+    return (L + chunk - 1) / chunk;
+}
+
+BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk, size_t *total) {
     const int T = tile_len(N);
     const int64_t K = std::max<int64_t>(1, (L + T - 1) / T);
     const int64_t G = (D + kCPB - 1) / kCPB;
+    const int64_t KC = num_bwd_chunks(L, chunk);
     char *base = static_cast<char *>(ws);
     size_t off = 0;
-    BwdWs r;
+    BwdWs r{};
     auto take = [&](size_t n) {
         float *ptr = reinterpret_cast<float *>(base ? base + off : nullptr);
         off += ws_align(n * sizeof(float));
@@ -728,30 +905,69 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, size_t *total)
     r.ckpt = take((size_t)(B * K * D * N));
     r.pB = take((size_t)(G * B * L * N));
     r.pC = take((size_t)(G * B * L * N));
-    r.pA = take((size_t)(B * D * N));
-    r.pD = take((size_t)(B * D));
-    r.pT = take((size_t)(B * D));
-    r.pW = take((size_t)(B * D * 8));
-    r.pCb = take((size_t)(B * D));
+    r.pA = take((size_t)(B * KC * D * N));
+    r.pD = take((size_t)(B * KC * D));
+    r.pT = take((size_t)(B * KC * D));
+    r.pW = take((size_t)(B * KC * D * 8));
+    r.pCb = take((size_t)(B * KC * D));
+    if (KC > 1) {
+        r.agg_h = take((size_t)(B * KC * D * N));
+        r.agg_s = take((size_t)(B * KC * D));
+        r.RG = take((size_t)(B * KC * D * N));
+        r.Sdt = take((size_t)(B * KC * D));
+        r.bnd = take((size_t)(B * KC * (SSM_MAX_CONV_WIDTH_DEV - 1) * D));
+    }
     if (total) *total = off;
     return r;
 }
 
 template <typename IOT, int S>
 hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s) {
+    const int64_t KC = num_bwd_chunks(a.L, a.chunk);
+    const int G = (int)((a.D + kCPB - 1) / kCPB);
+    hipError_t e;
     BwdParams p{};
+    p.h0 = a.h0; p.h0_bs = a.D * a.N; p.h0_ks = 0;
+    p.dhT = a.dhT; p.dhT_bs = a.D * a.N; p.dhT_ks = 0;
+    if (KC > 1) {
+        // start states of the chunks (forward chunk scan + carry)
+        ScanFwdArgs f{};
+        f.B = a.B; f.L = a.L; f.D = a.D; f.N = a.N; f.W = a.W; f.bf16 = a.bf16; f.disc = a.disc;
+        f.x = a.x; f.dt = a.dt; f.dt_bias = a.dt_bias; f.A_log = a.A_log; f.Bm = a.Bm; f.Cm = a.Cm;
+        f.conv_w = a.conv_w; f.conv_b = a.conv_b; f.conv_state_in = a.conv_state_in; f.h0 = a.h0;
+        e = launch_scan_chunk_starts(f, a.chunk, w.agg_h, w.agg_s, s);
+        if (e != hipSuccess) return e;
+        // local end-to-start adjoints of chunks 1.., then the end adjoints
+        BwdLocalParams q{};
+        q.dt = a.dt; q.Cm = a.Cm; q.z = a.z; q.dy = a.dy; q.dt_bias = a.dt_bias; q.A_log = a.A_log;
+        q.R = w.RG; q.Sdt = w.Sdt;
+        q.B = a.B; q.L = a.L; q.D = a.D; q.N = a.N; q.chunk = a.chunk; q.KC = (int)KC; q.G = G;
+        hipLaunchKernelGGL((bwd_local_kernel<IOT, S>), dim3((unsigned)(a.B * (KC - 1) * G)), dim3(kThreads), 0,
+                           s, q);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t nstate = a.B * a.D * a.N;
+        hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, a.A_log,
+                           a.dhT, w.RG, w.Sdt, a.B, a.D, a.N, (int)KC);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.h0 = w.agg_h; p.h0_bs = KC * a.D * a.N; p.h0_ks = a.D * a.N;
+        p.dhT = w.RG; p.dhT_bs = KC * a.D * a.N; p.dhT_ks = a.D * a.N;
+    }
     p.u = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
     p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z; p.dy = a.dy;
-    p.h0 = a.h0; p.dhT = a.dhT;
     p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_hist = a.conv_state_in; p.dhist = a.dconv_state_in;
+    p.bnd = w.bnd;
     p.ckpt = w.ckpt;
     p.du = a.dx; p.ddt = a.ddt; p.dz = a.dz; p.dh0 = a.dh0;
     p.pB = w.pB; p.pC = w.pC; p.pA = w.pA; p.pD = w.pD; p.pT = w.pT; p.pW = w.pW; p.pCb = w.pCb;
     p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N; p.W = a.W;
     constexpr int T = BGeo<S>::T;
-    p.K = (int)((a.L + T - 1) / T);
-    p.G = (int)((a.D + kCPB - 1) / kCPB);
-    const int64_t blocks = (int64_t)p.G * a.B;
+    p.Kt = (int)((a.L + T - 1) / T);
+    p.chunk = KC > 1 ? a.chunk : std::max<int64_t>(a.L, 1);
+    p.KC = (int)KC;
+    p.G = G;
+    const int64_t blocks = (int64_t)G * KC * a.B;
     const dim3 grid((unsigned)blocks), block(kThreads);
     if (a.disc == DISC_ZOH) {
         if (a.W > 0)
@@ -764,18 +980,25 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
         else
             hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB, false>), grid, block, 0, s, p);
     }
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if (KC > 1 && a.W > 1 && a.dx != nullptr) {
+        const int64_t nb = a.B * (KC - 1) * (a.W - 1) * a.D;
+        hipLaunchKernelGGL((bwd_conv_boundary<IOT>), dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
+                           static_cast<IOT *>(a.dx), w.bnd, a.B, a.L, a.D, a.W, (int)KC, a.chunk);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     const int64_t total = a.B * a.L * a.N;
     if ((a.dB || a.dC) && total > 0) {
         hipLaunchKernelGGL((bwd_reduce_bc<IOT>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w.pB,
-                           w.pC, p.G, total, static_cast<IOT *>(a.dB), static_cast<IOT *>(a.dC));
+                           w.pC, G, total, static_cast<IOT *>(a.dB), static_cast<IOT *>(a.dC));
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int64_t pn = std::max(std::max(a.D * a.N, a.D), a.D * a.W);
     hipLaunchKernelGGL(bwd_reduce_params, dim3((unsigned)((pn + 255) / 256)), dim3(256), 0, s, a.A_log, w.pA,
-                       w.pD, w.pT, w.pW, w.pCb, a.B, a.D, a.N, a.W, a.dA_log, a.dD, a.ddt_bias,
+                       w.pD, w.pT, w.pW, w.pCb, a.B * KC, a.D, a.N, a.W, a.dA_log, a.dD, a.ddt_bias,
                        a.W > 0 ? a.dconv_w : nullptr, a.W > 0 ? a.dconv_b : nullptr);
     return hipGetLastError();
 }
@@ -789,14 +1012,29 @@ hipError_t launch_bwd_s(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s) {
 
 }  // namespace
 
-size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N) {
+int64_t scan_bwd_chunk(int64_t B, int64_t L, int64_t D, int64_t N, int64_t requested) {
+    (void)N;
+    const int64_t whole = L > 0 ? L : 1;
+    if (requested < 0) return whole;
+    if (requested > 0) return std::min<int64_t>((requested + 63) / 64 * 64, whole);
+    // the library's choice: about one workgroup per CU (256 CUs), chunks of
+    // at least 1024 tokens
+    const int64_t wgs = B * ((D + kCPB - 1) / kCPB);
+    if (wgs >= 128 || L < 2048) return whole;
+    int64_t KC = std::min<int64_t>((256 + wgs - 1) / wgs, L / 1024);
+    if (KC <= 1) return whole;
+    const int64_t chunk = ((L + KC - 1) / KC + 63) / 64 * 64;
+    return std::min<int64_t>(chunk, whole);
+}
+
+size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk) {
     size_t total = 0;
-    carve(nullptr, B, L, D, N, &total);
+    carve(nullptr, B, L, D, N, chunk, &total);
     return total;
 }
 
 hipError_t launch_scan_bwd(const ScanBwdArgs &a, hipStream_t s) {
-    BwdWs w = carve(a.ws, a.B, a.L, a.D, a.N, nullptr);
+    BwdWs w = carve(a.ws, a.B, a.L, a.D, a.N, a.chunk, nullptr);
     if (a.bf16) return launch_bwd_s<bf16_t>(a, w, s);
     return launch_bwd_s<float>(a, w, s);
 }

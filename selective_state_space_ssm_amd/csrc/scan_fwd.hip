@@ -600,6 +600,29 @@ size_t scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int 
            ws_align(sizeof(float) * (size_t)(B * (W > 1 ? W - 1 : 0) * D));
 }
 
+hipError_t launch_scan_chunk_starts(const ScanFwdArgs &a, int64_t chunk, float *agg_h, float *agg_s,
+                                   hipStream_t s) {
+    FwdParams p{};
+    p.x = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
+    p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = nullptr; p.z = nullptr;
+    p.conv_w = a.conv_w; p.conv_b = a.conv_b;
+    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N; p.W = a.W;
+    p.groups = (int)((a.D + kCPW - 1) / kCPW);
+    const int64_t K = num_chunks(a.L, chunk);
+    if (K <= 1) return hipErrorInvalidValue;
+    p.chunk = chunk;
+    p.K = (int)K;
+    p.agg_h = agg_h; p.agg_s = agg_s;
+    p.Kgrid = (int)K - 1;
+    p.conv_hist = a.conv_state_in;
+    hipError_t e = dispatch(p, a.bf16, a.disc, a.W > 0, MODE_LOCAL, s);
+    if (e != hipSuccess) return e;
+    const int64_t total = a.B * a.D * a.N;
+    hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.A_log, a.h0,
+                       agg_h, agg_s, a.B, a.D, a.N, (int)K, nullptr, nullptr, (int64_t)0);
+    return hipGetLastError();
+}
+
 hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s) {
     FwdParams p{};
     p.x = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;

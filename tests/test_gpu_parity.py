@@ -22,11 +22,14 @@ def ssm():
     return m
 
 
-def _rand(seed, Bn, L, D, N, W=4, bf16=False, scale_dt=1.0):
+def _rand(seed, Bn, L, D, N, W=4, bf16=False, scale_dt=1.0, slow=False):
+    """Seeded normal inputs.  slow=True draws A_log around -4 (|A| ~ 0.02), so
+    the state and the adjoint carry across hundreds of tokens."""
     r = np.random.default_rng(seed)
     f = lambda *s: r.standard_normal(s).astype(np.float32)
+    a_log = (0.2 * f(D, N) - 4.0).astype(np.float32) if slow else 0.5 * f(D, N)
     p = dict(x=f(Bn, L, D), dt_raw=(f(Bn, L, D) * np.float32(scale_dt)), B=f(Bn, L, N), C=f(Bn, L, N),
-             z=f(Bn, L, D), dy=f(Bn, L, D), dt_bias=(0.3 * f(D)), A_log=(0.5 * f(D, N)),
+             z=f(Bn, L, D), dy=f(Bn, L, D), dt_bias=(0.3 * f(D)), A_log=a_log,
              Dskip=f(D), h0=f(Bn, D, N), dhT=f(Bn, D, N), conv_w=f(D, W), conv_b=f(D),
              conv_state=f(Bn, max(W - 1, 0), D))
     if bf16:
@@ -420,7 +423,8 @@ _GRADS = ["dx", "d_dt_raw", "d_dt_bias", "dA_log", "dB", "dC", "dD", "dz", "dh0"
 _CONV_GRADS = ["dconv_w", "dconv_b", "dconv_state"]
 
 
-def _bwd_check(ssm, p, dtype, disc, gate=True, h0=True, dhT=True, conv=False, state=False, tolerance=None):
+def _bwd_check(ssm, p, dtype, disc, gate=True, h0=True, dhT=True, conv=False, state=False, tolerance=None,
+               chunk=0):
     """ssm_scan_bwd against the oracle.  With conv, x is the conv input and
     the expected gradients come from the oracle's conv, its scan backward on
     the conv output, and its conv backward on that dLoss/du."""
@@ -432,7 +436,8 @@ def _bwd_check(ssm, p, dtype, disc, gate=True, h0=True, dhT=True, conv=False, st
                          Dskip=dev(p["Dskip"]), z=dev(p["z"], dtype) if gate else None,
                          conv_w=dev(p["conv_w"]) if conv else None, conv_b=dev(p["conv_b"]) if conv else None,
                          conv_state_in=dev(st) if st is not None else None,
-                         h0=dev(p["h0"]) if h0 else None, dhT=dev(p["dhT"]) if dhT else None, disc=disc)
+                         h0=dev(p["h0"]) if h0 else None, dhT=dev(p["dhT"]) if dhT else None, disc=disc,
+                         chunk_len=chunk)
     torch.cuda.synchronize()
     u = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"], st)[0] if conv else p["x"]
     r = oracle.scan_bwd(u, p["dt_raw"], p["A_log"], p["B"], p["C"], p["dy"], dt_bias=p["dt_bias"],
@@ -545,3 +550,56 @@ def test_bwd_conv_deterministic(ssm):
     b = _bwd_check(ssm, p, torch.float32, DB, conv=True, state=True)
     for k in _GRADS + _CONV_GRADS:
         assert torch.equal(a[k], b[k]), k
+
+
+# --------------------------------------------------------------------------- backward split in time
+
+@pytest.mark.parametrize("Bn,L,D,N,chunk,W,state", [
+    (1, 600, 40, 16, 128, 0, False),     # ragged L and D, last chunk partial
+    (2, 1000, 24, 3, 64, 0, False),
+    (1, 300, 70, 33, 64, 0, False),      # 8-token tiles
+    (1, 200, 16, 64, 64, 0, False),      # 4-token tiles
+    (1, 700, 40, 16, 128, 4, True),      # conv: the boundary inputs feed two chunks
+    (1, 500, 48, 16, 64, 8, True),
+    (1, 130, 16, 16, 64, 2, False),      # a 2-token last chunk
+    (1, 64, 16, 16, 64, 4, True),        # chunk == L: no split
+])
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_bwd_chunked_shapes(ssm, Bn, L, D, N, chunk, W, state, disc):
+    """The backward split into time chunks (start states from the forward
+    chunk scan, end adjoints from the reverse walk) against the sequential
+    oracle."""
+    p = _rand(31, Bn, L, D, N, max(W, 1), slow=True)
+    _bwd_check(ssm, p, torch.float32, disc, conv=W > 0, state=state, chunk=chunk)
+
+
+def test_bwd_chunked_auto_bf16(ssm):
+    """Few channel workgroups and a long sequence: the library splits time on
+    its own (B 1, L 4096, D 64 -> 4 chunks of 1024)."""
+    p = _rand(32, 1, 4096, 64, 16, 4, bf16=True, slow=True)
+    d = ssm.ssm_scan_desc(1, 4096, 64, 16, 0, 1, 0, 0)
+    assert ssm.ssm_scan_bwd_workspace_size(d) > ssm.ssm_scan_bwd_workspace_size(
+        ssm.ssm_scan_desc(1, 4096, 64, 16, 0, 1, 0, -1))
+    _bwd_check(ssm, p, torch.bfloat16, DB)
+
+
+def test_bwd_chunked_matches_unsplit(ssm):
+    """Split and unsplit backward agree to rounding on the same inputs."""
+    p = _rand(33, 1, 1024, 48, 16, 4, slow=True)
+    args = (dev(p["x"]), dev(p["dt_raw"]), dev(p["A_log"]), dev(p["B"]), dev(p["C"]), dev(p["dy"]))
+    kw = dict(dt_bias=dev(p["dt_bias"]), Dskip=dev(p["Dskip"]), z=dev(p["z"]), conv_w=dev(p["conv_w"]),
+              conv_b=dev(p["conv_b"]), conv_state_in=dev(p["conv_state"]), h0=dev(p["h0"]), dhT=dev(p["dhT"]))
+    a = ssm.ssm_scan_bwd(*args, chunk_len=-1, **kw)
+    b = ssm.ssm_scan_bwd(*args, chunk_len=192, **kw)
+    torch.cuda.synchronize()
+    for k in _GRADS + _CONV_GRADS:
+        assert rel_linf(b[k], a[k]) <= FP32_TOL, k
+
+
+def test_bwd_long_sequence_bf16_workload(ssm):
+    """Backward of the long-sequence workload: batch 1, L=65,536, D_inner=1536,
+    N=16, bf16 inputs and gradients, float32 state, SiLU(z) gate; time split
+    by the library (8 chunks of 8192), against the sequential oracle."""
+    p = si.mamba_block(1, 65536, 1536, 16, 4, workload=si.WL_LONG, bf16=True, with_dy=True)
+    q = dict(p, h0=np.zeros((1, 1536, 16), np.float32), dhT=np.zeros((1, 1536, 16), np.float32))
+    _bwd_check(ssm, q, torch.bfloat16, DB, h0=False, dhT=False)
