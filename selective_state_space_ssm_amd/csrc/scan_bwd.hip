@@ -205,74 +205,102 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     }
     const float *wk = s_wk + cl * 8;
 
-    // ---- tile staging: registers one tile ahead, then LDS.  Values out of
-    // range (tokens past L, channels past D, states past N) stage as zeros.
-    float ru[XUL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL], rck[S];
+    // ---- tile staging: registers one tile ahead, then LDS.  Loads go through
+    // buffer descriptors whose range ends at the end of the chunk (tokens past
+    // it read 0), unconditionally, with 32-bit per-thread offsets on a scalar
+    // base, and are kept as raw io bits until staged.  Channels past D read
+    // neighbouring finite values that only feed lanes whose results are not
+    // stored; states past N are zeroed when staged (B and C must be zero
+    // there).  The first tile of a conv sequence, whose history rows come from
+    // conv_state_in, is loaded when staged instead (once per phase).
+    static_assert(kThreads % kCPB == 0 && kThreads % NP == 0, "offset strides");
+    typedef typename RawOf<IOT>::type raw_t;
+    const uint32_t es = sizeof(IOT);
+    const uint32_t xoff = (uint32_t)((tid / kCPB) * (int)D + tid % kCPB) * es;
+    const uint32_t xstep = (uint32_t)((kThreads / kCPB) * (int)D) * es;
+    const uint32_t boff = (uint32_t)((tid / NP) * (int)N + tid % NP) * es;
+    const uint32_t bstep = (uint32_t)((kThreads / NP) * (int)N) * es;
+    const uint32_t ckoff = (uint32_t)(dc * N + l) * 4u;
+    raw_t ru[XUL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL];
+    uint32_t rck[S];
     auto fetch = [&](int k, bool bwd) {
         const int64_t ts = (int64_t)(tile0 + k) * T;
+        const int64_t rows = Le - ts;   // tokens of the chunk from ts on
         if (bwd) {
             // this lane's own checkpoint of the tile (written in phase 1)
+            const buf_t bK = make_buf(p.ckpt + (b * Kt + tile0 + k) * D * N, (uint64_t)(D * N) * 4u);
 #pragma unroll
-            for (int s = 0; s < S; ++s)
-                rck[s] = sv[s] ? p.ckpt[((b * Kt + tile0 + k) * D + dc) * N + l + 16 * s] : 0.0f;
+            for (int s = 0; s < S; ++s) rck[s] = buf_ld_raw(bK, ckoff + 64u * s, p.ckpt);
         }
+        if (!(CONV && ts < XH)) {
+            const buf_t bU = make_buf(U + (b * L + ts - XH) * D + d0, (uint64_t)((rows + XH) * D - d0) * es);
 #pragma unroll
-        for (int q = 0; q < XUL; ++q) {
-            // row r of the first input holds token ts + r - XH; with the conv,
-            // tokens before 0 come from the carried history (or are zero)
-            const int e = q * kThreads + tid;
-            const int rr = e / kCPB, cc = e % kCPB;
-            const int64_t t = ts + rr - XH;
-            float v = 0.0f;
-            if (e < XUE && t < Le && d0 + cc < D) {
-                if (!CONV || t >= 0)
-                    v = to_f32(U[(b * L + t) * D + d0 + cc]);
-                else if (p.conv_hist != nullptr && t >= -(int64_t)(W - 1))
-                    v = p.conv_hist[(b * (W - 1) + (W - 1) + t) * D + d0 + cc];
-            }
-            ru[q] = v;
+            for (int q = 0; q < XUL; ++q) ru[q] = buf_ld_raw(bU, xoff + q * xstep, U);
         }
+        const uint64_t xr = (uint64_t)(rows * D - d0) * es;
+        const buf_t bDT = make_buf(DT + (b * L + ts) * D + d0, xr);
 #pragma unroll
-        for (int q = 0; q < XL; ++q) {
-            const int e = q * kThreads + tid;
-            const int tt = e / kCPB, cc = e % kCPB;
-            const bool v = e < XE && ts + tt < Le && d0 + cc < D;
-            const int64_t o = (b * L + ts + tt) * D + d0 + cc;
-            rdt[q] = v ? to_f32(DT[o]) : 0.0f;
-            if (bwd) {
-                rz[q] = (v && gate) ? to_f32(Z[o]) : 0.0f;
-                rdy[q] = v ? to_f32(DY[o]) : 0.0f;
+        for (int q = 0; q < XL; ++q) rdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
+        if (bwd) {
+            const buf_t bDY = make_buf(DY + (b * L + ts) * D + d0, xr);
+#pragma unroll
+            for (int q = 0; q < XL; ++q) rdy[q] = buf_ld_raw(bDY, xoff + q * xstep, DY);
+            if (gate) {
+                const buf_t bZ = make_buf(Z + (b * L + ts) * D + d0, xr);
+#pragma unroll
+                for (int q = 0; q < XL; ++q) rz[q] = buf_ld_raw(bZ, xoff + q * xstep, Z);
+            } else {
+#pragma unroll
+                for (int q = 0; q < XL; ++q) rz[q] = 0;
             }
         }
+        const uint64_t br = (uint64_t)(rows * N) * es;
+        const buf_t bB = make_buf(Bp + (b * L + ts) * N, br);
 #pragma unroll
-        for (int q = 0; q < BL; ++q) {
-            const int e = q * kThreads + tid;
-            const int tt = e / NP, n = e % NP;
-            const bool v = e < BE && ts + tt < Le && n < N;
-            const int64_t o = (b * L + ts + tt) * N + n;
-            rB[q] = v ? to_f32(Bp[o]) : 0.0f;
-            if (bwd) rC[q] = v ? to_f32(Cp[o]) : 0.0f;
+        for (int q = 0; q < BL; ++q) rB[q] = buf_ld_raw(bB, boff + q * bstep, Bp);
+        if (bwd) {
+            const buf_t bC = make_buf(Cp + (b * L + ts) * N, br);
+#pragma unroll
+            for (int q = 0; q < BL; ++q) rC[q] = buf_ld_raw(bC, boff + q * bstep, Cp);
         }
     };
-    auto stage = [&](bool bwd) {
+    const bool nval = (tid % NP) < N;   // the state of this thread's B, C elements
+    auto stage = [&](bool bwd, int k) {
         // One unconditional wait for the fetched tile: the staging writes
         // below are lane-masked, and a wait inside a masked block would not
         // count for the code after it.
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        const int64_t ts = (int64_t)(tile0 + k) * T;
+        if (CONV && ts < XH) {
+            // row r holds token ts + r - XH; before 0 the carried history
+            for (int e = tid; e < XUE; e += kThreads) {
+                const int rr = e / kCPB, cc = e % kCPB;
+                const int64_t t = ts + rr - XH;
+                float v = 0.0f;
+                if (t < Le && d0 + cc < D) {
+                    if (t >= 0)
+                        v = to_f32(U[(b * L + t) * D + d0 + cc]);
+                    else if (p.conv_hist != nullptr && t >= -(int64_t)(W - 1))
+                        v = p.conv_hist[(b * (W - 1) + (W - 1) + t) * D + d0 + cc];
+                }
+                s_u[rr * kXR + cc] = v;
+            }
+        } else {
 #pragma unroll
-        for (int q = 0; q < XUL; ++q) {
-            const int e = q * kThreads + tid;
-            if (e < XUE) s_u[(e / kCPB) * kXR + e % kCPB] = ru[q];
+            for (int q = 0; q < XUL; ++q) {
+                const int e = q * kThreads + tid;
+                if (e < XUE) s_u[(e / kCPB) * kXR + e % kCPB] = raw_f32(ru[q], U);
+            }
         }
 #pragma unroll
         for (int q = 0; q < XL; ++q) {
             const int e = q * kThreads + tid;
             if (e < XE) {
                 const int ep = (e / kCPB) * kXR + e % kCPB;
-                s_dt[ep] = rdt[q];
+                s_dt[ep] = raw_f32(rdt[q], DT);
                 if (bwd) {
-                    s_z[ep] = rz[q];
-                    s_dy[ep] = rdy[q];
+                    s_z[ep] = raw_f32(rz[q], Z);
+                    s_dy[ep] = raw_f32(rdy[q], DY);
                 }
             }
         }
@@ -280,8 +308,8 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         for (int q = 0; q < BL; ++q) {
             const int e = q * kThreads + tid;
             if (e < BE) {
-                s_B[e] = rB[q];
-                if (bwd) s_C[e] = rC[q];
+                s_B[e] = nval ? raw_f32(rB[q], Bp) : 0.0f;
+                if (bwd) s_C[e] = nval ? raw_f32(rC[q], Cp) : 0.0f;
             }
         }
     };
@@ -345,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             break;
         }
         __syncthreads();
-        stage(false);
+        stage(false, k);
         __syncthreads();
         store_ckpt(k);
         if (k + 2 < K) fetch(k + 1, false);
@@ -433,10 +461,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     for (int k = K - 1; k >= 0; --k) {
         const int64_t ts = (int64_t)(tile0 + k) * T;
         __syncthreads();
-        stage(true);
+        stage(true, k);
         float hck[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) hck[s] = rck[s];
+        for (int s = 0; s < S; ++s) hck[s] = sv[s] ? __uint_as_float(rck[s]) : 0.0f;
         if (k + 1 < K) read_out();
         if constexpr (CONV) {
             if (k + 1 < K && tid < 7 * kCPB) s_gx[(T + tid / kCPB) * kXR + tid % kCPB] = gshift;
@@ -757,10 +785,13 @@ struct BwdLocalParams {
 
 template <typename IOT, int S>
 __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
-    using Gm = BGeo<S>;
-    constexpr int NP = Gm::NP, T = Gm::T, TP = Gm::TP;
+    // tiles of 64 tokens (four per lane of a row), the next tile's inputs
+    // loaded into registers while the current one is walked
+    constexpr int NP = 16 * S, T = 64, TP = T / 16;
+    constexpr int XE = T * kCPB, XL = (XE + kThreads - 1) / kThreads;
+    constexpr int CE = T * NP, CL = (CE + kThreads - 1) / kThreads;
     __shared__ float s_dt[T * kXR], s_z[T * kXR], s_dy[T * kXR];
-    __shared__ float s_C[T * NP];
+    __shared__ float s_C[CE];
     const IOT *DT = static_cast<const IOT *>(p.dt);
     const IOT *Cp = static_cast<const IOT *>(p.Cm);
     const IOT *Z = static_cast<const IOT *>(p.z);
@@ -788,33 +819,79 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
         A2[s] = n < N ? neg_exp_f(p.A_log[dc * N + n]) * kLog2e : 0.0f;
         g[s] = 0.0f;
     }
-    const float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
+    // consumed before the first request, so the loop never waits for it
+    asm volatile("" : "+v"(dtb));
     float sdl = 0.0f;   // sum of dt over this lane's tokens
 
+    // Loads through buffer descriptors whose range ends at the chunk's end:
+    // unconditional, 32-bit per-thread offsets on a scalar base (tokens past
+    // the end read 0; channels past D and states past N read neighbouring
+    // values that only feed lanes whose results are not stored).
+    static_assert(kThreads % kCPB == 0 && kThreads % NP == 0, "offset strides");
+    const uint32_t es = sizeof(IOT);
+    const uint32_t xoff = (uint32_t)((tid / kCPB) * (int)D + tid % kCPB) * es;   // q = 0
+    const uint32_t xstep = (uint32_t)((kThreads / kCPB) * (int)D) * es;
+    const uint32_t coff = (uint32_t)((tid / NP) * (int)N + tid % NP) * es;
+    const uint32_t cstep = (uint32_t)((kThreads / NP) * (int)N) * es;
+    typedef typename RawOf<IOT>::type raw_t;   // raw io bits, converted when staged
+    raw_t rdt[XL], rdy[XL], rz[XL], rC[CL];
+    auto fetch = [&](int k) {
+        const int64_t ts = t0 + (int64_t)k * T;
+        const uint64_t xr = (uint64_t)((Le - ts) * D - d0) * es;
+        const buf_t bDT = make_buf(DT + (b * L + ts) * D + d0, xr);
+        const buf_t bDY = make_buf(DY + (b * L + ts) * D + d0, xr);
+#pragma unroll
+        for (int q = 0; q < XL; ++q) {
+            rdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
+            rdy[q] = buf_ld_raw(bDY, xoff + q * xstep, DY);
+        }
+        if (gate) {
+            const buf_t bZ = make_buf(Z + (b * L + ts) * D + d0, xr);
+#pragma unroll
+            for (int q = 0; q < XL; ++q) rz[q] = buf_ld_raw(bZ, xoff + q * xstep, Z);
+        } else {
+#pragma unroll
+            for (int q = 0; q < XL; ++q) rz[q] = 0;
+        }
+        const buf_t bC = make_buf(Cp + (b * L + ts) * N, (uint64_t)((Le - ts) * N) * es);
+#pragma unroll
+        for (int q = 0; q < CL; ++q) rC[q] = buf_ld_raw(bC, coff + q * cstep, Cp);
+    };
+    auto stage = [&]() {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+#pragma unroll
+        for (int q = 0; q < XL; ++q) {
+            const int e = q * kThreads + tid;
+            if (e < XE) {
+                const int ep = (e / kCPB) * kXR + e % kCPB;
+                s_dt[ep] = raw_f32(rdt[q], DT);
+                s_dy[ep] = raw_f32(rdy[q], DY);
+                s_z[ep] = raw_f32(rz[q], Z);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < CL; ++q) {
+            const int e = q * kThreads + tid;
+            if (e < CE) s_C[e] = raw_f32(rC[q], Cp);
+        }
+    };
+
+    if (K > 0) fetch(K - 1);
     for (int k = K - 1; k >= 0; --k) {
         const int64_t ts = t0 + (int64_t)k * T;
         __syncthreads();
-        for (int e = tid; e < T * kCPB; e += kThreads) {
-            const int tt = e / kCPB, cc = e % kCPB;
-            const bool v = ts + tt < Le && d0 + cc < D;
-            const int64_t o = (b * L + ts + tt) * D + d0 + cc;
-            s_dt[tt * kXR + cc] = v ? to_f32(DT[o]) : 0.0f;
-            s_dy[tt * kXR + cc] = v ? to_f32(DY[o]) : 0.0f;
-            s_z[tt * kXR + cc] = (v && gate) ? to_f32(Z[o]) : 0.0f;
-        }
-        for (int e = tid; e < T * NP; e += kThreads) {
-            const int tt = e / NP, n = e % NP;
-            s_C[e] = (ts + tt < Le && n < N) ? to_f32(Cp[(b * L + ts + tt) * N + n]) : 0.0f;
-        }
+        stage();
         __syncthreads();
+        if (k > 0) fetch(k - 1);
         // per-token values of this lane's tokens; tokens past the chunk get
         // dt = dyv = 0, which leaves g unchanged
         float tk_dl[TP], tk_dyv[TP];
 #pragma unroll
         for (int jj = 0; jj < TP; ++jj) {
             const int tt = l + 16 * jj;
-            const bool v = tt < T && ts + tt < Le;
-            const int e = min(tt, T - 1) * kXR + cl;
+            const bool v = ts + tt < Le;
+            const int e = tt * kXR + cl;
             const float dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
             const float dyr = v ? s_dy[e] : 0.0f;
             tk_dl[jj] = dl;

@@ -76,13 +76,17 @@ constexpr int kRows = kTile / 16;   // tile rows per thread in the transform rol
 // kRows*rp .. kRows*rp + kRows-1 with rp = tid >> 4.  B and C: the [64][NP]
 // element tiles dealt over the block's threads in order, B first then C
 // (consecutive threads read consecutive elements).
-template <int NP>
+// The values are kept as raw io bits and converted where they are staged
+// or used (for bf16 a conversion right after the load would be a wait).
+template <typename IOT, int NP>
 struct RawTile {
     static constexpr int TE = kTile * NP;                 // elements per tensor tile
     static_assert(TE % kThreads == 0, "tile elements");
     static constexpr int BCS = 2 * TE / kThreads;
-    float x[kRows], dt[kRows], z[kRows];
-    float bc[BCS];
+    typedef typename RawOf<IOT>::type raw_t;
+    raw_t x[kRows], dt[kRows], z[kRows];
+    raw_t bc[BCS];
+    __device__ __forceinline__ static float f(raw_t v) { return raw_f32(v, (const IOT *)nullptr); }
 };
 
 // Per-thread byte offsets of the fetch inside a tile, the same for every
@@ -100,20 +104,20 @@ struct FetchOff {
 // Every load is unconditional, so the compiler never waits on one (or on
 // anything issued before it) until the data is staged.
 template <typename IOT, int NP, bool WANT_C>
-__device__ __forceinline__ void load_raw(RawTile<NP> &r, const FetchOff &fo, const IOT *X, const IOT *DT,
+__device__ __forceinline__ void load_raw(RawTile<IOT, NP> &r, const FetchOff &fo, const IOT *X, const IOT *DT,
                                          const IOT *Z, const IOT *Bp, const IOT *Cp, int64_t b, int64_t L,
                                          int64_t D, int64_t N, int64_t ts) {
-    constexpr int TE = RawTile<NP>::TE;
+    constexpr int TE = RawTile<IOT, NP>::TE;
     constexpr int per = TE / kThreads;                    // loads per tensor per thread
     const uint64_t es = sizeof(IOT);
     const int64_t left = L - ts;                          // tokens from ts to the end
     const buf_t rB = make_buf(Bp + (b * L + ts) * N, (uint64_t)(left * N) * es);
     const buf_t rC = make_buf(Cp + (b * L + ts) * N, (uint64_t)(left * N) * es);
 #pragma unroll
-    for (int i = 0; i < RawTile<NP>::BCS; ++i) {
+    for (int i = 0; i < RawTile<IOT, NP>::BCS; ++i) {
         const int tens = i / per;                         // 0: B, 1: C (compile time)
         const uint32_t off = fo.bc0 + (uint32_t)(i % per) * fo.bcstep;
-        r.bc[i] = (tens < (WANT_C ? 2 : 1)) ? buf_ld(tens == 0 ? rB : rC, off, Bp) : 0.0f;
+        r.bc[i] = (tens < (WANT_C ? 2 : 1)) ? buf_ld_raw(tens == 0 ? rB : rC, off, Bp) : 0;
     }
     const uint64_t tb = (uint64_t)(left * D) * es;
     const buf_t rX = make_buf(X + (b * L + ts) * D, tb);
@@ -121,16 +125,16 @@ __device__ __forceinline__ void load_raw(RawTile<NP> &r, const FetchOff &fo, con
 #pragma unroll
     for (int i = 0; i < kRows; ++i) {
         const uint32_t off = fo.x0 + (uint32_t)i * fo.xrow;
-        r.x[i] = buf_ld(rX, off, X);
-        r.dt[i] = buf_ld(rD, off, DT);
+        r.x[i] = buf_ld_raw(rX, off, X);
+        r.dt[i] = buf_ld_raw(rD, off, DT);
     }
     if (Z != nullptr) {
         const buf_t rZ = make_buf(Z + (b * L + ts) * D, tb);
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) r.z[i] = buf_ld(rZ, fo.x0 + (uint32_t)i * fo.xrow, Z);
+        for (int i = 0; i < kRows; ++i) r.z[i] = buf_ld_raw(rZ, fo.x0 + (uint32_t)i * fo.xrow, Z);
     } else {
 #pragma unroll
-        for (int i = 0; i < kRows; ++i) r.z[i] = 0.0f;
+        for (int i = 0; i < kRows; ++i) r.z[i] = 0;
     }
 }
 
@@ -139,16 +143,16 @@ __device__ __forceinline__ void load_raw(RawTile<NP> &r, const FetchOff &fo, con
 // state with one 16-byte access.  States past N are staged as zeros.
 constexpr int kTS = kTile + 4;
 
-template <int NP, bool WANT_C>
-__device__ __forceinline__ void store_bc(const RawTile<NP> &r, float *sB, float *sC, int tid, int64_t N) {
-    constexpr int TE = RawTile<NP>::TE;
+template <typename IOT, int NP, bool WANT_C>
+__device__ __forceinline__ void store_bc(const RawTile<IOT, NP> &r, float *sB, float *sC, int tid, int64_t N) {
+    constexpr int TE = RawTile<IOT, NP>::TE;
 #pragma unroll
-    for (int i = 0; i < RawTile<NP>::BCS; ++i) {
+    for (int i = 0; i < RawTile<IOT, NP>::BCS; ++i) {
         constexpr int per = TE / kThreads;
         const int tens = i / per;
         const int ec = (i % per) * kThreads + tid;
         const int row = ec / NP, n = ec % NP;
-        if (tens < (WANT_C ? 2 : 1)) (tens == 0 ? sB : sC)[n * kTS + row] = (n < N) ? r.bc[i] : 0.0f;
+        if (tens < (WANT_C ? 2 : 1)) (tens == 0 ? sB : sC)[n * kTS + row] = (n < N) ? r.f(r.bc[i]) : 0.0f;
     }
 }
 
@@ -283,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
         return 0.0f;
     };
 
-    RawTile<NP> raw;
+    RawTile<IOT, NP> raw;
     FetchOff fo;
     {
         const uint32_t es = sizeof(IOT);
@@ -309,15 +313,15 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) uu[i] = raw.x[i];
+            for (int i = 0; i < kRows; ++i) uu[i] = raw.f(raw.x[i]);
         }
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
             const int row = rp * kRows + i;
-            const float dl = softplus_f(raw.dt[i] + dtb);
+            const float dl = softplus_f(raw.f(raw.dt[i]) + dtb);
             s_dl[tc][row] = make_float2(dl, (DISC == DISC_DB) ? dl * uu[i] : uu[i]);
             if constexpr (FINAL)
-                s_gd[tc][row] = make_float2((Z != nullptr) ? silu_f(raw.z[i]) : 1.0f, Dd * uu[i]);
+                s_gd[tc][row] = make_float2((Z != nullptr) ? silu_f(raw.f(raw.z[i])) : 1.0f, Dd * uu[i]);
         }
         (void)nv;
     };
@@ -327,9 +331,9 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
         const int nv = (int)min((int64_t)T, t1 - ts);
         if constexpr (CONV) {
 #pragma unroll
-            for (int i = 0; i < kRows; ++i) s_x[(8 + rp * kRows + i) * kXS + tc] = raw.x[i];
+            for (int i = 0; i < kRows; ++i) s_x[(8 + rp * kRows + i) * kXS + tc] = raw.f(raw.x[i]);
         }
-        store_bc<NP, FINAL>(raw, s_B, s_C, tid, N);
+        store_bc<IOT, NP, FINAL>(raw, s_B, s_C, tid, N);
         __syncthreads();
         transform(nv);
         __syncthreads();

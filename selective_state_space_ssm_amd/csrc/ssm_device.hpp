@@ -127,6 +127,20 @@ __device__ __forceinline__ float buf_ld(buf_t r, uint32_t boff, const bf16_t *) 
     return __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, boff, 0, 0) << 16);
 }
 
+// Raw bits of one io value, converted only where the value is used:
+// converting right after the load would make the compiler wait for it
+// there, ahead of work the load was meant to overlap.
+template <typename IOT> struct RawOf { typedef uint32_t type; };
+template <> struct RawOf<bf16_t> { typedef uint16_t type; };
+__device__ __forceinline__ uint32_t buf_ld_raw(buf_t r, uint32_t boff, const float *) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, boff, 0, 0);
+}
+__device__ __forceinline__ uint16_t buf_ld_raw(buf_t r, uint32_t boff, const bf16_t *) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, boff, 0, 0);
+}
+__device__ __forceinline__ float raw_f32(uint32_t v, const float *) { return __uint_as_float(v); }
+__device__ __forceinline__ float raw_f32(uint16_t v, const bf16_t *) { return __uint_as_float((uint32_t)v << 16); }
+
 __device__ __forceinline__ void buf_st(buf_t r, uint32_t boff, float *, float v) {
     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, boff, 0, 0);
 }
