@@ -351,9 +351,21 @@ def bench_extras(torch, np, si, ssm, dev, args):
         ssm.ssm_step(h, i["x"], i["dt_raw"], prm["A_log"], i["B"], i["C"], conv_state=cs, z=i["z"],
                      conv_w=prm["conv_w"], conv_b=prm["conv_b"], dt_bias=prm["dt_bias"], Dskip=prm["Dskip"], y=ys)
 
+    # the same stacked step with the state stored in bf16 (an option of
+    # ssm_step: updated in float32, rounded when stored)
+    h16 = torch.zeros(nblk, S, D, N, device="cuda", dtype=torch.bfloat16)
+
+    def stacked_bf16_state(t):
+        i = toks[t]
+        ssm.ssm_step(h16, i["x"], i["dt_raw"], prm["A_log"], i["B"], i["C"], conv_state=cs, z=i["z"],
+                     conv_w=prm["conv_w"], conv_b=prm["conv_b"], dt_bias=prm["dt_bias"], Dskip=prm["Dskip"], y=ys)
+
     per_block_bytes = (2 * S * D * N * 4 + 2 * S * 3 * D * 4 + S * D * 4 * 4 + 2 * S * N * 4
                        + 4 * (D * N + 3 * D + 4 * D))
-    for name, fn in (("per_block_launches", per_block), ("stacked_one_launch", stacked)):
+    bytes16 = per_block_bytes - 2 * S * D * N * 2
+    for name, fn, nb in (("per_block_launches", per_block, per_block_bytes),
+                         ("stacked_one_launch", stacked, per_block_bytes),
+                         ("stacked_one_launch_bf16_state", stacked_bf16_state, bytes16)):
         for t in range(4):
             fn(t)
         torch.cuda.synchronize()
@@ -373,8 +385,9 @@ def bench_extras(torch, np, si, ssm, dev, args):
         ex["streaming_6blk_256streams_" + name] = {
             "tokens_per_s": S / (ms * 1e-3), "tokens_per_s_wall": S * steps / wall,
             "us_per_token_step": round(ms * 1e3, 2),
-            "algorithmic_GBps": round(nblk * per_block_bytes / (ms * 1e-3) / 1e9, 1),
-            "note": "state + history of the 6 blocks (179 MB) fit the 256 MB last-level cache"}
+            "algorithmic_GBps": round(nblk * nb / (ms * 1e-3) / 1e9, 1),
+            "note": "state + history of the 6 blocks (%d MB) fit the 256 MB last-level cache"
+                    % round(nblk * S * (D * N * (2 if nb == bytes16 else 4) + 3 * D * 4) / 1e6)}
         log("streaming %s: %.1f us per token step" % (name, ms * 1e3))
     return ex
 

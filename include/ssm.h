@@ -98,7 +98,8 @@ typedef struct ssm_step_desc {
     int32_t conv_width;  /* 0: x is u; 1..8: causal conv over the carried history + SiLU */
     int32_t io_dtype;    /* SSM_F32 or SSM_BF16 for x, dt_raw, B, C, z, y */
     int32_t disc;        /* SSM_DISC_DELTA_B or SSM_DISC_ZOH */
-    int32_t reserved;    /* must be 0 */
+    int32_t state_dtype; /* storage of h: SSM_F32 (0), or SSM_BF16 (updated in float32 and
+                            rounded to nearest, ties to even, when stored) */
 } ssm_step_desc;
 
 /* Descriptor of a causal depthwise convolution. */
@@ -230,8 +231,11 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
  *   u = SiLU(conv_b + sum_{j<W-1} conv_w[j] * hist[j] + conv_w[W-1] * x)   (conv_width > 0)
  *   hist <- [hist[1..W-2], x]
  *   then one recurrence step of the scan with u, updating h in place.
+ * y reads the updated state; with state_dtype SSM_BF16 what is kept for the
+ * next token is its bfloat16 rounding (the pages keep the state in float32;
+ * bf16 storage halves the state traffic that bounds a decode step).
  * Tensors (each with a leading [nblocks] axis, block-major):
- *   h          f32 [S, D, N]   state, in/out (required)
+ *   h          f32 or bf16 [S, D, N]   state (state_dtype), in/out (required)
  *   conv_state f32 [S, W-1, D] history, in/out (required when conv_width > 1)
  *   x, dt_raw  io  [S, D]      required
  *   B, C       io  [S, N]      required
@@ -241,7 +245,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
  *   A_log      f32 [D, N]      required
  *   y          io  [S, D]      output (required)
  */
-ssm_status ssm_step(const ssm_step_desc *desc, float *h, float *conv_state, const void *x,
+ssm_status ssm_step(const ssm_step_desc *desc, void *h, float *conv_state, const void *x,
                     const void *dt_raw, const void *B, const void *C, const void *z,
                     const float *conv_w, const float *conv_b, const float *dt_bias,
                     const float *A_log, const float *Dskip, void *y, void *stream);

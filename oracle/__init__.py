@@ -57,7 +57,9 @@ def _load():
         lib.orc_delta.argtypes = [i64, i64, i64, p, p, p]
         lib.orc_scan_fwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 12
         lib.orc_scan_bwd.argtypes = [i64, i64, i64, i64, i32] + [p] * 21
-        lib.orc_step.argtypes = [i64, i64, i64, i32, i32] + [p] * 13
+        lib.orc_step.argtypes = [i64, i64, i64, i32, i32] + [p] * 13 + [i32]
+        lib.orc_round_bf16_value.argtypes = [ctypes.c_double]
+        lib.orc_round_bf16_value.restype = ctypes.c_double
         for f in (lib.orc_conv1d_causal, lib.orc_conv1d_causal_bwd, lib.orc_scan_core, lib.orc_delta,
                   lib.orc_scan_fwd, lib.orc_scan_bwd, lib.orc_step):
             f.restype = ctypes.c_int
@@ -194,10 +196,19 @@ def scan_bwd(u, dt_raw, A_log, Bm, Cm, dy, dt_bias=None, Dskip=None, z=None,
     return out
 
 
+def round_bf16(x):
+    """orc_round_bf16_value: the nearest bfloat16 value of a float64, elementwise."""
+    f = _load().orc_round_bf16_value
+    a = np.asarray(x, dtype=np.float64)
+    return np.vectorize(f, otypes=[np.float64])(a) if a.size else a.copy()
+
+
 def step(h, conv_state, x, dt_raw, Bm, Cm, A_log, z=None, conv_w=None,
-         conv_b=None, dt_bias=None, Dskip=None, disc=DISC_DELTA_B):
+         conv_b=None, dt_bias=None, Dskip=None, disc=DISC_DELTA_B, state_bf16=False):
     """orc_step: one streaming token for S streams.  h [S,D,N] and conv_state
-    [S,W-1,D] are float64 numpy arrays updated in place; returns y [S,D]."""
+    [S,W-1,D] are float64 numpy arrays updated in place; returns y [S,D].
+    With state_bf16 the kept state is rounded to bfloat16 after the update
+    (y reads the unrounded update)."""
     assert isinstance(h, np.ndarray) and h.dtype == np.float64 and h.flags.c_contiguous
     if conv_state is not None:
         assert conv_state.dtype == np.float64 and conv_state.flags.c_contiguous
@@ -211,5 +222,5 @@ def step(h, conv_state, x, dt_raw, Bm, Cm, A_log, z=None, conv_w=None,
     _check(_load().orc_step(S, D, N, W, int(disc), _ptr(h), _ptr(conv_state),
                             _ptr(x), _ptr(dt_raw), _ptr(Bm), _ptr(Cm), _ptr(z),
                             _ptr(conv_w), _ptr(conv_b), _ptr(dt_bias),
-                            _ptr(A_log), _ptr(Dskip), _ptr(y)), "step")
+                            _ptr(A_log), _ptr(Dskip), _ptr(y), int(bool(state_bf16))), "step")
     return y

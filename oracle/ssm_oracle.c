@@ -523,12 +523,30 @@ int orc_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
  * With conv_w == NULL the input x is used as u directly and the history is
  * left alone.  h is [S, D, N], conv_state [S, W-1, D], x/dt_raw/z/y [S, D],
  * Bm/Cm [S, N]. */
+/* The bfloat16 value nearest to x (8 significant bits, ties to even), for
+ * finite x in bfloat16's normal range: frexp splits x = f * 2^e with
+ * 0.5 <= |f| < 1, so the 8 significant bits are the integer part of
+ * x * 2^(8-e), which nearbyint rounds to nearest, ties to even. */
+static double orc_round_bf16(double x)
+{
+    if (x == 0.0 || !isfinite(x))
+        return x;
+    int e;
+    frexp(x, &e);
+    return ldexp(nearbyint(ldexp(x, 8 - e)), e - 8);
+}
+
+double orc_round_bf16_value(double x) { return orc_round_bf16(x); }
+
+/* One streaming token.  With state_bf16 the carried state is stored in
+ * bfloat16: y reads the updated state itself, and what is kept for the next
+ * token is its bfloat16 rounding. */
 int orc_step(int64_t S, int64_t D, int64_t N, int32_t W, int32_t disc,
              double *h, double *conv_state, const double *x,
              const double *dt_raw, const double *Bm, const double *Cm,
              const double *z, const double *conv_w, const double *conv_b,
              const double *dt_bias, const double *A_log, const double *Dskip,
-             double *y)
+             double *y, int32_t state_bf16)
 {
     if (S < 0 || D < 0 || N < 1 || !h || !x || !dt_raw || !Bm || !Cm ||
         !A_log || !y || (disc != ORC_DISC_DELTA_B && disc != ORC_DISC_ZOH))
@@ -560,8 +578,9 @@ int orc_step(int64_t S, int64_t D, int64_t N, int32_t W, int32_t disc,
             double An = -exp(A_log[d * N + n]);
             double a = exp(dt * An);
             double *hn = &h[(s * D + d) * N + n];
-            *hn = a * *hn + orc_write_coef(disc, dt, An) * Bm[s * N + n] * ut;
-            yv += Cm[s * N + n] * *hn;
+            double hnew = a * *hn + orc_write_coef(disc, dt, An) * Bm[s * N + n] * ut;
+            yv += Cm[s * N + n] * hnew;
+            *hn = state_bf16 ? orc_round_bf16(hnew) : hnew;
         }
         if (Dskip)
             yv += Dskip[d] * ut;

@@ -54,7 +54,7 @@ class ssm_scan_desc(ctypes.Structure):
 class ssm_step_desc(ctypes.Structure):
     _fields_ = [("nblocks", ctypes.c_int64), ("nstreams", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("conv_width", ctypes.c_int32),
-                ("io_dtype", ctypes.c_int32), ("disc", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("io_dtype", ctypes.c_int32), ("disc", ctypes.c_int32), ("state_dtype", ctypes.c_int32)]
 
 
 class ssm_conv_desc(ctypes.Structure):
@@ -253,17 +253,20 @@ def ssm_scan_bwd(x, dt_raw, A_log, B, C, dy, dt_bias=None, Dskip=None, z=None, c
 
 def ssm_step(h, x, dt_raw, A_log, B, C, conv_state=None, z=None, conv_w=None, conv_b=None, dt_bias=None,
              Dskip=None, y=None, disc=SSM_DISC_DELTA_B, stream=None):
-    """One streaming token.  h [nblk, S, D, N] and conv_state [nblk, S, W-1, D]
-    (float32) are updated in place; x/dt_raw/z [nblk, S, D], B/C [nblk, S, N],
-    per-block parameters with a leading [nblk] axis.  Returns y [nblk, S, D]."""
+    """One streaming token.  h [nblk, S, D, N] (float32, or bfloat16 for a
+    bf16-stored state) and conv_state [nblk, S, W-1, D] (float32) are updated
+    in place; x/dt_raw/z [nblk, S, D], B/C [nblk, S, N], per-block parameters
+    with a leading [nblk] axis.  Returns y [nblk, S, D]."""
     K, S, D, N = h.shape
     W = conv_w.shape[-1] if conv_w is not None else 0
     t = x.dtype
-    desc = ssm_step_desc(K, S, D, N, W, _io_code(x), disc, 0)
+    if h.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("h must be float32 or bfloat16, got %s" % h.dtype)
+    desc = ssm_step_desc(K, S, D, N, W, _io_code(x), disc, _io_code(h))
     if y is None:
         y = torch.empty_like(x)
     _check("ssm_step", lib().ssm_step(
-        ctypes.byref(desc), _f32(h, "h"), _f32(conv_state, "conv_state"), _ptr(x, t, "x"),
+        ctypes.byref(desc), _ptr(h, h.dtype, "h"), _f32(conv_state, "conv_state"), _ptr(x, t, "x"),
         _ptr(dt_raw, t, "dt_raw"), _ptr(B, t, "B"), _ptr(C, t, "C"), _ptr(z, t, "z"), _f32(conv_w, "conv_w"),
         _f32(conv_b, "conv_b"), _f32(dt_bias, "dt_bias"), _f32(A_log, "A_log"), _f32(Dskip, "Dskip"),
         _ptr(y, t, "y"), _stream(stream)))

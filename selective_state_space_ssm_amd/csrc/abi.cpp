@@ -279,11 +279,12 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
     return hip_status(ssm::launch_scan_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
-ssm_status ssm_step(const ssm_step_desc *desc, float *h, float *conv_state, const void *x, const void *dt_raw,
+ssm_status ssm_step(const ssm_step_desc *desc, void *h, float *conv_state, const void *x, const void *dt_raw,
                     const void *B, const void *C, const void *z, const float *conv_w, const float *conv_b,
                     const float *dt_bias, const float *A_log, const float *Dskip, void *y, void *stream) {
     if (!desc) return SSM_ERR_NULL_ARG;
-    if (!valid_io(desc->io_dtype) || !valid_disc(desc->disc) || desc->reserved != 0) return SSM_ERR_UNSUPPORTED;
+    if (!valid_io(desc->io_dtype) || !valid_disc(desc->disc) || !valid_io(desc->state_dtype))
+        return SSM_ERR_UNSUPPORTED;
     if (desc->nblocks < 1 || desc->nstreams < 1 || desc->dim < 1 || desc->dstate < 1 ||
         desc->dstate > SSM_MAX_DSTATE || desc->conv_width < 0 || desc->conv_width > SSM_MAX_CONV_WIDTH)
         return SSM_ERR_BAD_SHAPE;
@@ -312,10 +313,11 @@ ssm_status ssm_step(const ssm_step_desc *desc, float *h, float *conv_state, cons
               {dt_bias, dt_bias ? K * D * 4 : 0},
               {A_log, K * D * N * 4},
               {Dskip, Dskip ? K * D * 4 : 0}};
-    ac.outs = {{h, nh * 4}, {conv_state, W > 1 ? nst * 4 : 0}, {y, nsd * es}};
+    ac.outs = {{h, nh * io_size(desc->state_dtype)}, {conv_state, W > 1 ? nst * 4 : 0}, {y, nsd * es}};
     if (!ac.ok()) return SSM_ERR_ALIAS;
     ssm::StepArgs a{};
     a.nblk = K; a.S = S; a.D = D; a.N = N; a.W = W; a.bf16 = desc->io_dtype == SSM_BF16; a.disc = desc->disc;
+    a.state_bf16 = desc->state_dtype == SSM_BF16;
     a.h = h; a.conv_state = W > 1 ? conv_state : nullptr;
     a.x = x; a.dt = dt_raw; a.Bm = B; a.Cm = C; a.z = z;
     a.conv_w = W > 0 ? conv_w : nullptr; a.conv_b = W > 0 ? conv_b : nullptr;

@@ -85,7 +85,9 @@ struct StepArgs {
     int W;
     int bf16;
     int disc;
-    float *h, *conv_state;
+    int state_bf16;          // h stored as bf16 (computed in float32)
+    void *h;
+    float *conv_state;
     const void *x, *dt, *Bm, *Cm, *z;
     const float *conv_w, *conv_b, *dt_bias, *A_log, *Dskip;
     void *y;

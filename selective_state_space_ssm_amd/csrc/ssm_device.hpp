@@ -21,16 +21,13 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ float to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
 __device__ __forceinline__ void store_io(float *p, float v) { *p = v; }
-// float -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ void store_io(bf16_t *p, float v) {
+// float -> bf16 bits, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t bf16_rne(float v) {
     uint32_t b = __float_as_uint(v);
-    uint16_t r;
-    if ((b & 0x7fffffffu) > 0x7f800000u)
-        r = (uint16_t)((b >> 16) | 0x40u);
-    else
-        r = (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
-    *p = r;
+    if ((b & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((b >> 16) | 0x40u);
+    return (uint16_t)((b + 0x7fffu + ((b >> 16) & 1u)) >> 16);
 }
+__device__ __forceinline__ void store_io(bf16_t *p, float v) { *p = bf16_rne(v); }
 
 // Load K consecutive io values into floats.  `vec` says the address is
 // aligned to the full vector (K*sizeof(T) bytes, capped at 16).
@@ -106,6 +103,25 @@ __device__ __forceinline__ void store_k(float *p, const float (&v)[K], int valid
 #pragma unroll
     for (int i = 0; i < K; ++i)
         if (i < valid) p[i] = v[i];
+}
+
+// K values rounded to bf16; 8-byte stores of four when `vec` (aligned) and all valid.
+template <int K>
+__device__ __forceinline__ void store_k(bf16_t *p, const float (&v)[K], int valid, bool vec) {
+    if constexpr (K % 4 == 0) {
+        if (valid >= K && vec) {
+#pragma unroll
+            for (int i = 0; i < K; i += 4) {
+                const uint32_t lo = (uint32_t)bf16_rne(v[i]) | ((uint32_t)bf16_rne(v[i + 1]) << 16);
+                const uint32_t hi = (uint32_t)bf16_rne(v[i + 2]) | ((uint32_t)bf16_rne(v[i + 3]) << 16);
+                *reinterpret_cast<uint2 *>(p + i) = make_uint2(lo, hi);
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i)
+        if (i < valid) p[i] = bf16_rne(v[i]);
 }
 
 // ------------------------------------------------------------ buffer access

@@ -16,6 +16,10 @@
 // compute identical values; lane 0 of the channel stores y and the history.
 // Every load of a lane is issued before any arithmetic.
 //
+// The state may be stored in bf16 (HT = bf16_t): it is loaded, updated and
+// read out in float32 and rounded to bf16 (nearest, ties to even) only when
+// stored, which halves the traffic that bounds the step.
+//
 // Arithmetic follows the sequence kernel operation by operation: the same
 // conv tap order, softplus, decay 2^(dt*A*log2 e) with A = -exp(A_log), and
 // the same readout tree -- chains over the sequence kernel's states per
@@ -35,7 +39,7 @@ enum { DISC_DB = 0, DISC_ZOH = 1 };
 
 // LPC lanes per channel, 4 states per lane; VL = states per lane of the
 // sequence kernel (its readout chains); MAXW = widest conv carried.
-template <typename IOT, int LPC, int VL, int DISC, bool CONV, int MAXW>
+template <typename IOT, typename HT, int LPC, int VL, int DISC, bool CONV, int MAXW>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     const IOT *X = static_cast<const IOT *>(a.x);
     const IOT *DT = static_cast<const IOT *>(a.dt);
@@ -62,7 +66,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 
     // ---- loads
     float hq[kSPL], Bq[kSPL], Cq[kSPL], al[kSPL];
-    float *hp = a.h + sd * N + n0;
+    HT *hp = static_cast<HT *>(a.h) + sd * N + n0;
     const int64_t bc = (k * S + s) * N + n0;     // [nblk, S, N]
     load_k_guard<kSPL>(hp, hq, nvalid, vecN);
     load_k_guard<kSPL>(Bp + bc, Bq, nvalid, vecN);
@@ -149,14 +153,14 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
 }
 
-template <typename IOT, int LPC, int VL>
+template <typename IOT, typename HT, int LPC, int VL>
 hipError_t launch_g(const StepArgs &a, hipStream_t s) {
     const int64_t threads = a.nblk * a.S * a.D * LPC;
     const unsigned blocks = (unsigned)((threads + 255) / 256);
     const bool conv = a.W > 0;
 #define SSM_STEP_CASE(DI, CV, MW)                                                                        \
     if (a.disc == DI && conv == CV && (!CV || a.W <= MW)) {                                              \
-        hipLaunchKernelGGL((step_kernel<IOT, LPC, VL, DI, CV, MW>), dim3(blocks), dim3(256), 0, s, a); \
+        hipLaunchKernelGGL((step_kernel<IOT, HT, LPC, VL, DI, CV, MW>), dim3(blocks), dim3(256), 0, s, a); \
         return hipGetLastError();                                                                        \
     }
     SSM_STEP_CASE(DISC_DB, false, 1)
@@ -169,20 +173,24 @@ hipError_t launch_g(const StepArgs &a, hipStream_t s) {
     return hipErrorInvalidValue;
 }
 
-template <typename IOT>
+template <typename IOT, typename HT>
 hipError_t launch_io(const StepArgs &a, hipStream_t s) {
     // four states per lane; readout chains = the sequence kernel's states per lane
-    if (a.N <= 16) return launch_g<IOT, 4, 1>(a, s);
-    if (a.N <= 32) return launch_g<IOT, 8, 2>(a, s);
-    return launch_g<IOT, 16, 4>(a, s);
+    if (a.N <= 16) return launch_g<IOT, HT, 4, 1>(a, s);
+    if (a.N <= 32) return launch_g<IOT, HT, 8, 2>(a, s);
+    return launch_g<IOT, HT, 16, 4>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     if (a.nblk * a.S * a.D == 0) return hipSuccess;
-    if (a.bf16) return launch_io<bf16_t>(a, s);
-    return launch_io<float>(a, s);
+    if (a.state_bf16) {
+        if (a.bf16) return launch_io<bf16_t, bf16_t>(a, s);
+        return launch_io<float, bf16_t>(a, s);
+    }
+    if (a.bf16) return launch_io<bf16_t, float>(a, s);
+    return launch_io<float, float>(a, s);
 }
 
 }  // namespace ssm

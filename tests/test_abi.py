@@ -177,7 +177,7 @@ def test_step_validation(ssm):
     L = ssm.lib()
     good = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, 0, 0)
     ptrs = [_addr(i) for i in range(13)]
-    bad = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, 0, 1)
+    bad = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, 0, 2)   # no such state dtype
     assert L.ssm_step(ctypes.byref(bad), *ptrs, None) == ssm.SSM_ERR_UNSUPPORTED
     bad = ssm.ssm_step_desc(0, 8, 32, 16, 4, 0, 0, 0)
     assert L.ssm_step(ctypes.byref(bad), *ptrs, None) == ssm.SSM_ERR_BAD_SHAPE

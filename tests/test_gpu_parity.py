@@ -269,14 +269,16 @@ def test_long_sequence_bf16_chunked(ssm):
 
 # --------------------------------------------------------------------------- step
 
-def _step_oracle_loop(p, steps, disc=DB, gate=True):
+def _step_oracle_loop(p, steps, disc=DB, gate=True, state_bf16=False):
     h = p["h0"].astype(np.float64).copy()
+    if state_bf16:
+        h = oracle.round_bf16(h)
     cs = p["conv_state"].astype(np.float64).copy()
     ys = []
     for t in range(steps):
         ys.append(oracle.step(h, cs, p["x"][:, t], p["dt_raw"][:, t], p["B"][:, t], p["C"][:, t], p["A_log"],
                               z=p["z"][:, t] if gate else None, conv_w=p["conv_w"], conv_b=p["conv_b"],
-                              dt_bias=p["dt_bias"], Dskip=p["Dskip"], disc=disc))
+                              dt_bias=p["dt_bias"], Dskip=p["Dskip"], disc=disc, state_bf16=state_bf16))
     return np.stack(ys, 1), h, cs
 
 
@@ -382,6 +384,52 @@ def test_step_bf16(ssm):
         assert y.dtype == bf
         assert rel_linf(y, y_ref[:, t]) <= BF16_TOL
     assert rel_linf(h[0], h_ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("S,D,N,W,io", [(4, 40, 16, 4, torch.float32), (2, 16, 33, 2, torch.float32),
+                                        (3, 24, 64, 4, torch.float32), (4, 32, 16, 4, torch.bfloat16)])
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_step_bf16_state(ssm, S, D, N, W, io, disc):
+    """Streaming with the state stored in bf16 (updated in float32, rounded
+    when stored) against the oracle's step with the same storage rule, over
+    48 tokens."""
+    steps = 48
+    p = _rand(17, S, steps, D, N, W, bf16=io == torch.bfloat16)
+    y_ref, h_ref, cs_ref = _step_oracle_loop(p, steps, disc=disc, state_bf16=True)
+    h = dev(p["h0"], torch.bfloat16)[None].contiguous()
+    cs = dev(p["conv_state"])[None].contiguous() if W > 1 else None
+    ys = []
+    for t in range(steps):
+        ys.append(ssm.ssm_step(h, dev(p["x"][:, t], io)[None], dev(p["dt_raw"][:, t], io)[None],
+                               dev(p["A_log"])[None], dev(p["B"][:, t], io)[None], dev(p["C"][:, t], io)[None],
+                               conv_state=cs, z=dev(p["z"][:, t], io)[None], conv_w=dev(p["conv_w"])[None],
+                               conv_b=dev(p["conv_b"])[None], dt_bias=dev(p["dt_bias"])[None],
+                               Dskip=dev(p["Dskip"])[None], disc=disc)[0])
+    torch.cuda.synchronize()
+    assert h.dtype == torch.bfloat16
+    assert rel_linf(torch.stack(ys, 1), y_ref) <= BF16_TOL
+    assert rel_linf(h[0], h_ref) <= BF16_TOL
+    if cs is not None:
+        np.testing.assert_array_equal(host(cs[0]), cs_ref)
+
+
+def test_step_bf16_state_first_step_exact_rounding(ssm):
+    """One step from a bf16 state: the stored state is the bf16 rounding of
+    the float32 update, which the float32-state kernel computes (same
+    arithmetic), element for element."""
+    p = _rand(18, 4, 1, 48, 16, 4)
+    h32 = dev(oracle.round_bf16(p["h0"]).astype(np.float32))[None].contiguous()
+    h16 = h32.to(torch.bfloat16)
+    args = lambda: (dev(p["x"][:, 0])[None], dev(p["dt_raw"][:, 0])[None], dev(p["A_log"])[None],
+                    dev(p["B"][:, 0])[None], dev(p["C"][:, 0])[None])
+    kw = lambda: dict(conv_state=dev(p["conv_state"])[None].contiguous(), z=dev(p["z"][:, 0])[None],
+                      conv_w=dev(p["conv_w"])[None], conv_b=dev(p["conv_b"])[None],
+                      dt_bias=dev(p["dt_bias"])[None], Dskip=dev(p["Dskip"])[None])
+    y32 = ssm.ssm_step(h32, *args(), **kw())
+    y16 = ssm.ssm_step(h16, *args(), **kw())
+    torch.cuda.synchronize()
+    assert torch.equal(y16, y32)
+    assert torch.equal(h16, h32.to(torch.bfloat16))
 
 
 def test_streaming_decode_six_blocks(ssm):

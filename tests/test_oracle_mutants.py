@@ -42,6 +42,8 @@ MUTANTS = {
     "bwd_adjoint_not_decayed": ("                            g[n] *= a;\n", ""),
     "conv_bwd_silu_derivative": ("g *= sg * (1.0 + acc * (1.0 - sg));", "g *= sg;"),
     "conv_bwd_taps_reversed": ("int64_t t = i + (W - 1) - k;", "int64_t t = i + k;"),
+    "step_bf16_state_read_rounded": ("yv += Cm[s * N + n] * hnew;",
+                                     "yv += Cm[s * N + n] * (state_bf16 ? orc_round_bf16(hnew) : hnew);"),
 }
 
 

@@ -504,3 +504,38 @@ def test_conv_backward_against_torch_autograd(oracle_lib, silu, W):
     np.testing.assert_allclose(g["db"], tb.grad.numpy(), rtol=1e-12, atol=1e-13)
     if W > 1:
         np.testing.assert_allclose(g["dstate"], ts.grad.numpy(), rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------- bf16 streaming state
+
+def test_round_bf16_matches_torch():
+    """The oracle's bfloat16 rounding (nearest, ties to even) against torch's
+    float32 -> bfloat16 conversion, including exact ties."""
+    r = np.random.default_rng(5)
+    x = r.standard_normal(20000).astype(np.float32) * np.float32(3.0)
+    bits = x.view(np.uint32)
+    ties = ((bits & np.uint32(0xFFFF0000)) | np.uint32(0x8000)).view(np.float32)   # exactly halfway
+    for v in (x, ties):
+        got = oracle.round_bf16(v.astype(np.float64))
+        want = torch.from_numpy(v).to(torch.bfloat16).double().numpy()
+        np.testing.assert_array_equal(got, want)
+
+
+def test_step_bf16_state_rounds_after_the_readout():
+    """A step with a bf16-stored state: y is the float64 step's y (it reads the
+    updated state), and the kept state is the bf16 rounding of the float64
+    step's state."""
+    p = si.mamba_block(1, 1, 24, 16, 4, workload=si.WL_STREAM, seed=3)
+    r = np.random.default_rng(6)
+    h0 = oracle.round_bf16(r.standard_normal((2, 24, 16)))
+    cs0 = r.standard_normal((2, 3, 24))
+    x, dt, z = (r.standard_normal((2, 24)) for _ in range(3))
+    B, C = (r.standard_normal((2, 16)) for _ in range(2))
+    kw = dict(z=z, conv_w=p["conv_w"], conv_b=p["conv_b"], dt_bias=p["dt_bias"], Dskip=p["Dskip"])
+    h64, c64 = h0.copy(), cs0.copy()
+    y64 = oracle.step(h64, c64, x, dt, B, C, p["A_log"], **kw)
+    hb, cb = h0.copy(), cs0.copy()
+    yb = oracle.step(hb, cb, x, dt, B, C, p["A_log"], state_bf16=True, **kw)
+    np.testing.assert_array_equal(yb, y64)
+    np.testing.assert_array_equal(hb, oracle.round_bf16(h64))
+    np.testing.assert_array_equal(cb, c64)
