@@ -24,6 +24,9 @@ _LIB = os.environ.get("SSM_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 DISC_DELTA_B = 0
 DISC_ZOH = 1
+# Constant decay source: a = exp(-exp(A_log)) per (channel, state), write B*u,
+# no step size (dt_raw and dt_bias are not read and may be None).
+DECAY_CONST = 2
 
 _lib = None
 
@@ -154,7 +157,8 @@ def scan_core(u, delta_, A_log, Bm, Cm, Dskip=None, z=None, h0=None,
 
 def scan_fwd(u, dt_raw, A_log, Bm, Cm, dt_bias=None, Dskip=None, z=None,
              h0=None, disc=DISC_DELTA_B):
-    """orc_scan_fwd: dt = softplus(dt_raw + dt_bias), then the scan.
+    """orc_scan_fwd: dt = softplus(dt_raw + dt_bias), then the scan (with
+    disc=DECAY_CONST there is no dt and dt_raw may be None).
     Returns (y [B,L,D], hT [B,D,N])."""
     u, dt_raw, A_log = _f64(u), _f64(dt_raw), _f64(A_log)
     Bm, Cm, dt_bias, Dskip = _f64(Bm), _f64(Cm), _f64(dt_bias), _f64(Dskip)
@@ -174,7 +178,8 @@ def scan_bwd(u, dt_raw, A_log, Bm, Cm, dy, dt_bias=None, Dskip=None, z=None,
              h0=None, dhT=None, disc=DISC_DELTA_B):
     """orc_scan_bwd: gradients of scan_fwd's y (and hT) w.r.t. its inputs.
     Returns a dict with du, d_dt_raw, d_delta, d_dt_bias, dA_log, dB, dC,
-    dD, dz (None without z) and dh0."""
+    dD, dz (None without z) and dh0 (the dt gradients are zeros with
+    disc=DECAY_CONST, where dt_raw may be None)."""
     u, dt_raw, A_log = _f64(u), _f64(dt_raw), _f64(A_log)
     Bm, Cm, dy = _f64(Bm), _f64(Cm), _f64(dy)
     dt_bias, Dskip, z, h0, dhT = _f64(dt_bias), _f64(Dskip), _f64(z), _f64(h0), _f64(dhT)

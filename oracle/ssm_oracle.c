@@ -48,6 +48,18 @@
 
 #define ORC_DISC_DELTA_B 0
 #define ORC_DISC_ZOH 1
+/* Constant decay source ("the s6 cell", section "one cell, two
+ * architectures"): the same diagonal cell h <- a*h + b*u, but with the decay
+ * a fixed per (channel, state) instead of computed from the input at every
+ * token.  Here a = exp(A) with A = -exp(A_log), so a = 2^(negative) as the
+ * page requires, the write is b*u = B[t,n]*u_t, and there is no step size:
+ * dt_raw and dt_bias are not read. */
+#define ORC_DECAY_CONST 2
+
+static int orc_valid_form(int32_t disc)
+{
+    return disc == ORC_DISC_DELTA_B || disc == ORC_DISC_ZOH || disc == ORC_DECAY_CONST;
+}
 
 /* softplus(r) = log(1 + e^r), evaluated without overflow.
  * ("mamba, live": dt = softplus(dt_proj(.)) > 0.) */
@@ -225,9 +237,21 @@ int orc_conv1d_causal_bwd(int64_t B, int64_t L, int64_t D, int32_t W,
  * The write is then coef * B[n] * u. */
 static double orc_write_coef(int32_t disc, double delta, double A)
 {
+    if (disc == ORC_DECAY_CONST)
+        return 1.0;
     if (disc == ORC_DISC_ZOH)
         return expm1(delta * A) / A;
     return delta;
+}
+
+/* Decay of one state coordinate over one token: exp(dt*A) when it is
+ * computed from the input ("the s6 cell", section "the recurrence"), the
+ * per-(channel, state) constant exp(A) for the constant source. */
+static double orc_decay(int32_t disc, double delta, double A)
+{
+    if (disc == ORC_DECAY_CONST)
+        return exp(A);
+    return exp(delta * A);
 }
 
 /* The selective scan given dt (already softplus'ed).  For every (b, d):
@@ -236,6 +260,8 @@ static double orc_write_coef(int32_t disc, double delta, double A)
  *   for t: a = exp(dt_t * A[n]);  h[n] = a*h[n] + coef(dt_t, A[n]) * B[t,n] * u_t
  *          yv = sum_n C[t,n] * h[n] + Dskip * u_t      (C reads the updated state)
  *          y  = yv * SiLU(z_t)  if z is given, else yv
+ * With the constant decay source (ORC_DECAY_CONST) a = exp(A[n]) and the
+ * write is B[t,n] * u_t; delta is not read and may be NULL.
  * Optional traces record a, the write and h for every (b, t, d, n). */
 int orc_scan_core(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                   const double *u, const double *delta, const double *A_log,
@@ -243,10 +269,9 @@ int orc_scan_core(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                   const double *z, const double *h0, double *hT, double *y,
                   double *trace_a, double *trace_w, double *trace_h)
 {
-    if (B < 0 || L < 0 || D < 0 || N < 1 || !A_log ||
-        (disc != ORC_DISC_DELTA_B && disc != ORC_DISC_ZOH))
+    if (B < 0 || L < 0 || D < 0 || N < 1 || !A_log || !orc_valid_form(disc))
         return -1;
-    if (L > 0 && (!u || !delta || !Bm || !Cm || !y))
+    if (L > 0 && (!u || (!delta && disc != ORC_DECAY_CONST) || !Bm || !Cm || !y))
         return -1;
     int64_t rows = B * D;
     int failed = 0;
@@ -269,10 +294,10 @@ int orc_scan_core(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                 }
                 for (int64_t t = 0; t < L; ++t) {
                     int64_t i = (b * L + t) * D + d;
-                    double dt = delta[i], ut = u[i];
+                    double dt = disc == ORC_DECAY_CONST ? 0.0 : delta[i], ut = u[i];
                     double yv = 0.0;
                     for (int64_t n = 0; n < N; ++n) {
-                        double a = exp(dt * A[n]);
+                        double a = orc_decay(disc, dt, A[n]);
                         double wr = orc_write_coef(disc, dt, A[n]) * Bm[(b * L + t) * N + n] * ut;
                         h[n] = a * h[n] + wr;
                         yv += Cm[(b * L + t) * N + n] * h[n];
@@ -308,13 +333,18 @@ int orc_delta(int64_t B, int64_t L, int64_t D, const double *dt_raw,
     return 0;
 }
 
-/* Full forward: dt from dt_raw, then the scan.  delta_out may be NULL. */
+/* Full forward: dt from dt_raw, then the scan.  delta_out may be NULL.
+ * The constant decay source has no dt: dt_raw is not read (may be NULL) and
+ * delta_out, if given, is left untouched. */
 int orc_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                  const double *u, const double *dt_raw, const double *dt_bias,
                  const double *A_log, const double *Bm, const double *Cm,
                  const double *Dskip, const double *z, const double *h0,
                  double *hT, double *y, double *delta_out)
 {
+    if (disc == ORC_DECAY_CONST)
+        return orc_scan_core(B, L, D, N, disc, u, NULL, A_log, Bm, Cm, Dskip, z,
+                             h0, hT, y, NULL, NULL, NULL);
     int64_t total = B * L * D;
     double *delta = delta_out;
     if (!delta && total > 0) {
@@ -343,6 +373,9 @@ int orc_scan_fwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
  *     ZOH form (c = expm1(dt*A)/A):
  *                 ddt += da*a*A + g*a*B*u;  du += g*c*B;  dB += g*c*u;
  *                 dA += da*a*dt + g*B*u*(dt*a*A - expm1(dt*A))/A^2
+ *     constant decay source (a = exp(A), write B*u, no dt):
+ *                 du += g*B;  dB += g*u;  dA += da*a;  no dt gradient (d_dt_raw,
+ *                 d_delta and d_dt_bias are written as zeros)
  *     g = a*g
  *   end:    dh0 = g;  dA_log = dA*A  (A = -exp(A_log));
  *           d_dt_raw = ddt * sigmoid(dt_raw + dt_bias);  d_dt_bias = sum_{b,t} d_dt_raw
@@ -360,10 +393,9 @@ int orc_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                  double *dA_log, double *dB, double *dC, double *dDskip,
                  double *dz, double *dh0)
 {
-    if (B < 0 || L < 0 || D < 1 || N < 1 || !A_log ||
-        (disc != ORC_DISC_DELTA_B && disc != ORC_DISC_ZOH))
+    if (B < 0 || L < 0 || D < 1 || N < 1 || !A_log || !orc_valid_form(disc))
         return -1;
-    if (L > 0 && (!u || !dt_raw || !Bm || !Cm || !dy))
+    if (L > 0 && (!u || (!dt_raw && disc != ORC_DECAY_CONST) || !Bm || !Cm || !dy))
         return -1;
     int64_t G = D < ORC_BWD_GROUPS ? D : ORC_BWD_GROUPS;
     size_t bln = (size_t)(B * L * N);
@@ -412,11 +444,13 @@ int orc_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                     /* forward, recording a, h and the pre-gate output */
                     for (int64_t t = 0; t < L; ++t) {
                         int64_t i = (b * L + t) * D + d;
-                        double dt = orc_softplus(dt_raw[i] + (dt_bias ? dt_bias[d] : 0.0));
+                        double dt = disc == ORC_DECAY_CONST
+                                        ? 0.0
+                                        : orc_softplus(dt_raw[i] + (dt_bias ? dt_bias[d] : 0.0));
                         double acc = 0.0;
                         dl[t] = dt;
                         for (int64_t n = 0; n < N; ++n) {
-                            double a = exp(dt * A[n]);
+                            double a = orc_decay(disc, dt, A[n]);
                             g[n] = a * g[n] + orc_write_coef(disc, dt, A[n]) *
                                                   Bm[(b * L + t) * N + n] * u[i];
                             ha[t * N + n] = a;
@@ -456,6 +490,10 @@ int orc_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                                 dut += g[n] * c * Bv;
                                 gB[t * N + n] += g[n] * c * ut;
                                 dA[n] += da * a * dt + g[n] * Bv * ut * (dt * a * An - em1) / (An * An);
+                            } else if (disc == ORC_DECAY_CONST) {
+                                dut += g[n] * Bv;
+                                gB[t * N + n] += g[n] * ut;
+                                dA[n] += da * a;
                             } else {
                                 ddt += da * a * An + g[n] * Bv * ut;
                                 dut += g[n] * dt * Bv;
@@ -464,7 +502,9 @@ int orc_scan_bwd(int64_t B, int64_t L, int64_t D, int64_t N, int32_t disc,
                             }
                             g[n] *= a;
                         }
-                        double sg = orc_sigmoid(dt_raw[i] + (dt_bias ? dt_bias[d] : 0.0));
+                        double sg = disc == ORC_DECAY_CONST
+                                        ? 0.0
+                                        : orc_sigmoid(dt_raw[i] + (dt_bias ? dt_bias[d] : 0.0));
                         if (du) du[i] = dut;
                         if (d_delta) d_delta[i] = ddt;
                         if (d_dt_raw) d_dt_raw[i] = ddt * sg;
@@ -548,8 +588,8 @@ int orc_step(int64_t S, int64_t D, int64_t N, int32_t W, int32_t disc,
              const double *dt_bias, const double *A_log, const double *Dskip,
              double *y, int32_t state_bf16)
 {
-    if (S < 0 || D < 0 || N < 1 || !h || !x || !dt_raw || !Bm || !Cm ||
-        !A_log || !y || (disc != ORC_DISC_DELTA_B && disc != ORC_DISC_ZOH))
+    if (S < 0 || D < 0 || N < 1 || !h || !x || (!dt_raw && disc != ORC_DECAY_CONST) ||
+        !Bm || !Cm || !A_log || !y || !orc_valid_form(disc))
         return -1;
     if (conv_w && (W < 1 || (W > 1 && !conv_state)))
         return -1;
@@ -572,11 +612,13 @@ int orc_step(int64_t S, int64_t D, int64_t N, int32_t W, int32_t disc,
         } else {
             ut = xt;
         }
-        double dt = orc_softplus(dt_raw[s * D + d] + (dt_bias ? dt_bias[d] : 0.0));
+        double dt = disc == ORC_DECAY_CONST
+                        ? 0.0
+                        : orc_softplus(dt_raw[s * D + d] + (dt_bias ? dt_bias[d] : 0.0));
         double yv = 0.0;
         for (int64_t n = 0; n < N; ++n) {
             double An = -exp(A_log[d * N + n]);
-            double a = exp(dt * An);
+            double a = orc_decay(disc, dt, An);
             double *hn = &h[(s * D + d) * N + n];
             double hnew = a * *hn + orc_write_coef(disc, dt, An) * Bm[s * N + n] * ut;
             yv += Cm[s * N + n] * hnew;

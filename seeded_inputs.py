@@ -11,7 +11,10 @@ same shapes stand in for them):
   dt_raw                            0.1 * standard normal
   dt_bias[d]                        inverse softplus of delta0[d], with
                                     delta0 log-uniform in [1e-3, 1e-1]
-  A_log[d, n]                       log(n + 1)   (perturbed variant: + 0.1*normal)
+  A_log[d, n]                       log(n + 1)   (perturbed variant: + 0.1*normal;
+                                    constant-decay variant: + log(delta0[d]), so a
+                                    decay fixed per channel, exp(-exp(A_log)), is
+                                    the one the input-driven cell has at delta0)
   Dskip[d]                          1            (perturbed variant: normal)
   conv_w [D, W], conv_b [D]         standard normal
 Every tensor has its own numpy Generator seeded with
@@ -74,9 +77,10 @@ def tiny_block(seed=0):
 
 
 def mamba_block(Bn, L, D, N, W=4, workload=WL_BLOCK, seed=0, bf16=False,
-                perturbed=False, with_dy=False, with_state=False):
+                perturbed=False, with_dy=False, with_state=False, const_decay=False):
     """Mamba-mini-shaped block inputs with the recipe in the module docstring.
-    Returns float32 numpy arrays (bf16-representable when bf16=True)."""
+    Returns float32 numpy arrays (bf16-representable when bf16=True).
+    const_decay: A_log for a decay fixed per channel (see the docstring)."""
     def g(t, shape, scale=1.0):
         v = rng(seed, workload, t).standard_normal(shape, dtype=np.float32)
         if scale != 1.0:
@@ -88,6 +92,8 @@ def mamba_block(Bn, L, D, N, W=4, workload=WL_BLOCK, seed=0, bf16=False,
     if perturbed:
         A_log = A_log + 0.1 * rng(seed, workload, "A_log").standard_normal((D, N))
         Dskip = rng(seed, workload, "Dskip").standard_normal(D)
+    if const_decay:
+        A_log = A_log + np.log(delta0)[:, None]
     out = dict(
         x=g("x", (Bn, L, D)), dt_raw=g("dt_raw", (Bn, L, D), 0.1),
         B=g("B", (Bn, L, N)), C=g("C", (Bn, L, N)), z=g("z", (Bn, L, D)),

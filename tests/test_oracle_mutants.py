@@ -17,8 +17,15 @@ SRC = os.path.join(ROOT, "oracle", "ssm_oracle.c")
 MUTANTS = {
     "softplus_sign": ("log1p(exp(-fabs(r)))", "log1p(exp(fabs(r)))"),
     "zoh_coef_sign": ("return expm1(delta * A) / A;", "return expm1(delta * A) / (-A);"),
-    "decay_sign": ("double a = exp(dt * A[n]);\n                        double wr",
-                   "double a = exp(-dt * A[n]);\n                        double wr"),
+    "decay_sign": ("    return exp(delta * A);\n}", "    return exp(-delta * A);\n}"),
+    # constant decay source
+    "const_decay_base2": ("        return exp(A);\n", "        return exp2(A);\n"),
+    "const_write_scaled_by_dt": ("    if (disc == ORC_DECAY_CONST)\n        return 1.0;",
+                                 "    if (disc == ORC_DECAY_CONST)\n        return delta;"),
+    "const_write_uses_zoh": ("    if (disc == ORC_DECAY_CONST)\n        return 1.0;",
+                             "    if (disc == ORC_DECAY_CONST)\n        return expm1(A) / A;"),
+    "const_bwd_dA_missing_decay": ("dA[n] += da * a;\n", "dA[n] += da;\n"),
+    "const_bwd_du_uses_output_weight": ("dut += g[n] * Bv;\n", "dut += g[n] * Cm[(b * L + t) * N + n];\n"),
     "A_not_exponentiated": ("A[n] = -exp(A_log[d * N + n]);\n                    h[n] = h0",
                             "A[n] = -(A_log[d * N + n]);\n                    h[n] = h0"),
     "readout_before_update": ("yv += Cm[(b * L + t) * N + n] * h[n];",

@@ -539,3 +539,185 @@ def test_step_bf16_state_rounds_after_the_readout():
     np.testing.assert_array_equal(yb, y64)
     np.testing.assert_array_equal(hb, oracle.round_bf16(h64))
     np.testing.assert_array_equal(cb, c64)
+
+
+# --------------------------------------------------------------------------- constant decay source
+# "the s6 cell", section "one cell, two architectures": the same diagonal cell
+# h <- a*h + b*u with the decay a constant per (channel, state) (the RWKV side)
+# instead of computed from the input at every token.  The oracle's constant
+# source takes a = exp(-exp(A_log)) and the write B_t*u_t, with no step size.
+
+def _const_fwd(p, **kw):
+    return oracle.scan_fwd(p["x"], None, p["A_log"], p["B"], p["C"], Dskip=p.get("Dskip"),
+                           z=p.get("z"), h0=p.get("h0"), disc=oracle.DECAY_CONST, **kw)
+
+
+def test_const_decay_single_state_is_lfilter(oracle_lib):
+    """State width 1 with a constant decay: h is the first-order IIR filter
+    h_t = a h_{t-1} + B_t u_t with a = exp(-exp(A_log)) (scipy.signal.lfilter),
+    and y = (C_t h_t + D u_t) * SiLU(z_t)."""
+    r = np.random.default_rng(21)
+    L, D = 80, 3
+    u, z = r.standard_normal((1, L, D)), r.standard_normal((1, L, D))
+    Bm, Cm = r.standard_normal((1, L, 1)), r.standard_normal((1, L, 1))
+    A_log, Dsk = r.uniform(-2.0, 1.0, (D, 1)), r.standard_normal(D)
+    y, hT = oracle.scan_fwd(u, None, A_log, Bm, Cm, Dskip=Dsk, z=z, disc=oracle.DECAY_CONST)
+    for d in range(D):
+        a = np.exp(-np.exp(A_log[d, 0]))
+        h = scipy.signal.lfilter([1.0], [1.0, -a], Bm[0, :, 0] * u[0, :, d])
+        ref = (Cm[0, :, 0] * h + Dsk[d] * u[0, :, d]) * z[0, :, d] * scipy.special.expit(z[0, :, d])
+        np.testing.assert_allclose(y[0, :, d], ref, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(hT[0, d, 0], h[-1], rtol=1e-12, atol=1e-14)
+
+
+def test_const_decay_time_invariant_is_a_convolution(oracle_lib):
+    """Constant decay and constant B, C: impulse response K_k = sum_n C_n a_n^k B_n,
+    y = K * u + D u (np.convolve)."""
+    r = np.random.default_rng(22)
+    L, D, N = 50, 2, 6
+    u = r.standard_normal((1, L, D))
+    A_log = r.uniform(-3, 1.0, (D, N))
+    b, c = r.standard_normal(N), r.standard_normal(N)
+    Dsk = r.standard_normal(D)
+    y, _ = oracle.scan_fwd(u, None, A_log, np.tile(b, (1, L, 1)), np.tile(c, (1, L, 1)), Dskip=Dsk,
+                           disc=oracle.DECAY_CONST)
+    for d in range(D):
+        a = np.exp(-np.exp(A_log[d]))
+        K = np.array([np.sum(c * a ** k * b) for k in range(L)])
+        ref = np.convolve(u[0, :, d], K)[:L] + Dsk[d] * u[0, :, d]
+        np.testing.assert_allclose(y[0, :, d], ref, rtol=1e-11, atol=1e-12)
+
+
+def test_const_decay_closed_form(oracle_lib):
+    """h_t = a^(t+1) h0 + sum_{s<=t} a^(t-s) B_s u_s: the recurrent state equals
+    an O(L^2) sum of powers of the constant decay (np.power), at every t."""
+    p = _rand_block(Bn=2, L=12, D=3, N=4)
+    Bn, L, D = p["x"].shape
+    a = np.exp(-np.exp(p["A_log"]))                  # [D, N]
+    w = p["B"][:, :, None, :] * p["x"][..., None]    # [B, L, D, N]
+    y, hT = _const_fwd(dict(p, z=None))
+    for t in range(L):
+        ref = np.power(a, t + 1)[None] * p["h0"]
+        for s in range(t + 1):
+            ref = ref + np.power(a, t - s)[None] * w[:, s]
+        yref = np.einsum("bn,bdn->bd", p["C"][:, t], ref) + p["Dskip"] * p["x"][:, t]
+        np.testing.assert_allclose(y[:, t], yref, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(hT, ref, rtol=1e-12, atol=1e-14)
+
+
+def test_const_decay_reads_no_step_size(oracle_lib):
+    """With the constant source dt_raw and dt_bias are not read: any values give
+    the result of passing none, bit for bit (forward, backward and step)."""
+    p = _rand_block(Bn=2, L=9, D=3, N=4)
+    y0, h0 = _const_fwd(p)
+    y1, h1 = oracle.scan_fwd(p["x"], p["dt_raw"], p["A_log"], p["B"], p["C"], dt_bias=p["dt_bias"],
+                             Dskip=p["Dskip"], z=p["z"], h0=p["h0"], disc=oracle.DECAY_CONST)
+    np.testing.assert_array_equal(y0, y1)
+    np.testing.assert_array_equal(h0, h1)
+    kw = dict(Dskip=p["Dskip"], z=p["z"], h0=p["h0"], dhT=p["dhT"], disc=oracle.DECAY_CONST)
+    g0 = oracle.scan_bwd(p["x"], None, p["A_log"], p["B"], p["C"], p["dy"], **kw)
+    g1 = oracle.scan_bwd(p["x"], p["dt_raw"], p["A_log"], p["B"], p["C"], p["dy"],
+                         dt_bias=p["dt_bias"], **kw)
+    for k in g0:
+        if g0[k] is not None:
+            np.testing.assert_array_equal(g0[k], g1[k], err_msg=k)
+    for k in ("d_dt_raw", "d_delta", "d_dt_bias"):
+        assert not np.any(g0[k]), k
+    ha, hb = p["h0"].copy(), p["h0"].copy()
+    ya = oracle.step(ha, None, p["x"][:, 0], None, p["B"][:, 0], p["C"][:, 0], p["A_log"],
+                     Dskip=p["Dskip"], disc=oracle.DECAY_CONST)
+    yb = oracle.step(hb, None, p["x"][:, 0], p["dt_raw"][:, 0], p["B"][:, 0], p["C"][:, 0], p["A_log"],
+                     dt_bias=p["dt_bias"], Dskip=p["Dskip"], disc=oracle.DECAY_CONST)
+    np.testing.assert_array_equal(ya, yb)
+    np.testing.assert_array_equal(ha, hb)
+
+
+def test_const_decay_is_the_live_cell_at_unit_step(oracle_lib):
+    """One cell, two parameterisations: the constant source is the dt*B cell
+    with dt fixed at 1 (a = exp(1*A), write 1*B*u), bit for bit."""
+    p = _rand_block(Bn=2, L=10, D=3, N=5)
+    yc, hc = _const_fwd(p)
+    yl, hl = oracle.scan_core(p["x"], np.ones_like(p["x"]), p["A_log"], p["B"], p["C"], Dskip=p["Dskip"],
+                              z=p["z"], h0=p["h0"], disc=oracle.DISC_DELTA_B)
+    np.testing.assert_array_equal(yc, yl)
+    np.testing.assert_array_equal(hc, hl)
+
+
+def test_const_decay_streaming_equals_full_forward(oracle_lib):
+    """Token-by-token steps with the constant source (and the conv prologue)
+    reproduce the full forward bit for bit."""
+    p = _rand_block(Bn=2, L=10, D=6, N=3, W=4)
+    u, cs = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"], p["conv_state"])
+    y, hT = oracle.scan_fwd(u, None, p["A_log"], p["B"], p["C"], Dskip=p["Dskip"], z=p["z"],
+                            h0=p["h0"], disc=oracle.DECAY_CONST)
+    h, conv = p["h0"].copy(), p["conv_state"].copy()
+    for t in range(p["x"].shape[1]):
+        yt = oracle.step(h, conv, p["x"][:, t], None, p["B"][:, t], p["C"][:, t], p["A_log"],
+                         z=p["z"][:, t], conv_w=p["conv_w"], conv_b=p["conv_b"], Dskip=p["Dskip"],
+                         disc=oracle.DECAY_CONST)
+        np.testing.assert_array_equal(yt, y[:, t])
+    np.testing.assert_array_equal(h, hT)
+    np.testing.assert_array_equal(conv, cs)
+
+
+_CONST_GRAD_OF = dict(x="du", A_log="dA_log", B="dB", C="dC", Dskip="dD", z="dz", h0="dh0")
+
+
+def _const_loss(p):
+    y, hT = _const_fwd(p)
+    return np.sum(y * p["dy"]) + np.sum(hT * p["dhT"])
+
+
+def test_const_decay_backward_against_finite_differences(oracle_lib):
+    """Every gradient of the constant-source backward matches central finite
+    differences of its forward (float64, step 1e-6)."""
+    p = _rand_block(Bn=2, L=7, D=3, N=4)
+    g = oracle.scan_bwd(p["x"], None, p["A_log"], p["B"], p["C"], p["dy"], Dskip=p["Dskip"], z=p["z"],
+                        h0=p["h0"], dhT=p["dhT"], disc=oracle.DECAY_CONST)
+    eps = 1e-6
+    for name, gname in _CONST_GRAD_OF.items():
+        fd = np.zeros_like(p[name])
+        for idx in np.ndindex(p[name].shape):
+            q = {k: v.copy() for k, v in p.items()}
+            q[name][idx] += eps
+            lp = _const_loss(q)
+            q[name][idx] -= 2 * eps
+            lm = _const_loss(q)
+            fd[idx] = (lp - lm) / (2 * eps)
+        scale = max(np.max(np.abs(fd)), 1e-3)
+        err = np.max(np.abs(g[gname] - fd)) / scale
+        assert err < 2e-7, (name, err)
+        assert np.any(g[gname] != 0), name
+
+
+def test_const_decay_backward_against_torch_autograd(oracle_lib):
+    """The constant-source backward against float64 autograd of an
+    independently written torch loop."""
+    p = _rand_block(Bn=2, L=11, D=4, N=3)
+    names = ["x", "A_log", "B", "C", "Dskip", "z", "h0"]
+    ts = {k: torch.tensor(p[k], dtype=torch.float64, requires_grad=True) for k in names}
+    a = torch.exp(-torch.exp(ts["A_log"]))
+    h = ts["h0"]
+    ys = []
+    for t in range(p["x"].shape[1]):
+        h = a * h + ts["B"][:, t, None, :] * ts["x"][:, t, :, None]
+        yv = (h * ts["C"][:, t, None, :]).sum(-1) + ts["Dskip"] * ts["x"][:, t]
+        ys.append(yv * torch.nn.functional.silu(ts["z"][:, t]))
+    loss = (torch.stack(ys, 1) * torch.from_numpy(p["dy"])).sum() + (h * torch.from_numpy(p["dhT"])).sum()
+    loss.backward()
+    g = oracle.scan_bwd(p["x"], None, p["A_log"], p["B"], p["C"], p["dy"], Dskip=p["Dskip"], z=p["z"],
+                        h0=p["h0"], dhT=p["dhT"], disc=oracle.DECAY_CONST)
+    for k in names:
+        np.testing.assert_allclose(g[_CONST_GRAD_OF[k]], ts[k].grad.numpy(), rtol=1e-10, atol=1e-12,
+                                   err_msg=k)
+
+
+def test_const_decay_recipe(oracle_lib):
+    """The constant-decay workload's decays lie in (0, 1) and equal the decays
+    the input-driven cell has at its bias step delta0 (float32 A_log)."""
+    p = si.mamba_block(1, 4, 64, 16, const_decay=True)
+    q = si.mamba_block(1, 4, 64, 16)
+    a = np.exp(-np.exp(p["A_log"].astype(np.float64)))
+    assert a.min() > 0 and a.max() < 1
+    d0 = oracle.delta(np.zeros((1, 1, 64)), q["dt_bias"])[0, 0]
+    np.testing.assert_allclose(a, np.exp(-d0[:, None] * np.exp(q["A_log"].astype(np.float64))), rtol=1e-5)
