@@ -55,10 +55,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def fwd_bytes(B, L, D, N, W, es, gate=True, conv=True):
-    per_tok = B * L * D * es * (3 + (1 if gate else 0))      # x, dt_raw, y (+ z)
+def fwd_bytes(B, L, D, N, W, es, gate=True, conv=True, dt=True):
+    """x, dt_raw (not with a constant decay), y (+ z) once each; B, C; parameters."""
+    per_tok = B * L * D * es * ((3 if dt else 2) + (1 if gate else 0))
     bc = 2 * B * L * N * es
-    params = 4 * (D + D * N + D + (D * W + D if conv else 0))
+    params = 4 * ((D if dt else 0) + D * N + D + (D * W + D if conv else 0))
     return per_tok + bc + params
 
 
@@ -277,6 +278,29 @@ def bench_extras(torch, np, si, ssm, dev, args):
                              "note": "working set fits the 256 MB last-level cache"}
     del Q, y2
     torch.cuda.empty_cache()
+
+    # the constant decay source (decay fixed per channel and state, no step
+    # size): the headline shape with state width 16, and width 1
+    for Nc in (16, 1):
+        c = si.mamba_block(B, L, D, Nc, 4, workload=si.WL_FWDBWD, const_decay=True)
+        Cc = {k: dev(c[k]) for k in ("x", "A_log", "B", "C", "z", "Dskip", "conv_w", "conv_b")}
+        del c
+        yc = torch.empty(B, L, D, device="cuda")
+        fc = lambda: ssm.ssm_scan_fwd(Cc["x"], None, Cc["A_log"], Cc["B"], Cc["C"], Dskip=Cc["Dskip"], z=Cc["z"],
+                                      conv_w=Cc["conv_w"], conv_b=Cc["conv_b"], y=yc, disc=ssm.SSM_DECAY_CONST)
+        for _ in range(3):
+            fc()
+        tm = EventTimer(torch)
+        for _ in range(reps):
+            tm.run(fc)
+        ms = tm.mean_ms()
+        nb = fwd_bytes(B, L, D, Nc, 4, 4, dt=False)
+        ex["forward_const_decay_B8_L2048_N%d" % Nc] = {
+            "us_per_call": round(ms * 1e3, 2), "elements_per_s": B * L * D * Nc / (ms * 1e-3),
+            "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1), "algorithmic_bytes": nb}
+        log("constant-decay forward, N=%d: %.1f us" % (Nc, ms * 1e3))
+        del Cc, yc
+        torch.cuda.empty_cache()
 
     # long sequence, bf16, two-level scan
     L4 = 65536

@@ -15,6 +15,15 @@
  *   y      = (sum_n C[t, n] * h[n] + Dskip * u) * SiLU(z)   (C reads the
  *            updated state; the gate only when z is given)
  *
+ * The same diagonal cell h <- a*h + b*u with the decay fixed per channel
+ * instead of computed per token ("the s6 cell", section "one cell, two
+ * architectures"; the fixed-decay side) is selected with
+ * disc = SSM_DECAY_CONST:
+ *   h[n]  <- exp(A[n]) * h[n] + B[t, n] * u,   A = -exp(A_log)
+ * with no step size: dt_raw and dt_bias are not read (they may be NULL) and
+ * the backward produces no d_dt_raw / d_dt_bias (those outputs are not
+ * written).  State width is dstate (1 for a scalar state per channel).
+ *
  * Conventions shared by every call
  *  - Layouts are row-major and channel-last:
  *      x, u, dt_raw, z, y and their gradients       [B, L, D]
@@ -72,6 +81,8 @@ typedef int32_t ssm_status;
 
 #define SSM_DISC_DELTA_B 0     /* write = dt * B * u ("mamba, live"; "the s6 cell") */
 #define SSM_DISC_ZOH 1         /* write = expm1(dt*A)/A * B * u (TensorViz explorer) */
+#define SSM_DECAY_CONST 2      /* decay exp(A) fixed per (channel, state), write = B * u,
+                                  no step size ("the s6 cell", "one cell, two architectures") */
 
 #define SSM_MAX_DSTATE 64
 #define SSM_MAX_CONV_WIDTH 8
@@ -84,7 +95,7 @@ typedef struct ssm_scan_desc {
     int64_t dstate;      /* N in [1, SSM_MAX_DSTATE] */
     int32_t conv_width;  /* 0: x already is the scan input u; 1..8: fused causal conv + SiLU */
     int32_t io_dtype;    /* SSM_F32 or SSM_BF16 */
-    int32_t disc;        /* SSM_DISC_DELTA_B or SSM_DISC_ZOH */
+    int32_t disc;        /* SSM_DISC_DELTA_B, SSM_DISC_ZOH or SSM_DECAY_CONST */
     int32_t chunk_len;   /* 0: library's choice; > 0: split time into chunks of this
                             length (two-level scan); -1: never split time */
 } ssm_scan_desc;
@@ -97,7 +108,7 @@ typedef struct ssm_step_desc {
     int64_t dstate;      /* N in [1, SSM_MAX_DSTATE] */
     int32_t conv_width;  /* 0: x is u; 1..8: causal conv over the carried history + SiLU */
     int32_t io_dtype;    /* SSM_F32 or SSM_BF16 for x, dt_raw, B, C, z, y */
-    int32_t disc;        /* SSM_DISC_DELTA_B or SSM_DISC_ZOH */
+    int32_t disc;        /* SSM_DISC_DELTA_B, SSM_DISC_ZOH or SSM_DECAY_CONST */
     int32_t state_dtype; /* storage of h: SSM_F32 (0), or SSM_BF16 (updated in float32 and
                             rounded to nearest, ties to even, when stored) */
 } ssm_step_desc;
@@ -150,7 +161,7 @@ ssm_status ssm_scan_fwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes)
  * and then re-scanned from their exact starting states; the result equals the
  * sequential recurrence up to rounding.
  *   x              io  [B, L, D]   u, or the conv input when conv_width > 0 (required)
- *   dt_raw         io  [B, L, D]   required
+ *   dt_raw         io  [B, L, D]   required (not read with SSM_DECAY_CONST)
  *   dt_bias        f32 [D]         optional
  *   A_log          f32 [D, N]      required
  *   B, C           io  [B, L, N]   required
@@ -197,6 +208,8 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes)
  *                                    needs z)
  *   dB, dC             io [B, L, N]  optional outputs (summed over channels)
  *   d_dt_bias, dDskip  f32 [D]       optional outputs (summed over batch and time)
+ *                                    (d_dt_raw and d_dt_bias are not written with
+ *                                    SSM_DECAY_CONST, which has no step size)
  *   dA_log             f32 [D, N]    optional output (summed over batch and time)
  *   dh0                f32 [B, D, N] optional output
  *   dconv_w   f32 [D, W]      optional output (summed over batch and time)
@@ -237,7 +250,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
  * Tensors (each with a leading [nblocks] axis, block-major):
  *   h          f32 or bf16 [S, D, N]   state (state_dtype), in/out (required)
  *   conv_state f32 [S, W-1, D] history, in/out (required when conv_width > 1)
- *   x, dt_raw  io  [S, D]      required
+ *   x, dt_raw  io  [S, D]      required (dt_raw not read with SSM_DECAY_CONST)
  *   B, C       io  [S, N]      required
  *   z          io  [S, D]      optional gate input
  *   conv_w     f32 [D, W]      required when conv_width > 0

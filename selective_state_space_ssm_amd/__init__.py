@@ -32,6 +32,7 @@ SSM_F32 = 0
 SSM_BF16 = 1
 SSM_DISC_DELTA_B = 0
 SSM_DISC_ZOH = 1
+SSM_DECAY_CONST = 2   # decay fixed per (channel, state); no step size, dt_raw may be None
 
 EXPORTED_SYMBOLS = (
     "ssm_version", "ssm_status_string", "conv1d_causal", "ssm_scan_fwd_workspace_size",
@@ -216,7 +217,7 @@ def ssm_scan_bwd(x, dt_raw, A_log, B, C, dy, dt_bias=None, Dskip=None, z=None, c
     x is u, or the conv input when conv_w is given (then dx flows through
     the conv + SiLU prologue).  Returns a dict of the requested gradients
     (allocated unless given in `out`); the conv ones only with conv_w, dz only
-    with z."""
+    with z, the dt ones not with SSM_DECAY_CONST."""
     Bn, L, D = x.shape
     N = A_log.shape[1]
     W = conv_w.shape[1] if conv_w is not None else 0
@@ -232,6 +233,8 @@ def ssm_scan_bwd(x, dt_raw, A_log, B, C, dy, dt_bias=None, Dskip=None, z=None, c
         if k == "dz" and z is None:
             continue
         if k.startswith("dconv") and W == 0:
+            continue
+        if k in ("d_dt_raw", "d_dt_bias") and disc == SSM_DECAY_CONST:
             continue
         if k not in out:
             shp, dt_ = shapes[k]

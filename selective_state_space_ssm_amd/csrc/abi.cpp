@@ -72,7 +72,8 @@ struct AliasCheck {
 ssm_status hip_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_HIP; }
 
 bool valid_io(int32_t io) { return io == SSM_F32 || io == SSM_BF16; }
-bool valid_disc(int32_t d) { return d == SSM_DISC_DELTA_B || d == SSM_DISC_ZOH; }
+bool valid_disc(int32_t d) { return d == SSM_DISC_DELTA_B || d == SSM_DISC_ZOH || d == SSM_DECAY_CONST; }
+bool has_step_size(int32_t d) { return d != SSM_DECAY_CONST; }
 
 ssm_status check_scan_desc(const ssm_scan_desc *d) {
     if (!d) return SSM_ERR_NULL_ARG;
@@ -159,7 +160,10 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
     if (st != SSM_OK) return st;
     const int64_t Bn = desc->batch, L = desc->seqlen, D = desc->dim, N = desc->dstate;
     const int W = desc->conv_width;
-    if (!A_log || (L > 0 && (!x || !dt_raw || !B || !C || !y)) || (W > 0 && !conv_w)) return SSM_ERR_NULL_ARG;
+    const bool live = has_step_size(desc->disc);
+    if (!live) dt_raw = nullptr, dt_bias = nullptr;   // not read
+    if (!A_log || (L > 0 && (!x || (live && !dt_raw) || !B || !C || !y)) || (W > 0 && !conv_w))
+        return SSM_ERR_NULL_ARG;
     for (const void *p : {(const void *)x, (const void *)dt_raw, (const void *)dt_bias, (const void *)A_log,
                           (const void *)B, (const void *)C, (const void *)Dskip, (const void *)z,
                           (const void *)conv_w, (const void *)conv_b, (const void *)conv_state_in,
@@ -173,7 +177,7 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
     const int64_t nbld = Bn * L * D, nbln = Bn * L * N, nbdn = Bn * D * N, nst = Bn * (W > 0 ? W - 1 : 0) * D;
     AliasCheck ac;
     ac.ins = {{x, nbld * es},
-              {dt_raw, nbld * es},
+              {dt_raw, dt_raw ? nbld * es : 0},
               {dt_bias, dt_bias ? D * 4 : 0},
               {A_log, D * N * 4},
               {B, nbln * es},
@@ -220,7 +224,10 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
     if (st != SSM_OK) return st;
     const int64_t Bn = desc->batch, L = desc->seqlen, D = desc->dim, N = desc->dstate;
     const int W = desc->conv_width;
-    if (!A_log || (L > 0 && (!x || !dt_raw || !B || !C || !dy)) || (W > 0 && !conv_w)) return SSM_ERR_NULL_ARG;
+    const bool live = has_step_size(desc->disc);
+    if (!live) dt_raw = nullptr, dt_bias = nullptr, d_dt_raw = nullptr, d_dt_bias = nullptr;   // no step size
+    if (!A_log || (L > 0 && (!x || (live && !dt_raw) || !B || !C || !dy)) || (W > 0 && !conv_w))
+        return SSM_ERR_NULL_ARG;
     if (dz && !z) return SSM_ERR_NULL_ARG;
     if (W == 0 && (dconv_w || dconv_b || dconv_state_in)) return SSM_ERR_BAD_SHAPE;
     for (const void *p : {(const void *)x, (const void *)dt_raw, (const void *)dt_bias, (const void *)A_log,
@@ -239,7 +246,7 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
     const int64_t nbld = Bn * L * D, nbln = Bn * L * N, nbdn = Bn * D * N, nst = Bn * (W > 0 ? W - 1 : 0) * D;
     AliasCheck ac;
     ac.ins = {{x, nbld * es},
-              {dt_raw, nbld * es},
+              {dt_raw, dt_raw ? nbld * es : 0},
               {dt_bias, dt_bias ? D * 4 : 0},
               {A_log, D * N * 4},
               {B, nbln * es},
@@ -294,7 +301,10 @@ ssm_status ssm_step(const ssm_step_desc *desc, void *h, float *conv_state, const
     if (!elems({K, S, D, N}, &nh) || !elems({K, S, D}, &nsd) || !elems({K, S, N}, &nsn) ||
         !elems({K, S, (int64_t)(W > 0 ? W - 1 : 0), D}, &nst))
         return SSM_ERR_BAD_SHAPE;
-    if (!h || !x || !dt_raw || !B || !C || !A_log || !y || (W > 0 && !conv_w) || (W > 1 && !conv_state))
+    const bool live = has_step_size(desc->disc);
+    if (!live) dt_raw = nullptr, dt_bias = nullptr;   // not read
+    if (!h || !x || (live && !dt_raw) || !B || !C || !A_log || !y || (W > 0 && !conv_w) ||
+        (W > 1 && !conv_state))
         return SSM_ERR_NULL_ARG;
     for (const void *p : {(const void *)h, (const void *)conv_state, (const void *)x, (const void *)dt_raw,
                           (const void *)B, (const void *)C, (const void *)z, (const void *)conv_w,
@@ -304,7 +314,7 @@ ssm_status ssm_step(const ssm_step_desc *desc, void *h, float *conv_state, const
     const int64_t es = io_size(desc->io_dtype);
     AliasCheck ac;
     ac.ins = {{x, nsd * es},
-              {dt_raw, nsd * es},
+              {dt_raw, dt_raw ? nsd * es : 0},
               {B, nsn * es},
               {C, nsn * es},
               {z, z ? nsd * es : 0},

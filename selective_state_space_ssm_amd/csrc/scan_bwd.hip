@@ -9,6 +9,13 @@
 //   dt*B:   ddt += da*a*A + g*B*u,  du += g*dt*B,  dB += g*dt*u,  dA += da*a*dt
 //   ZOH:    c = expm1(dt*A)/A;  ddt += da*a*A + g*a*B*u,  du += g*c*B,  dB += g*c*u,
 //           dA += da*a*dt + g*B*u*(dt*a*A - expm1(dt*A))/A^2
+//   const:  (decay fixed per channel and state, a = e^A, write B*u, no dt:
+//           "the s6 cell", section "one cell, two architectures")
+//           du += g*B,  dB += g*u,  dA += da*a;  run as the dt*B form with dt = 1,
+//           dt_raw never loaded and no dt gradient.  Like the forward, the
+//           state and the adjoint are updated in complement form,
+//           h + ((a-1) h + w) and g + (a-1) g with a-1 = expm1(A), which keeps
+//           decays close to 1 accurate
 //   gate:   dyv = dy*z*s,  dz = dy*yv*s*(1 + z*(1-s)),  s = sigmoid(z)
 //   dA_log = A * dA,  d_dt_raw = ddt * sigmoid(dt_raw + dt_bias)
 //   conv:   u = SiLU(xc),  xc_t = cb + sum_k w_k x_{t-(W-1)+k}  ("mamba, live", the
@@ -54,7 +61,7 @@ namespace {
 constexpr int kCPB = 48;                 // channels per workgroup
 constexpr int kWaves = kCPB / 4;         // four channels (rows) per wavefront
 constexpr int kThreads = kWaves * 64;
-enum { DISC_DB = 0, DISC_ZOH = 1 };
+enum { DISC_DB = 0, DISC_ZOH = 1, DISC_CONST = 2 };
 
 // S states per lane (16 lanes per channel), T tokens per tile.
 template <int S>
@@ -178,7 +185,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     const bool gate = Z != nullptr;
 
     // this lane's states n = l + 16 s
-    float A2[S], An[S], Ainv[S];
+    float A2[S], An[S], Ainv[S], am1[DISC == DISC_CONST ? S : 1];
     bool sv[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) {
@@ -188,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         A2[s] = sv[s] ? A * kLog2e : 0.0f;
         An[s] = A;
         Ainv[s] = 1.0f / A;
+        if constexpr (DISC == DISC_CONST) am1[s] = expm1f(A);   // a - 1
     }
     float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
     float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
@@ -238,9 +246,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             for (int q = 0; q < XUL; ++q) ru[q] = buf_ld_raw(bU, xoff + q * xstep, U);
         }
         const uint64_t xr = (uint64_t)(rows * D - d0) * es;
-        const buf_t bDT = make_buf(DT + (b * L + ts) * D + d0, xr);
+        if constexpr (DISC != DISC_CONST) {
+            const buf_t bDT = make_buf(DT + (b * L + ts) * D + d0, xr);
 #pragma unroll
-        for (int q = 0; q < XL; ++q) rdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
+            for (int q = 0; q < XL; ++q) rdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
+        }
         if (bwd) {
             const buf_t bDY = make_buf(DY + (b * L + ts) * D + d0, xr);
 #pragma unroll
@@ -297,7 +307,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             const int e = q * kThreads + tid;
             if (e < XE) {
                 const int ep = (e / kCPB) * kXR + e % kCPB;
-                s_dt[ep] = raw_f32(rdt[q], DT);
+                if constexpr (DISC != DISC_CONST) s_dt[ep] = raw_f32(rdt[q], DT);
                 if (bwd) {
                     s_z[ep] = raw_f32(rz[q], Z);
                     s_dy[ep] = raw_f32(rdy[q], DY);
@@ -335,7 +345,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 tk_xc[jj] = 0.0f;
                 uu = v ? s_u[e] : 0.0f;
             }
-            const float dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
+            float dl;
+            if constexpr (DISC == DISC_CONST)
+                dl = v ? 1.0f : 0.0f;
+            else
+                dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
             tk_dl[jj] = dl;
             tk_u[jj] = uu;
             tk_du[jj] = (DISC == DISC_DB) ? dl * uu : uu;
@@ -384,13 +398,18 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const float bq = s_B[i * NP + l + 16 * s];
-                const float a = hw_exp2(dli * A2[s]);
-                float w;
-                if constexpr (DISC == DISC_DB)
-                    w = dui * bq;
-                else
-                    w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
-                h[s] = fmaf(a, h[s], w);
+                if constexpr (DISC == DISC_CONST) {
+                    // dt is 1, or 0 past the end (no decay, no write there)
+                    h[s] += fmaf(dli * am1[s], h[s], dui * bq);
+                } else {
+                    const float a = hw_exp2(dli * A2[s]);
+                    float w;
+                    if constexpr (DISC == DISC_DB)
+                        w = dui * bq;
+                    else
+                        w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
+                    h[s] = fmaf(a, h[s], w);
+                }
             }
         }
     }
@@ -483,7 +502,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             const bool v = tt < T && ts + tt < Le && dvalid;
             const int e = min(tt, T - 1) * kXR + cl;
             tk_v[jj] = v;
-            tk_sg[jj] = sigmoid_f(s_dt[e] + dtb);
+            tk_sg[jj] = (DISC != DISC_CONST) ? sigmoid_f(s_dt[e] + dtb) : 0.0f;
             const float dyr = v ? s_dy[e] : 0.0f;
             tk_dy[jj] = dyr;
             if (gate) {
@@ -517,14 +536,20 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
                     for (int s = 0; s < S; ++s) {
                         const float bq = s_B[i * NP + l + 16 * s];
-                        const float a = hw_exp2(dli * A2[s]);
-                        float w;
-                        if constexpr (DISC == DISC_DB)
-                            w = dui * bq;
-                        else
-                            w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
-                        hs[i + 1][s] = fmaf(a, hs[i][s], w);
-                        as[i][s] = a;
+                        if constexpr (DISC == DISC_CONST) {
+                            const float dm = dli * am1[s];   // a - 1 of this token
+                            hs[i + 1][s] = hs[i][s] + fmaf(dm, hs[i][s], dui * bq);
+                            as[i][s] = dm;
+                        } else {
+                            const float a = hw_exp2(dli * A2[s]);
+                            float w;
+                            if constexpr (DISC == DISC_DB)
+                                w = dui * bq;
+                            else
+                                w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
+                            hs[i + 1][s] = fmaf(a, hs[i][s], w);
+                            as[i][s] = a;
+                        }
                         if (gate) yacc = fmaf(s_C[i * NP + l + 16 * s], hs[i + 1][s], yacc);
                     }
                     yp[kk] = yacc;
@@ -560,7 +585,8 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                         const float bq = s_B[i * NP + l + 16 * s];
                         const float cq = s_C[i * NP + l + 16 * s];
                         const float gj = fmaf(cq, dyv, g[s]);
-                        const float a = as[i][s];
+                        // as holds a - 1 for the constant decay
+                        const float a = (DISC == DISC_CONST) ? 1.0f + as[i][s] : as[i][s];
                         const float daa = gj * hs[i][s] * a;
                         float bpart;
                         if constexpr (DISC == DISC_DB) {
@@ -570,6 +596,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                             pu += gB;
                             bpart = gj * dui;
                             dA[s] = fmaf(daa, dli, dA[s]);
+                        } else if constexpr (DISC == DISC_CONST) {
+                            pu = fmaf(gj, bq, pu);
+                            bpart = gj * uu;
+                            dA[s] = fmaf(daa, dli, dA[s]);   // dt = 0 past the end
                         } else {
                             const float em1 = expm1f(dli * An[s]);
                             const float cz = em1 * Ainv[s];
@@ -582,7 +612,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                             dA[s] = fmaf(gBu * (dli * a * An[s] - em1), Ainv[s] * Ainv[s], dA[s]);
                         }
                         const float cpart = hs[i + 1][s] * dyv;
-                        g[s] = a * gj;
+                        if constexpr (DISC == DISC_CONST)
+                            g[s] = fmaf(as[i][s], gj, gj);
+                        else
+                            g[s] = a * gj;
                         // dB, dC terms of this channel; summed over channels below
                         s_rB[i][cl][l + 16 * s] = bpart;
                         s_rC[i][cl][l + 16 * s] = cpart;
@@ -592,7 +625,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 }
             }
             // lane l finishes token l + 16 jj
-            const float ddt = row_transpose_sum(pdt, l);
+            const float ddt = (DISC != DISC_CONST) ? row_transpose_sum(pdt, l) : 0.0f;
             const float dup = row_transpose_sum(pdu, l);
             tk_gx[jj] = 0.0f;
             if (tk_v[jj]) {
@@ -783,7 +816,7 @@ struct BwdLocalParams {
     int G;
 };
 
-template <typename IOT, int S>
+template <typename IOT, int S, bool CONSTD>
 __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
     // tiles of 64 tokens (four per lane of a row), the next tile's inputs
     // loaded into registers while the current one is walked
@@ -816,7 +849,9 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         const int n = l + 16 * s;
-        A2[s] = n < N ? neg_exp_f(p.A_log[dc * N + n]) * kLog2e : 0.0f;
+        const float A = n < N ? neg_exp_f(p.A_log[dc * N + n]) : 0.0f;
+        // constant decay: a - 1, applied in complement form below
+        A2[s] = CONSTD ? expm1f(A) : A * kLog2e;
         g[s] = 0.0f;
     }
     float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
@@ -839,12 +874,20 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
     auto fetch = [&](int k) {
         const int64_t ts = t0 + (int64_t)k * T;
         const uint64_t xr = (uint64_t)((Le - ts) * D - d0) * es;
-        const buf_t bDT = make_buf(DT + (b * L + ts) * D + d0, xr);
         const buf_t bDY = make_buf(DY + (b * L + ts) * D + d0, xr);
+        if constexpr (!CONSTD) {
+            const buf_t bDT = make_buf(DT + (b * L + ts) * D + d0, xr);
 #pragma unroll
-        for (int q = 0; q < XL; ++q) {
-            rdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
-            rdy[q] = buf_ld_raw(bDY, xoff + q * xstep, DY);
+            for (int q = 0; q < XL; ++q) {
+                rdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
+                rdy[q] = buf_ld_raw(bDY, xoff + q * xstep, DY);
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < XL; ++q) {
+                rdt[q] = 0;
+                rdy[q] = buf_ld_raw(bDY, xoff + q * xstep, DY);
+            }
         }
         if (gate) {
             const buf_t bZ = make_buf(Z + (b * L + ts) * D + d0, xr);
@@ -892,7 +935,7 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
             const int tt = l + 16 * jj;
             const bool v = ts + tt < Le;
             const int e = tt * kXR + cl;
-            const float dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
+            const float dl = v ? (CONSTD ? 1.0f : softplus_f(s_dt[e] + dtb)) : 0.0f;
             const float dyr = v ? s_dy[e] : 0.0f;
             tk_dl[jj] = dl;
             tk_dyv[jj] = gate ? dyr * silu_f(s_z[e]) : dyr;
@@ -904,7 +947,10 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const float gj = fmaf(s_C[i * NP + l + 16 * s], dyv, g[s]);
-                g[s] = hw_exp2(dli * A2[s]) * gj;
+                if constexpr (CONSTD)
+                    g[s] = fmaf(dli * A2[s], gj, gj);
+                else
+                    g[s] = hw_exp2(dli * A2[s]) * gj;
             }
         }
     }
@@ -928,13 +974,14 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(const float *A_log, cons
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= B * D * N) return;
     const int64_t n = i % N, d = (i / N) % D, b = i / (N * D);
-    const float A2 = neg_exp_f(A_log[d * N + n]) * kLog2e;
+    const float A = neg_exp_f(A_log[d * N + n]);
     float G = dhT ? dhT[i] : 0.0f;
     for (int k = KC - 1; k >= 0; --k) {
         const int64_t o = ((b * KC + k) * D + d) * N + n;
         const float Rk = k > 0 ? RG[o] : 0.0f;
         RG[o] = G;
-        if (k > 0) G = fmaf(hw_exp2(A2 * Sdt[(b * KC + k) * D + d]), G, Rk);
+        // Lambda_k G + R_k in complement form, G + ((Lambda_k - 1) G + R_k)
+        if (k > 0) G += fmaf(expm1f(A * Sdt[(b * KC + k) * D + d]), G, Rk);
     }
 }
 
@@ -1019,8 +1066,11 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
         q.dt = a.dt; q.Cm = a.Cm; q.z = a.z; q.dy = a.dy; q.dt_bias = a.dt_bias; q.A_log = a.A_log;
         q.R = w.RG; q.Sdt = w.Sdt;
         q.B = a.B; q.L = a.L; q.D = a.D; q.N = a.N; q.chunk = a.chunk; q.KC = (int)KC; q.G = G;
-        hipLaunchKernelGGL((bwd_local_kernel<IOT, S>), dim3((unsigned)(a.B * (KC - 1) * G)), dim3(kThreads), 0,
-                           s, q);
+        const dim3 lgrid((unsigned)(a.B * (KC - 1) * G));
+        if (a.disc == DISC_CONST)
+            hipLaunchKernelGGL((bwd_local_kernel<IOT, S, true>), lgrid, dim3(kThreads), 0, s, q);
+        else
+            hipLaunchKernelGGL((bwd_local_kernel<IOT, S, false>), lgrid, dim3(kThreads), 0, s, q);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         const int64_t nstate = a.B * a.D * a.N;
@@ -1051,6 +1101,11 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
             hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH, true>), grid, block, 0, s, p);
         else
             hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH, false>), grid, block, 0, s, p);
+    } else if (a.disc == DISC_CONST) {
+        if (a.W > 0)
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_CONST, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_CONST, false>), grid, block, 0, s, p);
     } else {
         if (a.W > 0)
             hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB, true>), grid, block, 0, s, p);

@@ -23,6 +23,19 @@
 //    wavefronts through LDS, in the fixed order ((w0 + w1) + (w2 + w3)).
 // The recurrence itself stays strictly sequential in time inside a chunk.
 //
+// Decay source ("the s6 cell", section "one cell, two architectures": one
+// diagonal cell h = a*h + b*u, two parameterisations).  DISC_DB and DISC_ZOH
+// compute the decay from the input at every token (one exp2 per state and
+// token).  DISC_CONST fixes it per (channel, state), a = e^A, so it is
+// computed once per lane before the time loop; the write is B*u and dt_raw is
+// never loaded.  The update is taken in complement form,
+// h + ((a - 1) h + w) with a - 1 = expm1(A): a decay close to 1 (a long
+// memory) stored as a float32 would carry an error of half an ulp of 1 in
+// its distance from 1, which the state amplifies by up to 1/(1 - a); the
+// complement keeps that distance to float32's relative precision.  Per
+// state and token this is a multiply, two FMAs and an add, no exp.  The time
+// split below sees dt = 1 per token.
+//
 // Long sequences with few independent channels are split in time (two-level
 // scan): MODE_LOCAL scans every chunk from a zero state and records its end
 // state W_k and sum of dt S_k; carry_kernel walks the chunks in order with
@@ -40,7 +53,7 @@ namespace {
 constexpr int kCPW = 16;            // channels per block
 constexpr int kNumXcd = 8;          // XCDs of an MI355X
 enum { MODE_FINAL = 0, MODE_LOCAL = 1 };
-enum { DISC_DB = 0, DISC_ZOH = 1 };
+enum { DISC_DB = 0, DISC_ZOH = 1, DISC_CONST = 2 };
 
 struct FwdParams {
     const void *x, *dt;
@@ -103,7 +116,7 @@ struct FetchOff {
 // boundary) are read but never used, states past N are zeroed at staging.
 // Every load is unconditional, so the compiler never waits on one (or on
 // anything issued before it) until the data is staged.
-template <typename IOT, int NP, bool WANT_C>
+template <typename IOT, int NP, bool WANT_C, bool WANT_DT>
 __device__ __forceinline__ void load_raw(RawTile<IOT, NP> &r, const FetchOff &fo, const IOT *X, const IOT *DT,
                                          const IOT *Z, const IOT *Bp, const IOT *Cp, int64_t b, int64_t L,
                                          int64_t D, int64_t N, int64_t ts) {
@@ -121,12 +134,15 @@ __device__ __forceinline__ void load_raw(RawTile<IOT, NP> &r, const FetchOff &fo
     }
     const uint64_t tb = (uint64_t)(left * D) * es;
     const buf_t rX = make_buf(X + (b * L + ts) * D, tb);
-    const buf_t rD = make_buf(DT + (b * L + ts) * D, tb);
 #pragma unroll
-    for (int i = 0; i < kRows; ++i) {
-        const uint32_t off = fo.x0 + (uint32_t)i * fo.xrow;
-        r.x[i] = buf_ld_raw(rX, off, X);
-        r.dt[i] = buf_ld_raw(rD, off, DT);
+    for (int i = 0; i < kRows; ++i) r.x[i] = buf_ld_raw(rX, fo.x0 + (uint32_t)i * fo.xrow, X);
+    if constexpr (WANT_DT) {
+        const buf_t rD = make_buf(DT + (b * L + ts) * D, tb);
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) r.dt[i] = buf_ld_raw(rD, fo.x0 + (uint32_t)i * fo.xrow, DT);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRows; ++i) r.dt[i] = 0;
     }
     if (Z != nullptr) {
         const buf_t rZ = make_buf(Z + (b * L + ts) * D, tb);
@@ -245,7 +261,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     const bool tvalid = td < D;
     const int64_t tdc = tvalid ? td : (D - 1);
 
-    float A2[SPL], An[SPL], Ainv[SPL], h[SPL];
+    float A2[SPL], An[SPL], Ainv[SPL], h[SPL], am1[DISC == DISC_CONST ? SPL : 1];
 #pragma unroll
     for (int s = 0; s < SPL; ++s) h[s] = 0.0f;
     // The starting state is requested first, so the wait for A_log below
@@ -263,11 +279,12 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
         A2[s] = v ? A * kLog2e : 0.0f;
         An[s] = A;
         Ainv[s] = 1.0f / A;
+        if constexpr (DISC == DISC_CONST) am1[s] = expm1f(A);   // a - 1
     }
 #pragma unroll
     for (int s = 0; s < SPL; ++s) asm volatile("" : "+v"(h[s]) : "v"(A2[s]));
 
-    const float dtb = p.dt_bias ? p.dt_bias[tdc] : 0.0f;
+    const float dtb = (DISC != DISC_CONST && p.dt_bias) ? p.dt_bias[tdc] : 0.0f;
     const float Dd = p.Dskip ? p.Dskip[tdc] : 0.0f;
     float wk[8], cb = 0.0f;
     const int W = p.W;
@@ -318,7 +335,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int i = 0; i < kRows; ++i) {
             const int row = rp * kRows + i;
-            const float dl = softplus_f(raw.f(raw.dt[i]) + dtb);
+            const float dl = (DISC == DISC_CONST) ? 1.0f : softplus_f(raw.f(raw.dt[i]) + dtb);
             s_dl[tc][row] = make_float2(dl, (DISC == DISC_DB) ? dl * uu[i] : uu[i]);
             if constexpr (FINAL)
                 s_gd[tc][row] = make_float2((Z != nullptr) ? silu_f(raw.f(raw.z[i])) : 1.0f, Dd * uu[i]);
@@ -341,7 +358,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
 
     auto fetch = [&](int it) {
         const int64_t ts = t0 + (int64_t)it * T;
-        load_raw<IOT, NP, FINAL>(raw, fo, X, DT, Z, Bp, Cp, b, L, D, N, ts);
+        load_raw<IOT, NP, FINAL, DISC != DISC_CONST>(raw, fo, X, DT, Z, Bp, Cp, b, L, D, N, ts);
     };
 
     float ssum = 0.0f;
@@ -353,13 +370,17 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
 #pragma unroll
         for (int s2 = 0; s2 < SPL; ++s2) {
             const float bq = s_B[(n0 + s2) * kTS + t];
-            const float a = hw_exp2(dl * A2[s2]);
-            float w;
-            if constexpr (DISC == DISC_DB)
-                w = pk.y * bq;
-            else
-                w = expm1f(dl * An[s2]) * Ainv[s2] * bq * pk.y;
-            h[s2] = fmaf(a, h[s2], w);
+            if constexpr (DISC == DISC_CONST) {
+                h[s2] += fmaf(am1[s2], h[s2], pk.y * bq);
+            } else {
+                const float a = hw_exp2(dl * A2[s2]);
+                float w;
+                if constexpr (DISC == DISC_DB)
+                    w = pk.y * bq;
+                else
+                    w = expm1f(dl * An[s2]) * Ainv[s2] * bq * pk.y;
+                h[s2] = fmaf(a, h[s2], w);
+            }
             if constexpr (FINAL) part = fmaf(s_C[(n0 + s2) * kTS + t], h[s2], part);
         }
         if constexpr (FINAL) {
@@ -386,13 +407,17 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             }
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float a = hw_exp2(dl[i] * A2[s2]);
-                float w;
-                if constexpr (DISC == DISC_DB)
-                    w = dy[i] * bq[i];
-                else
-                    w = expm1f(dl[i] * An[s2]) * Ainv[s2] * bq[i] * dy[i];
-                h[s2] = fmaf(a, h[s2], w);
+                if constexpr (DISC == DISC_CONST) {
+                    h[s2] += fmaf(am1[s2], h[s2], dy[i] * bq[i]);
+                } else {
+                    const float a = hw_exp2(dl[i] * A2[s2]);
+                    float w;
+                    if constexpr (DISC == DISC_DB)
+                        w = dy[i] * bq[i];
+                    else
+                        w = expm1f(dl[i] * An[s2]) * Ainv[s2] * bq[i] * dy[i];
+                    h[s2] = fmaf(a, h[s2], w);
+                }
                 if constexpr (FINAL) part[i] = fmaf(cq[i], h[s2], part[i]);
             }
         }
@@ -500,7 +525,9 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
 }
 
 // Walks the chunks of every (b, d, n) in time order, replacing each chunk's
-// local end state by the exact state at the chunk's start.  Also copies the
+// local end state by the exact state at the chunk's start.  The chunk's
+// decay e^(A S_k) enters in complement form, H + (expm1(A S_k) H + W_k), which
+// keeps short chunks of slow decays accurate.  Also copies the
 // incoming conv history so that MODE_FINAL never reads a buffer the same
 // launch writes.
 __global__ __launch_bounds__(256) void carry_kernel(const float *A_log, const float *h0, float *agg_h,
@@ -511,13 +538,13 @@ __global__ __launch_bounds__(256) void carry_kernel(const float *A_log, const fl
     const int64_t total = B * D * N;
     if (i < total) {
         const int64_t n = i % N, d = (i / N) % D, b = i / (N * D);
-        const float A2 = neg_exp_f(A_log[d * N + n]) * kLog2e;
+        const float A = neg_exp_f(A_log[d * N + n]);
         float H = h0 ? h0[i] : 0.0f;
         for (int k = 0; k < K; ++k) {
             const int64_t o = ((b * K + k) * D + d) * N + n;
             const float Wk = agg_h[o];
             agg_h[o] = H;
-            if (k + 1 < K) H = fmaf(hw_exp2(A2 * agg_s[(b * K + k) * D + d]), H, Wk);
+            if (k + 1 < K) H += fmaf(expm1f(A * agg_s[(b * K + k) * D + d]), H, Wk);
         }
     }
     if (conv_in != nullptr)
@@ -545,6 +572,10 @@ hipError_t dispatch_mode(const FwdParams &p, int disc, bool conv, int mode, hipS
     SSM_FWD_CASE(DISC_ZOH, true, MODE_FINAL)
     SSM_FWD_CASE(DISC_ZOH, false, MODE_LOCAL)
     SSM_FWD_CASE(DISC_ZOH, true, MODE_LOCAL)
+    SSM_FWD_CASE(DISC_CONST, false, MODE_FINAL)
+    SSM_FWD_CASE(DISC_CONST, true, MODE_FINAL)
+    SSM_FWD_CASE(DISC_CONST, false, MODE_LOCAL)
+    SSM_FWD_CASE(DISC_CONST, true, MODE_LOCAL)
 #undef SSM_FWD_CASE
     return hipErrorInvalidValue;
 }

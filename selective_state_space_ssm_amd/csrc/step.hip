@@ -20,6 +20,11 @@
 // read out in float32 and rounded to bf16 (nearest, ties to even) only when
 // stored, which halves the traffic that bounds the step.
 //
+// With the constant decay source (DISC_CONST: "the s6 cell", section "one
+// cell, two architectures") the decay is e^A with no step size, the write is
+// B*u and dt_raw is not loaded; the update is the sequence kernel's
+// complement form h + (expm1(A) h + B u).
+//
 // Arithmetic follows the sequence kernel operation by operation: the same
 // conv tap order, softplus, decay 2^(dt*A*log2 e) with A = -exp(A_log), and
 // the same readout tree -- chains over the sequence kernel's states per
@@ -35,7 +40,7 @@ namespace ssm {
 namespace {
 
 constexpr int kSPL = 4;    // states per lane
-enum { DISC_DB = 0, DISC_ZOH = 1 };
+enum { DISC_DB = 0, DISC_ZOH = 1, DISC_CONST = 2 };
 
 // LPC lanes per channel, 4 states per lane; VL = states per lane of the
 // sequence kernel (its readout chains); MAXW = widest conv carried.
@@ -73,9 +78,9 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     load_k_guard<kSPL>(Cp + bc, Cq, nvalid, vecN);
     load_k_guard<kSPL>(a.A_log + kd * N + n0, al, nvalid, vecN);
     const float xr = to_f32(X[sd]);
-    const float dtr = to_f32(DT[sd]);
+    const float dtr = (DISC != DISC_CONST) ? to_f32(DT[sd]) : 0.0f;
     const float zr = Z != nullptr ? to_f32(Z[sd]) : 0.0f;
-    const float dtb = a.dt_bias ? a.dt_bias[kd] : 0.0f;
+    const float dtb = (DISC != DISC_CONST && a.dt_bias) ? a.dt_bias[kd] : 0.0f;
     const float Dd = a.Dskip ? a.Dskip[kd] : 0.0f;
     float hv[MAXW > 1 ? MAXW - 1 : 1], cw[MAXW], cb = 0.0f;
     float *hist = nullptr;
@@ -105,7 +110,7 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     } else {
         uu = xr;
     }
-    const float dl = softplus_f(dtr + dtb);
+    const float dl = (DISC != DISC_CONST) ? softplus_f(dtr + dtb) : 1.0f;
     const float du = dl * uu;
     float part[kSPL / VL];
 #pragma unroll
@@ -115,13 +120,17 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
         const bool v = j < nvalid;
         const float A = neg_exp_f(v ? al[j] : 0.0f);
         const float A2 = v ? A * kLog2e : 0.0f;
-        const float dec = hw_exp2(dl * A2);
-        float w;
-        if constexpr (DISC == DISC_DB)
-            w = du * Bq[j];
-        else
-            w = expm1f(dl * A) * (1.0f / A) * Bq[j] * uu;
-        hq[j] = fmaf(dec, hq[j], w);
+        if constexpr (DISC == DISC_CONST) {
+            hq[j] += fmaf(expm1f(A), hq[j], uu * Bq[j]);
+        } else {
+            const float dec = hw_exp2(dl * A2);
+            float w;
+            if constexpr (DISC == DISC_DB)
+                w = du * Bq[j];
+            else
+                w = expm1f(dl * A) * (1.0f / A) * Bq[j] * uu;
+            hq[j] = fmaf(dec, hq[j], w);
+        }
         part[j / VL] = fmaf(Cq[j], hq[j], part[j / VL]);
     }
     if (active && nvalid > 0) store_k<kSPL>(hp, hq, nvalid, vecN);
@@ -169,6 +178,9 @@ hipError_t launch_g(const StepArgs &a, hipStream_t s) {
     SSM_STEP_CASE(DISC_ZOH, false, 1)
     SSM_STEP_CASE(DISC_ZOH, true, 4)
     SSM_STEP_CASE(DISC_ZOH, true, 8)
+    SSM_STEP_CASE(DISC_CONST, false, 1)
+    SSM_STEP_CASE(DISC_CONST, true, 4)
+    SSM_STEP_CASE(DISC_CONST, true, 8)
 #undef SSM_STEP_CASE
     return hipErrorInvalidValue;
 }

@@ -80,11 +80,34 @@ def test_scan_fwd_bad_shape(ssm, field, value):
     assert _fwd(ssm, d) == ssm.SSM_ERR_BAD_SHAPE
 
 
-@pytest.mark.parametrize("field,value", [("io_dtype", 2), ("disc", 2), ("disc", -1)])
+@pytest.mark.parametrize("field,value", [("io_dtype", 2), ("disc", 3), ("disc", -1)])
 def test_scan_fwd_unsupported(ssm, field, value):
     d = _desc(ssm)
     setattr(d, field, value)
     assert _fwd(ssm, d) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_const_decay_needs_no_step_size(ssm):
+    """With the constant decay source dt_raw may be NULL (it is never read):
+    the call gets past the NULL checks to the next error planted (a
+    misaligned tensor), where the input-driven forms stop at dt_raw."""
+    assert ssm.SSM_DECAY_CONST == 2
+    d_live, d_const = _desc(ssm), _desc(ssm, disc=ssm.SSM_DECAY_CONST)
+    assert _fwd(ssm, d_live, dt_raw=None, y=_addr(40, 4)) == ssm.SSM_ERR_NULL_ARG
+    assert _fwd(ssm, d_const, dt_raw=None, y=_addr(40, 4)) == ssm.SSM_ERR_ALIGNMENT
+    n = ssm.ssm_scan_bwd_workspace_size(d_const)
+    assert _bwd(ssm, d_live, _addr(50), n, dt_raw=None, dx=_addr(40, 4)) == ssm.SSM_ERR_NULL_ARG
+    assert _bwd(ssm, d_const, _addr(50), n, dt_raw=None, dx=_addr(40, 4)) == ssm.SSM_ERR_ALIGNMENT
+    L = ssm.lib()
+    ptrs = [_addr(i) for i in range(13)]
+    ptrs[3] = None        # dt_raw
+    ptrs[12] = _addr(40, 4)   # misaligned y
+    live = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, 0, 0)
+    const = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, ssm.SSM_DECAY_CONST, 0)
+    assert L.ssm_step(ctypes.byref(live), *ptrs, None) == ssm.SSM_ERR_NULL_ARG
+    assert L.ssm_step(ctypes.byref(const), *ptrs, None) == ssm.SSM_ERR_ALIGNMENT
+    bad = ssm.ssm_step_desc(2, 8, 32, 16, 4, 0, 3, 0)
+    assert L.ssm_step(ctypes.byref(bad), *ptrs, None) == ssm.SSM_ERR_UNSUPPORTED
 
 
 def test_scan_fwd_null_desc(ssm):
