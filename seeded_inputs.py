@@ -28,13 +28,22 @@ import numpy as np
 
 # tensor ids inside one workload
 _T = dict(x=1, dt_raw=2, B=3, C=4, z=5, dy=6, dt_bias=7, A_log=8, Dskip=9,
-          conv_w=10, conv_b=11, h0=12, conv_state=13, dhT=14)
+          conv_w=10, conv_b=11, h0=12, conv_state=13, dhT=14,
+          emb=20, norm_w=21, norm_b=22, in_proj=23, x_proj=24, dt_proj_w=25, out_proj=26, tokens=27)
 
 WL_TINY = 1
 WL_BLOCK = 2
 WL_STREAM = 3
 WL_LONG = 4
 WL_FWDBWD = 5
+WL_MODEL = 6
+
+# Model shapes: the pages' Mamba-mini (6 blocks at width 384, expand 4, N 16,
+# dt rank 24, conv 4, 4k-token vocabulary with the head tied to the embedding)
+# and two small ones for quick parity runs.
+MAMBA_MINI = dict(vocab=4096, d_model=384, n_layers=6, d_inner=1536, d_state=16, dt_rank=24, conv_width=4)
+TINY_MODEL = dict(vocab=64, d_model=16, n_layers=2, d_inner=32, d_state=4, dt_rank=4, conv_width=4)
+RAGGED_MODEL = dict(vocab=50, d_model=24, n_layers=3, d_inner=40, d_state=3, dt_rank=5, conv_width=3)
 
 
 def rng(seed, workload, tensor, *extra):
@@ -135,3 +144,56 @@ def stream_token_torch(block, step, S, D, N, device, seed=0):
     Bm = torch.randn(S, N, **kw)
     Cm = torch.randn(S, N, **kw)
     return dict(x=x, dt_raw=dt_raw, z=z, B=Bm, C=Cm)
+
+
+def model_params(cfg, seed=0):
+    """Random-init weights of a whole Mamba-style language model of shape cfg
+    (keys as in MAMBA_MINI), float32:
+      emb [vocab, d_model]                    standard normal (also the tied head)
+      per layer:
+        norm_w, norm_b [d_model]              1 + 0.1*normal, 0.1*normal
+        in_proj [2*d_inner, d_model]          uniform(+-1/sqrt(d_model))
+        conv_w [d_inner, W], conv_b [d_inner] uniform(+-1/sqrt(W))
+        x_proj [dt_rank + 2N, d_inner]        uniform(+-1/sqrt(d_inner))
+        dt_proj_w [d_inner, dt_rank]          uniform(+-1/sqrt(dt_rank))
+        dt_proj_b [d_inner]                   inverse softplus of delta0, delta0
+                                              log-uniform in [1e-3, 1e-1]
+        A_log [d_inner, N] = log(n + 1),  Dskip [d_inner] = 1
+        out_proj [d_model, d_inner]           uniform(+-1/sqrt(d_inner))
+      norm_f_w, norm_f_b [d_model]            as the layers' norms
+    (the uniform ranges are PyTorch's default Linear / Conv1d init; the norms
+    are perturbed from 1 and 0 so that their parameters matter)."""
+    V, dm, nl = cfg["vocab"], cfg["d_model"], cfg["n_layers"]
+    Di, N, R, W = cfg["d_inner"], cfg["d_state"], cfg["dt_rank"], cfg["conv_width"]
+    wl = WL_MODEL
+
+    def u(t, shape, bound, *ex):
+        return rng(seed, wl, t, *ex).uniform(-bound, bound, shape).astype(np.float32)
+
+    def n(t, shape, *ex):
+        return rng(seed, wl, t, *ex).standard_normal(shape).astype(np.float32)
+
+    layers = []
+    for l in range(nl):
+        delta0 = np.exp(rng(seed, wl, "dt_bias", l).uniform(np.log(1e-3), np.log(1e-1), Di))
+        layers.append(dict(
+            norm_w=(1.0 + 0.1 * n("norm_w", (dm,), l)).astype(np.float32),
+            norm_b=(0.1 * n("norm_b", (dm,), l)).astype(np.float32),
+            in_proj=u("in_proj", (2 * Di, dm), 1.0 / np.sqrt(dm), l),
+            conv_w=u("conv_w", (Di, W), 1.0 / np.sqrt(W), l),
+            conv_b=u("conv_b", (Di,), 1.0 / np.sqrt(W), l),
+            x_proj=u("x_proj", (R + 2 * N, Di), 1.0 / np.sqrt(Di), l),
+            dt_proj_w=u("dt_proj_w", (Di, R), 1.0 / np.sqrt(R), l),
+            dt_proj_b=inverse_softplus(delta0).astype(np.float32),
+            A_log=np.tile(np.log(np.arange(1, N + 1, dtype=np.float64)), (Di, 1)).astype(np.float32),
+            Dskip=np.ones(Di, np.float32),
+            out_proj=u("out_proj", (dm, Di), 1.0 / np.sqrt(Di), l),
+        ))
+    return dict(cfg=dict(cfg), emb=n("emb", (V, dm)), layers=layers,
+                norm_f_w=(1.0 + 0.1 * n("norm_w", (dm,), nl)).astype(np.float32),
+                norm_f_b=(0.1 * n("norm_b", (dm,), nl)).astype(np.float32))
+
+
+def model_tokens(cfg, S, T, seed=0):
+    """Token ids [S, T], uniform over the vocabulary (int32)."""
+    return rng(seed, WL_MODEL, "tokens", S, T).integers(0, cfg["vocab"], (S, T)).astype(np.int32)
