@@ -413,6 +413,55 @@ def bench_extras(torch, np, si, ssm, dev, args):
             "note": "state + history of the 6 blocks (%d MB) fit the 256 MB last-level cache"
                     % round(nblk * S * (D * N * (2 if nb == bytes16 else 4) + 3 * D * 4) / 1e6)}
         log("streaming %s: %.1f us per token step" % (name, ms * 1e3))
+    del h, cs, toks, ys, prm
+    torch.cuda.empty_cache()
+
+    # the whole Mamba-mini model (random-init weights), one token per stream
+    # per step: embedding, 6 blocks (LayerNorm, in_proj + conv, x_proj,
+    # dt_proj, the selective step, out_proj + residual), final LayerNorm and
+    # the tied 4096-token head.  Steps captured in HIP graphs of 32 tokens.
+    cfg = si.MAMBA_MINI
+    mp = si.model_params(cfg)
+    emb = dev(mp["emb"])
+    nfw, nfb = dev(mp["norm_f_w"]), dev(mp["norm_f_b"])
+    layers = ssm.ModelLayers([{k: dev(v) for k, v in lay.items()} for lay in mp["layers"]])
+    wbytes = 4 * (sum(v.size for lay in mp["layers"] for v in lay.values()) + mp["emb"].size)
+    for Sm in (1, 256):
+        desc = ssm.model_desc(cfg, Sm)
+        ws = torch.empty(ssm.ssm_model_decode_workspace_size(desc), dtype=torch.uint8, device="cuda")
+        hm = torch.zeros(cfg["n_layers"], Sm, cfg["d_inner"], cfg["d_state"], device="cuda")
+        cm = torch.zeros(cfg["n_layers"], Sm, cfg["conv_width"] - 1, cfg["d_inner"], device="cuda")
+        tk = torch.from_numpy(si.model_tokens(cfg, Sm, pool).T.copy()).cuda()   # [pool, S]
+        lg = torch.empty(Sm, cfg["vocab"], device="cuda")
+
+        def dstep(t):
+            ssm.ssm_model_decode_step(desc, emb, layers, tk[t], hm, cm, logits=lg, norm_f_w=nfw, norm_f_b=nfb,
+                                      workspace=ws)
+
+        for t in range(4):
+            dstep(t)
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for t in range(pool):
+                dstep(t)
+        gr.replay()
+        torch.cuda.synchronize()
+        tm = EventTimer(torch)
+        nrep = max(4, 256 // pool)
+        t0 = time.perf_counter()
+        for _ in range(nrep):
+            tm.run(gr.replay)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = tm.mean_ms() / pool
+        ex["decode_mamba_mini_%dstream%s" % (Sm, "" if Sm == 1 else "s")] = {
+            "tokens_per_s": Sm / (ms * 1e-3), "tokens_per_s_wall": Sm * nrep * pool / wall,
+            "us_per_token_step": round(ms * 1e3, 2), "weights_MB": round(wbytes / 1e6, 1),
+            "note": "6 blocks + tied head, random-init weights (no quality claim); the pages' browser "
+                    "figure is 535 tokens/s for one stream on an unspecified machine"}
+        log("model decode, %d stream(s): %.1f us per token step" % (Sm, ms * 1e3))
+        del ws, hm, cm, tk, lg
     return ex
 
 

@@ -124,6 +124,36 @@ typedef struct ssm_conv_desc {
     int32_t reserved;    /* must be 0 */
 } ssm_conv_desc;
 
+/* Shape of a whole Mamba-style language model (ssm_model_decode_step). */
+typedef struct ssm_model_desc {
+    int64_t nstreams;    /* S >= 1 independent token streams decoded together */
+    int32_t vocab;       /* V >= 1 tokens; the head is tied to the embedding */
+    int32_t d_model;     /* residual width, 1 .. SSM_MAX_D_MODEL */
+    int32_t n_layers;    /* blocks, >= 1 */
+    int32_t d_inner;     /* inner channels per block, >= 1 */
+    int32_t d_state;     /* N in [1, SSM_MAX_DSTATE] */
+    int32_t dt_rank;     /* rank of the step-size projection, >= 1 */
+    int32_t conv_width;  /* W in [1, SSM_MAX_CONV_WIDTH] */
+    int32_t reserved;    /* must be 0 */
+} ssm_model_desc;
+#define SSM_MAX_D_MODEL 8192
+
+/* One block's weights, all float32 device pointers (PyTorch Linear layout,
+ * [out_features, in_features]).  NULL optionals: norm_w 1, norm_b 0,
+ * conv_b 0, dt_proj_b 0, Dskip 0. */
+typedef struct ssm_layer_weights {
+    const float *norm_w, *norm_b;      /* [d_model] LayerNorm (eps 1e-5), optional */
+    const float *in_proj;              /* [2*d_inner, d_model]: rows 0..d_inner-1 give xin, the rest z */
+    const float *conv_w;               /* [d_inner, W], tap W-1 on the current input */
+    const float *conv_b;               /* [d_inner], optional */
+    const float *x_proj;               /* [dt_rank + 2*d_state, d_inner]: rows give dt, B, C in that order */
+    const float *dt_proj_w;            /* [d_inner, dt_rank] */
+    const float *dt_proj_b;            /* [d_inner], optional (the scan's dt_bias) */
+    const float *A_log;                /* [d_inner, d_state] */
+    const float *Dskip;                /* [d_inner], optional */
+    const float *out_proj;             /* [d_model, d_inner] */
+} ssm_layer_weights;
+
 /* Library version (SSM_ABI_VERSION * 100 + minor). */
 int32_t ssm_version(void);
 
@@ -262,6 +292,40 @@ ssm_status ssm_step(const ssm_step_desc *desc, void *h, float *conv_state, const
                     const void *dt_raw, const void *B, const void *C, const void *z,
                     const float *conv_w, const float *conv_b, const float *dt_bias,
                     const float *A_log, const float *Dskip, void *y, void *stream);
+
+/*
+ * ssm_model_decode_step -- one token of every stream through a whole
+ * Mamba-style language model ("mamba, live", section "what is actually
+ * running": the streaming form, one token in, one token out):
+ *   x = emb[token]
+ *   for each block:  hn = LayerNorm(x);  [xin, z] = in_proj(hn)
+ *                    u = SiLU(causal conv of xin over the carried history)
+ *                    [dt, B, C] = x_proj(u);  dt_raw = dt_proj_w dt
+ *                    one ssm_step of the block's state with u, dt_raw,
+ *                    dt_bias = dt_proj_b, B, C and the gate z -> y
+ *                    x += out_proj(y)
+ *   logits = LayerNorm_out(x) emb^T          (head tied to the embedding)
+ * The projections run on the matrix cores in float32.  Everything is float32.
+ *   desc        host pointer, the model's shape
+ *   emb         f32 [V, d_model]   embedding and head (required)
+ *   norm_f_w, norm_f_b  f32 [d_model]  final LayerNorm, optional (1, 0)
+ *   layers      HOST array of n_layers ssm_layer_weights (device pointers inside),
+ *               read before the call returns
+ *   tokens      int32 [S]           device; a token outside [0, V) makes that
+ *                                   stream's logits and state NaN
+ *   h           f32 [n_layers, S, d_inner, d_state]   state, in/out (zeros to start)
+ *   conv_state  f32 [n_layers, S, W-1, d_inner]       conv history, in/out (oldest
+ *                                   first; may be NULL when W = 1)
+ *   logits      f32 [S, V]          output
+ *   workspace   ssm_model_decode_workspace_size bytes (required)
+ * Every pointer must be 16-byte aligned, except tokens (4-byte aligned);
+ * outputs may not overlap the inputs, the workspace or each other.
+ */
+ssm_status ssm_model_decode_workspace_size(const ssm_model_desc *desc, size_t *bytes);
+ssm_status ssm_model_decode_step(const ssm_model_desc *desc, const float *emb, const float *norm_f_w,
+                                 const float *norm_f_b, const ssm_layer_weights *layers,
+                                 const int32_t *tokens, float *h, float *conv_state, float *logits,
+                                 void *workspace, size_t workspace_bytes, void *stream);
 
 #ifdef __cplusplus
 }

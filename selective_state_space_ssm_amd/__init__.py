@@ -37,6 +37,7 @@ SSM_DECAY_CONST = 2   # decay fixed per (channel, state); no step size, dt_raw m
 EXPORTED_SYMBOLS = (
     "ssm_version", "ssm_status_string", "conv1d_causal", "ssm_scan_fwd_workspace_size",
     "ssm_scan_fwd", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_step",
+    "ssm_model_decode_workspace_size", "ssm_model_decode_step",
 )
 
 
@@ -62,6 +63,20 @@ class ssm_conv_desc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64), ("dim", ctypes.c_int64),
                 ("width", ctypes.c_int32), ("fuse_silu", ctypes.c_int32),
                 ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class ssm_model_desc(ctypes.Structure):
+    _fields_ = [("nstreams", ctypes.c_int64), ("vocab", ctypes.c_int32), ("d_model", ctypes.c_int32),
+                ("n_layers", ctypes.c_int32), ("d_inner", ctypes.c_int32), ("d_state", ctypes.c_int32),
+                ("dt_rank", ctypes.c_int32), ("conv_width", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+LAYER_FIELDS = ("norm_w", "norm_b", "in_proj", "conv_w", "conv_b", "x_proj", "dt_proj_w", "dt_proj_b",
+                "A_log", "Dskip", "out_proj")
+
+
+class ssm_layer_weights(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_void_p) for f in LAYER_FIELDS]
 
 
 _lib = None
@@ -92,6 +107,11 @@ def lib():
         L.ssm_scan_bwd.argtypes = [ctypes.POINTER(ssm_scan_desc)] + [p] * 27 + [sz, p]
         L.ssm_step.restype = i32
         L.ssm_step.argtypes = [ctypes.POINTER(ssm_step_desc)] + [p] * 14
+        L.ssm_model_decode_workspace_size.restype = i32
+        L.ssm_model_decode_workspace_size.argtypes = [ctypes.POINTER(ssm_model_desc), ctypes.POINTER(sz)]
+        L.ssm_model_decode_step.restype = i32
+        L.ssm_model_decode_step.argtypes = [ctypes.POINTER(ssm_model_desc), p, p, p,
+                                            ctypes.POINTER(ssm_layer_weights), p, p, p, p, p, sz, p]
         _lib = L
     return _lib
 
@@ -274,3 +294,50 @@ def ssm_step(h, x, dt_raw, A_log, B, C, conv_state=None, z=None, conv_w=None, co
         _f32(conv_b, "conv_b"), _f32(dt_bias, "dt_bias"), _f32(A_log, "A_log"), _f32(Dskip, "Dskip"),
         _ptr(y, t, "y"), _stream(stream)))
     return y
+
+
+def model_desc(cfg, S) -> ssm_model_desc:
+    """Descriptor of a model with shape cfg (keys vocab, d_model, n_layers,
+    d_inner, d_state, dt_rank, conv_width) decoding S streams."""
+    return ssm_model_desc(S, cfg["vocab"], cfg["d_model"], cfg["n_layers"], cfg["d_inner"], cfg["d_state"],
+                          cfg["dt_rank"], cfg["conv_width"], 0)
+
+
+def ssm_model_decode_workspace_size(desc) -> int:
+    n = ctypes.c_size_t(0)
+    _check("ssm_model_decode_workspace_size",
+           lib().ssm_model_decode_workspace_size(ctypes.byref(desc), ctypes.byref(n)))
+    return int(n.value)
+
+
+class ModelLayers:
+    """The host array of per-block weight pointers for ssm_model_decode_step,
+    built once from device tensors (keys LAYER_FIELDS) and kept with them."""
+
+    def __init__(self, layers):
+        self.tensors = [dict(lay) for lay in layers]
+        arr = (ssm_layer_weights * len(layers))()
+        for i, lay in enumerate(self.tensors):
+            for f in LAYER_FIELDS:
+                t = lay.get(f)
+                setattr(arr[i], f, None if t is None else _f32(t, f).value)
+        self.array = arr
+
+
+def ssm_model_decode_step(desc, emb, layers, tokens, h, conv_state, logits=None, norm_f_w=None, norm_f_b=None,
+                          workspace=None, stream=None):
+    """One token for every stream through the whole model.  layers is a
+    ModelLayers; tokens int32 [S] on the device; h [n_layers, S, d_inner, N]
+    and conv_state [n_layers, S, W-1, d_inner] (float32) are updated in place.
+    Returns logits [S, vocab]."""
+    S, V = desc.nstreams, desc.vocab
+    if logits is None:
+        logits = torch.empty(S, V, device=tokens.device, dtype=torch.float32)
+    ws = workspace
+    if ws is None:
+        ws = torch.empty(ssm_model_decode_workspace_size(desc), dtype=torch.uint8, device=tokens.device)
+    _check("ssm_model_decode_step", lib().ssm_model_decode_step(
+        ctypes.byref(desc), _f32(emb, "emb"), _f32(norm_f_w, "norm_f_w"), _f32(norm_f_b, "norm_f_b"),
+        layers.array, _ptr(tokens, torch.int32, "tokens"), _f32(h, "h"), _f32(conv_state, "conv_state"),
+        _f32(logits, "logits"), _ptr(ws, None, "workspace"), ctypes.c_size_t(ws.numel()), _stream(stream)))
+    return logits

@@ -17,7 +17,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_amd.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["abi.cpp", "conv1d.hip", "scan_fwd.hip", "scan_bwd.hip", "step.hip"]
+SOURCES = ["abi.cpp", "conv1d.hip", "scan_fwd.hip", "scan_bwd.hip", "step.hip", "model.hip"]
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",

@@ -100,7 +100,7 @@ int64_t resolve_chunk(const ssm_scan_desc *d) {
 
 extern "C" {
 
-int32_t ssm_version(void) { return SSM_ABI_VERSION * 100 + 0; }
+int32_t ssm_version(void) { return SSM_ABI_VERSION * 100 + 1; }
 
 const char *ssm_status_string(ssm_status s) {
     switch (s) {
@@ -333,6 +333,96 @@ ssm_status ssm_step(const ssm_step_desc *desc, void *h, float *conv_state, const
     a.conv_w = W > 0 ? conv_w : nullptr; a.conv_b = W > 0 ? conv_b : nullptr;
     a.dt_bias = dt_bias; a.A_log = A_log; a.Dskip = Dskip; a.y = y;
     return hip_status(ssm::launch_step(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+ssm_status check_model_desc(const ssm_model_desc *d) {
+    if (!d) return SSM_ERR_NULL_ARG;
+    if (d->reserved != 0) return SSM_ERR_UNSUPPORTED;
+    if (d->nstreams < 1 || d->vocab < 1 || d->d_model < 1 || d->d_model > SSM_MAX_D_MODEL || d->n_layers < 1 ||
+        d->d_inner < 1 || d->d_state < 1 || d->d_state > SSM_MAX_DSTATE || d->dt_rank < 1 ||
+        d->conv_width < 1 || d->conv_width > SSM_MAX_CONV_WIDTH)
+        return SSM_ERR_BAD_SHAPE;
+    int64_t n;
+    const int64_t S = d->nstreams, Di = d->d_inner;
+    if (!elems({S, d->vocab}, &n) || !elems({d->n_layers, S, Di, d->d_state}, &n) ||
+        !elems({d->n_layers, S, d->conv_width - 1, Di}, &n) || !elems({S, 2 * Di}, &n) ||
+        !elems({(int64_t)d->vocab, d->d_model}, &n) || !elems({2 * Di, d->d_model}, &n) ||
+        !elems({(int64_t)d->dt_rank + 2 * d->d_state, Di}, &n))
+        return SSM_ERR_BAD_SHAPE;
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_model_decode_workspace_size(const ssm_model_desc *desc, size_t *bytes) {
+    ssm_status st = check_model_desc(desc);
+    if (st != SSM_OK) return st;
+    if (!bytes) return SSM_ERR_NULL_ARG;
+    *bytes = ssm::model_workspace_bytes(desc->nstreams, desc->d_model, desc->d_inner, desc->d_state,
+                                        desc->dt_rank);
+    return SSM_OK;
+}
+
+ssm_status ssm_model_decode_step(const ssm_model_desc *desc, const float *emb, const float *norm_f_w,
+                                 const float *norm_f_b, const ssm_layer_weights *layers,
+                                 const int32_t *tokens, float *h, float *conv_state, float *logits,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    ssm_status st = check_model_desc(desc);
+    if (st != SSM_OK) return st;
+    const int64_t S = desc->nstreams, V = desc->vocab, dm = desc->d_model, nl = desc->n_layers;
+    const int64_t Di = desc->d_inner, N = desc->d_state, R = desc->dt_rank, W = desc->conv_width;
+    if (!emb || !layers || !tokens || !h || !logits || (W > 1 && !conv_state)) return SSM_ERR_NULL_ARG;
+    for (int64_t l = 0; l < nl; ++l) {
+        const ssm_layer_weights &L = layers[l];
+        if (!L.in_proj || !L.conv_w || !L.x_proj || !L.dt_proj_w || !L.A_log || !L.out_proj)
+            return SSM_ERR_NULL_ARG;
+    }
+    const size_t need = ssm::model_workspace_bytes(S, dm, Di, N, R);
+    if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
+    AliasCheck ac;
+    ac.ins = {{emb, V * dm * 4}, {norm_f_w, norm_f_w ? dm * 4 : 0}, {norm_f_b, norm_f_b ? dm * 4 : 0},
+              {tokens, S * 4}};
+    for (int64_t l = 0; l < nl; ++l) {
+        const ssm_layer_weights &L = layers[l];
+        const std::vector<Range> r = {{L.norm_w, L.norm_w ? dm * 4 : 0}, {L.norm_b, L.norm_b ? dm * 4 : 0},
+                                      {L.in_proj, 2 * Di * dm * 4},   {L.conv_w, Di * W * 4},
+                                      {L.conv_b, L.conv_b ? Di * 4 : 0}, {L.x_proj, (R + 2 * N) * Di * 4},
+                                      {L.dt_proj_w, Di * R * 4},      {L.dt_proj_b, L.dt_proj_b ? Di * 4 : 0},
+                                      {L.A_log, Di * N * 4},          {L.Dskip, L.Dskip ? Di * 4 : 0},
+                                      {L.out_proj, dm * Di * 4}};
+        for (const Range &x : r) {
+            if (!aligned16(x.p)) return SSM_ERR_ALIGNMENT;
+            ac.ins.push_back(x);
+        }
+    }
+    for (const void *p : {(const void *)emb, (const void *)norm_f_w, (const void *)norm_f_b, (const void *)h,
+                          (const void *)conv_state, (const void *)logits, (const void *)workspace})
+        if (!aligned16(p)) return SSM_ERR_ALIGNMENT;
+    // token ids are read one by one: 4-byte alignment, so that step t of a
+    // [T, S] token buffer can be passed as is
+    if ((reinterpret_cast<uintptr_t>(tokens) & 3u) != 0) return SSM_ERR_ALIGNMENT;
+    ac.outs = {{h, nl * S * Di * N * 4},
+               {conv_state, W > 1 ? nl * S * (W - 1) * Di * 4 : 0},
+               {logits, S * V * 4},
+               {workspace, (int64_t)need}};
+    if (!ac.ok()) return SSM_ERR_ALIAS;
+    std::vector<ssm::ModelLayer> ls((size_t)nl);
+    for (int64_t l = 0; l < nl; ++l) {
+        const ssm_layer_weights &L = layers[l];
+        ls[(size_t)l] = ssm::ModelLayer{L.norm_w, L.norm_b, L.in_proj, L.conv_w, L.conv_b, L.x_proj,
+                                        L.dt_proj_w, L.dt_proj_b, L.A_log, L.Dskip, L.out_proj};
+    }
+    ssm::ModelArgs a{};
+    a.S = S; a.V = (int)V; a.dm = (int)dm; a.nl = (int)nl; a.Di = (int)Di; a.N = (int)N; a.R = (int)R; a.W = (int)W;
+    a.emb = emb; a.norm_f_w = norm_f_w; a.norm_f_b = norm_f_b; a.layers = ls.data(); a.tok = tokens;
+    a.h = h; a.conv = W > 1 ? conv_state : nullptr; a.logits = logits; a.ws = workspace;
+    return hip_status(ssm::launch_model_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -91,8 +91,40 @@ struct StepArgs {
     const void *x, *dt, *Bm, *Cm, *z;
     const float *conv_w, *conv_b, *dt_bias, *A_log, *Dskip;
     void *y;
+    // launch_step_dtproj only: dt_raw = dt_low[s] . dt_w[d] (rank dt_rank)
+    const float *dt_low, *dt_w;
+    int dt_rank;
 };
 hipError_t launch_step(const StepArgs &a, hipStream_t s);
+// The step of the whole-model decode: float32, dt*B form, no conv, dt_raw
+// formed from the low-rank projection instead of loaded.
+hipError_t launch_step_dtproj(const StepArgs &a, hipStream_t s);
+
+// One streaming token of a whole Mamba-style model (model.hip).
+struct ModelLayer {
+    const float *norm_w, *norm_b;     // [dm] (NULL: 1, 0)
+    const float *in_proj;             // [2 Di, dm]
+    const float *conv_w, *conv_b;     // [Di, W], [Di]
+    const float *x_proj;              // [R + 2N, Di]
+    const float *dt_w, *dt_b;         // [Di, R], [Di]
+    const float *A_log;               // [Di, N]
+    const float *Dskip;               // [Di]
+    const float *out_proj;            // [dm, Di]
+};
+struct ModelArgs {
+    int64_t S;
+    int V, dm, nl, Di, N, R, W;
+    const float *emb;                 // [V, dm], also the head
+    const float *norm_f_w, *norm_f_b;
+    const ModelLayer *layers;         // host array [nl]
+    const int32_t *tok;               // [S]
+    float *h;                         // [nl, S, Di, N]
+    float *conv;                      // [nl, S, W-1, Di]
+    float *logits;                    // [S, V]
+    void *ws;
+};
+size_t model_workspace_bytes(int64_t S, int64_t dm, int64_t Di, int64_t N, int64_t R);
+hipError_t launch_model_decode(const ModelArgs &a, hipStream_t s);
 
 // Byte offset helper for workspace carving (256-byte aligned regions).
 inline size_t ws_align(size_t n) { return (n + 255) & ~(size_t)255; }

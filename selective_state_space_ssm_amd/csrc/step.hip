@@ -44,7 +44,9 @@ enum { DISC_DB = 0, DISC_ZOH = 1, DISC_CONST = 2 };
 
 // LPC lanes per channel, 4 states per lane; VL = states per lane of the
 // sequence kernel (its readout chains); MAXW = widest conv carried.
-template <typename IOT, typename HT, int LPC, int VL, int DISC, bool CONV, int MAXW>
+// DTPROJ (the whole-model decode): dt_raw is not loaded but formed as the
+// low-rank projection dt_low[s] . dt_w[d] (rank dt_rank), in order of r.
+template <typename IOT, typename HT, int LPC, int VL, int DISC, bool CONV, int MAXW, bool DTPROJ = false>
 __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     const IOT *X = static_cast<const IOT *>(a.x);
     const IOT *DT = static_cast<const IOT *>(a.dt);
@@ -78,7 +80,16 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     load_k_guard<kSPL>(Cp + bc, Cq, nvalid, vecN);
     load_k_guard<kSPL>(a.A_log + kd * N + n0, al, nvalid, vecN);
     const float xr = to_f32(X[sd]);
-    const float dtr = (DISC != DISC_CONST) ? to_f32(DT[sd]) : 0.0f;
+    float dtr = 0.0f;
+    if constexpr (DTPROJ) {
+        // the channel's LPC lanes take every LPC-th term, then sum over the lanes
+        const float *dl = a.dt_low + (k * S + s) * a.dt_rank;
+        const float *dw = a.dt_w + kd * a.dt_rank;
+        for (int r = q; r < a.dt_rank; r += LPC) dtr = fmaf(dl[r], dw[r], dtr);
+        dtr = group_sum<LPC>(dtr);
+    } else if constexpr (DISC != DISC_CONST) {
+        dtr = to_f32(DT[sd]);
+    }
     const float zr = Z != nullptr ? to_f32(Z[sd]) : 0.0f;
     const float dtb = (DISC != DISC_CONST && a.dt_bias) ? a.dt_bias[kd] : 0.0f;
     const float Dd = a.Dskip ? a.Dskip[kd] : 0.0f;
@@ -194,6 +205,19 @@ hipError_t launch_io(const StepArgs &a, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_step_dtproj(const StepArgs &a, hipStream_t s) {
+    if (a.nblk * a.S * a.D == 0) return hipSuccess;
+    if (a.bf16 || a.state_bf16 || a.disc != DISC_DB || a.W != 0) return hipErrorInvalidValue;
+    auto go = [&](auto kern, int lpc) {
+        const int64_t threads = a.nblk * a.S * a.D * lpc;
+        hipLaunchKernelGGL(kern, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
+        return hipGetLastError();
+    };
+    if (a.N <= 16) return go(step_kernel<float, float, 4, 1, DISC_DB, false, 1, true>, 4);
+    if (a.N <= 32) return go(step_kernel<float, float, 8, 2, DISC_DB, false, 1, true>, 8);
+    return go(step_kernel<float, float, 16, 4, DISC_DB, false, 1, true>, 16);
+}
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     if (a.nblk * a.S * a.D == 0) return hipSuccess;

@@ -236,3 +236,44 @@ def test_binding_rejects_host_tensors(ssm):
     x = torch.zeros(1, 4, 8)
     with pytest.raises(ValueError):
         ssm.conv1d_causal(x, torch.zeros(8, 4))
+
+
+def _model_call(ssm, desc, ws_bytes=None, layer_over=None, **over):
+    """ssm_model_decode_step with fake, aligned, disjoint device addresses."""
+    nl = desc.n_layers
+    arr = (ssm.ssm_layer_weights * nl)()
+    for i in range(nl):
+        for j, f in enumerate(ssm.LAYER_FIELDS):
+            setattr(arr[i], f, A + (100 + 16 * i + j) * 0x1000000)
+        for f, v in (layer_over or {}).items():
+            setattr(arr[i], f, v)
+    args = dict(emb=_addr(1), norm_f_w=_addr(2), norm_f_b=_addr(3), tokens=_addr(4), h=_addr(5),
+                conv_state=_addr(6), logits=_addr(7), workspace=_addr(8))
+    args.update(over)
+    n = ssm.ssm_model_decode_workspace_size(desc) if ws_bytes is None else ws_bytes
+    return ssm.lib().ssm_model_decode_step(
+        ctypes.byref(desc), args["emb"], args["norm_f_w"], args["norm_f_b"], arr, args["tokens"], args["h"],
+        args["conv_state"], args["logits"], args["workspace"], ctypes.c_size_t(n), None)
+
+
+def test_model_decode_validation(ssm):
+    import seeded_inputs as si
+    good = ssm.model_desc(si.TINY_MODEL, 4)
+    assert ssm.ssm_model_decode_workspace_size(good) > 0
+    for field, value, code in [("d_state", 65, ssm.SSM_ERR_BAD_SHAPE), ("conv_width", 0, ssm.SSM_ERR_BAD_SHAPE),
+                               ("conv_width", 9, ssm.SSM_ERR_BAD_SHAPE), ("nstreams", 0, ssm.SSM_ERR_BAD_SHAPE),
+                               ("dt_rank", 0, ssm.SSM_ERR_BAD_SHAPE), ("d_model", 8193, ssm.SSM_ERR_BAD_SHAPE),
+                               ("reserved", 1, ssm.SSM_ERR_UNSUPPORTED)]:
+        d = ssm.model_desc(si.TINY_MODEL, 4)
+        setattr(d, field, value)
+        assert _model_call(ssm, d, ws_bytes=1 << 20) == code, field
+    assert _model_call(ssm, good, emb=None) == ssm.SSM_ERR_NULL_ARG
+    assert _model_call(ssm, good, layer_over={"x_proj": None}) == ssm.SSM_ERR_NULL_ARG
+    assert _model_call(ssm, good, conv_state=None) == ssm.SSM_ERR_NULL_ARG      # W = 4 needs the history
+    n = ssm.ssm_model_decode_workspace_size(good)
+    assert _model_call(ssm, good, ws_bytes=n - 1) == ssm.SSM_ERR_WORKSPACE
+    assert _model_call(ssm, good, logits=_addr(7, 4)) == ssm.SSM_ERR_ALIGNMENT
+    assert _model_call(ssm, good, tokens=_addr(4, 2)) == ssm.SSM_ERR_ALIGNMENT
+    assert _model_call(ssm, good, layer_over={"A_log": A + 0x50000004}) == ssm.SSM_ERR_ALIGNMENT
+    assert _model_call(ssm, good, logits=_addr(1, 64)) == ssm.SSM_ERR_ALIAS     # logits inside emb
+    assert _model_call(ssm, good, h=_addr(8, 256)) == ssm.SSM_ERR_ALIAS         # state inside the workspace
