@@ -195,6 +195,8 @@ def main():
     if not args.no_cpu_baseline:
         try:
             out["cpu_baseline"] = cpu_baseline(np, si)
+            if not args.no_extra:
+                out["cpu_baseline"]["extras"] = cpu_baseline_extras(np, si)
         except Exception as e:
             log("cpu baseline failed: %r" % (e,))
             out["cpu_baseline"] = {"error": repr(e)}
@@ -501,6 +503,61 @@ def cpu_baseline(np, si):
                       "%d runs, mean %.3f s per run" % (reps, dt),
             "single_thread": {"value": L * D * N / dt1, "unit": "elements/s", "cores": 1,
                               "sample": "batch row 0 of the same workload, %.2f s" % dt1}}
+
+def cpu_baseline_extras(np, si):
+    """The oracle on bounded samples of the extra workloads, all host
+    threads, each a few seconds at most: the backward (batch row 0 of the
+    B=8, L=2048 workload), the constant-decay forward (whole workload), the
+    streaming step (one block-step of 256 streams) and the whole-model decode
+    (one stream, 8 tokens; 256 streams, 2 tokens)."""
+    import oracle
+    from oracle import mamba_model as mm
+    ex = {}
+    cores = oracle.num_threads()
+    B, L, D, N = 8, 2048, 1536, 16
+
+    def timed(fn):
+        t0 = time.perf_counter()
+        fn()
+        return time.perf_counter() - t0
+
+    p = si.mamba_block(1, L, D, N, 4, workload=si.WL_FWDBWD, with_dy=True)
+    u, _ = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"])
+    dt = timed(lambda: oracle.scan_bwd(u, p["dt_raw"], p["A_log"], p["B"], p["C"], p["dy"], dt_bias=p["dt_bias"],
+                                       Dskip=p["Dskip"], z=p["z"]))
+    ex["backward_B8_L2048"] = {"value": L * D * N / dt, "unit": "elements/s", "cores": cores,
+                               "sample": "batch row 0 (1/8 of the workload), %.2f s" % dt}
+    c = si.mamba_block(B, L, D, N, 4, workload=si.WL_FWDBWD, const_decay=True)
+
+    def const_fwd():
+        uc, _ = oracle.conv1d_causal(c["x"], c["conv_w"], c["conv_b"], want_state=False)
+        oracle.scan_fwd(uc, None, c["A_log"], c["B"], c["C"], Dskip=c["Dskip"], z=c["z"], disc=oracle.DECAY_CONST)
+
+    dt = timed(const_fwd)
+    ex["forward_const_decay_B8_L2048_N16"] = {"value": B * L * D * N / dt, "unit": "elements/s", "cores": cores,
+                                              "sample": "the whole workload, %.2f s" % dt}
+    del c, p, u
+    r = np.random.default_rng(0)
+    S = 256
+    h = np.zeros((S, D, N))
+    cs = np.zeros((S, 3, D))
+    prm = si.stream_params(1, D, N, 4)
+    x, dtr, z = (r.standard_normal((S, D)) for _ in range(3))
+    Bm, Cm = (r.standard_normal((S, N)) for _ in range(2))
+    dt = timed(lambda: oracle.step(h, cs, x, dtr, Bm, Cm, prm["A_log"][0], z=z, conv_w=prm["conv_w"][0],
+                                   conv_b=prm["conv_b"][0], dt_bias=prm["dt_bias"][0], Dskip=prm["Dskip"][0]))
+    ex["streaming_step_one_block_256streams"] = {"value": S / dt, "unit": "stream-steps/s (one block)",
+                                                 "cores": cores, "sample": "one block-step, %.3f s" % dt}
+    mp = si.model_params(si.MAMBA_MINI)
+    for Sm, T in ((1, 8), (256, 2)):
+        hm, cm = mm.new_state(si.MAMBA_MINI, Sm)
+        tok = si.model_tokens(si.MAMBA_MINI, Sm, T)
+        dt = timed(lambda: [mm.decode_step(mp, tok[:, t], hm, cm) for t in range(T)])
+        ex["decode_mamba_mini_%dstream%s" % (Sm, "" if Sm == 1 else "s")] = {
+            "value": Sm * T / dt, "unit": "tokens/s", "cores": cores,
+            "sample": "%d token step(s), %.2f s" % (T, dt)}
+    return ex
+
 
 if __name__ == "__main__":
     main()
