@@ -75,29 +75,6 @@ struct LinArgs {
     int R, Ns;
 };
 
-// Loads of one reduction step (16 k) of a lane: 4 consecutive k of its A row
-// and of its W row; zeros outside the row range or past ke.
-template <bool VEC>
-__device__ __forceinline__ void lin_load(const float *Ap, const float *Wp, bool arow, bool wrow, int64_t kk,
-                                         int64_t ke, float4 &x, float4 &y) {
-    if constexpr (VEC) {
-        // K and lda are multiples of 4: a 16-byte piece is wholly in or out
-        const bool in = kk < ke;
-        x = (arow && in) ? *reinterpret_cast<const float4 *>(Ap + kk) : make_float4(0, 0, 0, 0);
-        y = (wrow && in) ? *reinterpret_cast<const float4 *>(Wp + kk) : make_float4(0, 0, 0, 0);
-    } else {
-        float xa[4], ya[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const bool in = kk + q < ke;
-            xa[q] = (arow && in) ? Ap[kk + q] : 0.0f;
-            ya[q] = (wrow && in) ? Wp[kk + q] : 0.0f;
-        }
-        x = make_float4(xa[0], xa[1], xa[2], xa[3]);
-        y = make_float4(ya[0], ya[1], ya[2], ya[3]);
-    }
-}
-
 // 4 consecutive values of a [K] vector from k (VEC: one 16-byte load), `dflt`
 // for a NULL vector and past ke.
 template <bool VEC>
@@ -113,22 +90,24 @@ __device__ __forceinline__ float4 vec_load(const float *p, int64_t k, int64_t ke
     }
 }
 
-// Workgroup = WN x WK wavefronts: WN column tiles of 16, each reduction split
-// in WK shares (summed through LDS in a fixed order).  Each wavefront keeps
-// U reduction steps of loads in flight.
-template <int EPI, int WN, int WK, bool VEC, bool LNA, bool EMBED>
+// Workgroup = WN x WK wavefronts.  A wavefront owns TN column tiles of 16
+// (one A load feeds TN products), the workgroup WN such groups, and each
+// reduction is split in WK shares (summed through LDS in a fixed order).
+// Each wavefront keeps U reduction steps of loads in flight.
+template <int EPI, int WN, int WK, int TN, bool VEC, bool LNA, bool EMBED>
 __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
     constexpr int U = 4;
-    __shared__ floatx4 red[WK > 1 ? WN * WK : 1][64];
-    __shared__ float4 red2[(WK > 1 && LNA) ? WN * WK : 1][64];
+    constexpr int NW = 16 * TN;                        // columns per wavefront
+    __shared__ floatx4 red[WK > 1 ? WN * WK : 1][TN][64];
+    __shared__ float4 red2[(WK > 1 && LNA) ? WN * WK : 1][TN][64];
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int wn = wv % WN, wk = wv / WN;
-    const int64_t ntn = (a.N + 16 * WN - 1) / (16 * WN);
+    const int64_t ntn = (a.N + NW * WN - 1) / (NW * WN);
     const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 16;
-    const int64_t n0 = (int64_t)(blockIdx.x % ntn) * (16 * WN) + wn * 16;
+    const int64_t n0 = (int64_t)(blockIdx.x % ntn) * (NW * WN) + wn * NW;
     const int li = lane & 15, g = lane >> 4;
-    const int64_t am = m0 + li, wr = n0 + li;
-    const bool arow = am < a.M, wrow = wr < a.N;
+    const int64_t am = m0 + li;
+    const bool arow = am < a.M;
     const float *Ap;
     bool bad = false;
     if constexpr (EMBED) {
@@ -138,7 +117,14 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
     } else {
         Ap = a.A + (arow ? am : 0) * a.lda;
     }
-    const float *Wp = a.W + (wrow ? wr : 0) * a.K;
+    const float *Wp[TN];
+    bool wrow[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) {
+        const int64_t wr = n0 + 16 * tn + li;
+        wrow[tn] = wr < a.N;
+        Wp[tn] = a.W + (wrow[tn] ? wr : 0) * a.K;
+    }
     // LayerNorm folded into the product (LNA).  With w, b the norm's weight
     // and bias: sum_k LN(x)_k W_nk = rs (P_n - mu c_n) + d_n, where
     // P_n = sum_k x_k (w_k W_nk) is the MFMA product with W scaled by w,
@@ -147,7 +133,9 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
     // the one-pass variance free of cancellation).  Every sum is accumulated
     // from the loads the product makes anyway, so the norm adds no pass over
     // memory.
-    float sh = 0.0f, s1 = 0.0f, s2 = 0.0f, cs = 0.0f, ds = 0.0f;
+    float sh = 0.0f, s1 = 0.0f, s2 = 0.0f, cs[TN], ds[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) cs[tn] = ds[tn] = 0.0f;
     if constexpr (LNA) {
         sh = arow ? Ap[0] : 0.0f;
         if constexpr (EMBED) {
@@ -173,13 +161,17 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
     const int64_t steps = (a.K + 15) / 16;
     const int64_t per = (steps + WK - 1) / WK;
     const int64_t kb = wk * per * 16, ke = min(a.K, (wk + 1) * per * 16);
-    floatx4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
+    floatx4 acc[TN];
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn) acc[tn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
     for (int64_t k0 = kb; k0 < ke; k0 += 16 * U) {
-        float4 xa[U], xw[U], lw[U], lb[U];
+        float4 xa[U], xw[U][TN], lw[U], lb[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const int64_t kk = k0 + 16 * j + 4 * g;
-            lin_load<VEC>(Ap, Wp, arow, wrow, kk, ke, xa[j], xw[j]);
+            xa[j] = vec_load<VEC>(arow ? Ap : nullptr, kk, ke, 0.0f);
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) xw[j][tn] = vec_load<VEC>(wrow[tn] ? Wp[tn] : nullptr, kk, ke, 0.0f);
             if constexpr (LNA) {
                 lw[j] = vec_load<VEC>(a.lnw, kk, ke, 1.0f);
                 lb[j] = vec_load<VEC>(a.lnb, kk, ke, 0.0f);
@@ -188,11 +180,8 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const float av[4] = {xa[j].x, xa[j].y, xa[j].z, xa[j].w};
-            float bv[4] = {xw[j].x, xw[j].y, xw[j].z, xw[j].w};
             if constexpr (LNA) {
                 const int64_t kk = k0 + 16 * j + 4 * g;
-                const float wq[4] = {lw[j].x, lw[j].y, lw[j].z, lw[j].w};
-                const float bq[4] = {lb[j].x, lb[j].y, lb[j].z, lb[j].w};
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     if (kk + q < ke) {
@@ -200,26 +189,45 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
                         s1 += t;
                         s2 = fmaf(t, t, s2);
                     }
-                    ds = fmaf(bq[q], bv[q], ds);
-                    bv[q] = bv[q] * wq[q];
-                    cs += bv[q];
                 }
             }
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc, 0, 0, 0);
+            for (int tn = 0; tn < TN; ++tn) {
+                float bv[4] = {xw[j][tn].x, xw[j][tn].y, xw[j][tn].z, xw[j][tn].w};
+                if constexpr (LNA) {
+                    const float wq[4] = {lw[j].x, lw[j].y, lw[j].z, lw[j].w};
+                    const float bq[4] = {lb[j].x, lb[j].y, lb[j].z, lb[j].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        ds[tn] = fmaf(bq[q], bv[q], ds[tn]);
+                        bv[q] = bv[q] * wq[q];
+                        cs[tn] += bv[q];
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    acc[tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc[tn], 0, 0, 0);
+            }
         }
     }
     if constexpr (WK > 1) {
-        red[wv][lane] = acc;
-        if constexpr (LNA) red2[wv][lane] = make_float4(s1, s2, cs, ds);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            red[wv][tn][lane] = acc[tn];
+            if constexpr (LNA) red2[wv][tn][lane] = make_float4(s1, s2, cs[tn], ds[tn]);
+        }
         __syncthreads();
         if (wk != 0) return;
 #pragma unroll
         for (int j = 1; j < WK; ++j) {
-            acc += red[wn + j * WN][lane];
-            if constexpr (LNA) {
-                const float4 o = red2[wn + j * WN][lane];
-                s1 += o.x; s2 += o.y; cs += o.z; ds += o.w;
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                acc[tn] += red[wn + j * WN][tn][lane];
+                if constexpr (LNA) {
+                    const float4 o = red2[wn + j * WN][tn][lane];
+                    if (tn == 0) { s1 += o.x; s2 += o.y; }
+                    cs[tn] += o.z; ds[tn] += o.w;
+                }
             }
         }
     }
@@ -228,8 +236,11 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
     if constexpr (LNA) {
         s1 += __shfl_xor(s1, 16, 64); s1 += __shfl_xor(s1, 32, 64);
         s2 += __shfl_xor(s2, 16, 64); s2 += __shfl_xor(s2, 32, 64);
-        cs += __shfl_xor(cs, 16, 64); cs += __shfl_xor(cs, 32, 64);
-        ds += __shfl_xor(ds, 16, 64); ds += __shfl_xor(ds, 32, 64);
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            cs[tn] += __shfl_xor(cs[tn], 16, 64); cs[tn] += __shfl_xor(cs[tn], 32, 64);
+            ds[tn] += __shfl_xor(ds[tn], 16, 64); ds[tn] += __shfl_xor(ds[tn], 32, 64);
+        }
         const float mk = s1 / (float)a.K;
         const float mu = bad ? NAN : sh + mk;
         const float rs = 1.0f / sqrtf(fmaxf(s2 / (float)a.K - mk * mk, 0.0f) + kLnEps);
@@ -240,77 +251,82 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
             rsr[r] = __shfl(rs, 4 * g + r, 64);
         }
     }
-    // lane holds rows m0 + 4g + r, column n0 + li
-    const int64_t n = n0 + li;
-    if (n >= a.N) return;
+    // lane holds rows m0 + 4g + r, column n0 + 16 tn + li
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int64_t m = m0 + 4 * g + r;
-        if (m >= a.M) break;
-        float v = acc[r];
-        if constexpr (LNA) v = rsr[r] * (v - mur[r] * cs) + ds;
-        if constexpr (EPI == EPI_STORE) {
-            a.C[m * a.ldc + n] = v;
-        } else if constexpr (EPI == EPI_RESID) {
-            a.C[m * a.ldc + n] += v;
-        } else if constexpr (EPI == EPI_XPROJ) {
-            if (n < a.R)
-                a.dtl[m * a.R + n] = v;
-            else if (n < a.R + a.Ns)
-                a.Bv[m * a.Ns + (n - a.R)] = v;
-            else
-                a.Cv[m * a.Ns + (n - a.R - a.Ns)] = v;
-        } else {   // EPI_INPROJ
-            const int64_t Di = a.Di;
-            if (n < Di) {
-                // causal conv over [history, xin]: bias, then taps oldest to
-                // newest; the history shifts by one input (this thread owns
-                // the (stream, channel) column)
-                const int W = a.Wc;
-                float cacc = a.cb ? a.cb[n] : 0.0f;
-                float *hp = a.hist + m * (int64_t)(W - 1) * Di + n;
-                for (int j = 0; j < W - 1; ++j) {
-                    const float hv = hp[j * Di];   // slot j is read before slot j is rewritten
-                    cacc = fmaf(a.cw[n * W + j], hv, cacc);
-                    if (j > 0) hp[(j - 1) * Di] = hv;
+    for (int tn = 0; tn < TN; ++tn) {
+        const int64_t n = n0 + 16 * tn + li;
+        if (n >= a.N) continue;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t m = m0 + 4 * g + r;
+            if (m >= a.M) break;
+            float v = acc[tn][r];
+            if constexpr (LNA) v = rsr[r] * (v - mur[r] * cs[tn]) + ds[tn];
+            if constexpr (EPI == EPI_STORE) {
+                a.C[m * a.ldc + n] = v;
+            } else if constexpr (EPI == EPI_RESID) {
+                a.C[m * a.ldc + n] += v;
+            } else if constexpr (EPI == EPI_XPROJ) {
+                if (n < a.R)
+                    a.dtl[m * a.R + n] = v;
+                else if (n < a.R + a.Ns)
+                    a.Bv[m * a.Ns + (n - a.R)] = v;
+                else
+                    a.Cv[m * a.Ns + (n - a.R - a.Ns)] = v;
+            } else {   // EPI_INPROJ
+                const int64_t Di = a.Di;
+                if (n < Di) {
+                    // causal conv over [history, xin]: bias, then taps oldest to
+                    // newest; the history shifts by one input (this thread owns
+                    // the (stream, channel) column)
+                    const int W = a.Wc;
+                    float cacc = a.cb ? a.cb[n] : 0.0f;
+                    float *hp = a.hist + m * (int64_t)(W - 1) * Di + n;
+                    for (int j = 0; j < W - 1; ++j) {
+                        const float hv = hp[j * Di];   // slot j is read before slot j is rewritten
+                        cacc = fmaf(a.cw[n * W + j], hv, cacc);
+                        if (j > 0) hp[(j - 1) * Di] = hv;
+                    }
+                    cacc = fmaf(a.cw[n * W + (W - 1)], v, cacc);
+                    if (W > 1) hp[(W - 2) * Di] = v;
+                    a.u[m * Di + n] = silu_f(cacc);
+                } else {
+                    a.z[m * Di + (n - Di)] = v;
                 }
-                cacc = fmaf(a.cw[n * W + (W - 1)], v, cacc);
-                if (W > 1) hp[(W - 2) * Di] = v;
-                a.u[m * Di + n] = silu_f(cacc);
-            } else {
-                a.z[m * Di + (n - Di)] = v;
             }
         }
     }
 }
 
-template <int EPI, int WN, int WK, bool LNA, bool EMBED>
+template <int EPI, int WN, int WK, int TN, bool LNA, bool EMBED>
 hipError_t launch_lin_cfg(const LinArgs &a, hipStream_t s) {
-    const int64_t blocks = ((a.M + 15) / 16) * ((a.N + 16 * WN - 1) / (16 * WN));
+    const int64_t blocks = ((a.M + 15) / 16) * ((a.N + 16 * TN * WN - 1) / (16 * TN * WN));
     if (blocks <= 0) return hipSuccess;
     const bool vec = (a.K % 4 == 0) && (a.lda % 4 == 0);
     const dim3 grid((unsigned)blocks), blk(64 * WN * WK);
     if (vec)
-        hipLaunchKernelGGL((linear_kernel<EPI, WN, WK, true, LNA, EMBED>), grid, blk, 0, s, a);
+        hipLaunchKernelGGL((linear_kernel<EPI, WN, WK, TN, true, LNA, EMBED>), grid, blk, 0, s, a);
     else
-        hipLaunchKernelGGL((linear_kernel<EPI, WN, WK, false, LNA, EMBED>), grid, blk, 0, s, a);
+        hipLaunchKernelGGL((linear_kernel<EPI, WN, WK, TN, false, LNA, EMBED>), grid, blk, 0, s, a);
     return hipGetLastError();
 }
 
-// Enough 16 x 16 tiles: four column tiles per workgroup.  Otherwise one
-// column tile per workgroup and the reduction split over up to 16
-// wavefronts (shares of at least 96), so that few-stream products stream
-// their weights from many CUs with several loads in flight per lane.
+// Plenty of 16 x 16 tiles (many streams): a wavefront takes two column tiles
+// and a workgroup four wavefronts side by side.  Otherwise one column tile
+// per workgroup and the reduction split over up to 16 wavefronts (shares of
+// at least 96), so that few-stream products stream their weights from many
+// CUs with several loads in flight per lane.
 template <int EPI, bool LNA = false, bool EMBED = false>
 hipError_t launch_lin(const LinArgs &a, hipStream_t s) {
     const int64_t tiles = ((a.M + 15) / 16) * ((a.N + 15) / 16);
-    if (tiles >= 1024) return launch_lin_cfg<EPI, 4, 1, LNA, EMBED>(a, s);
+    if (tiles >= 2048) return launch_lin_cfg<EPI, 4, 1, 2, LNA, EMBED>(a, s);
+    if (tiles >= 1024) return launch_lin_cfg<EPI, 4, 1, 1, LNA, EMBED>(a, s);
     const int64_t share = a.K / 96;
-    if (share >= 16) return launch_lin_cfg<EPI, 1, 16, LNA, EMBED>(a, s);
-    if (share >= 8) return launch_lin_cfg<EPI, 1, 8, LNA, EMBED>(a, s);
-    if (share >= 4) return launch_lin_cfg<EPI, 1, 4, LNA, EMBED>(a, s);
-    if (share >= 2) return launch_lin_cfg<EPI, 1, 2, LNA, EMBED>(a, s);
-    return launch_lin_cfg<EPI, 1, 1, LNA, EMBED>(a, s);
+    if (share >= 16) return launch_lin_cfg<EPI, 1, 16, 1, LNA, EMBED>(a, s);
+    if (share >= 8) return launch_lin_cfg<EPI, 1, 8, 1, LNA, EMBED>(a, s);
+    if (share >= 4) return launch_lin_cfg<EPI, 1, 4, 1, LNA, EMBED>(a, s);
+    if (share >= 2) return launch_lin_cfg<EPI, 1, 2, 1, LNA, EMBED>(a, s);
+    return launch_lin_cfg<EPI, 1, 1, 1, LNA, EMBED>(a, s);
 }
 
 struct ModelWs {

@@ -79,6 +79,22 @@ def test_model_decode_small(ssm, cfg, S):
     assert eh <= MODEL_TOL and ec <= MODEL_TOL, (eh, ec)
 
 
+EDGE_MODELS = [
+    dict(vocab=7, d_model=5, n_layers=2, d_inner=9, d_state=64, dt_rank=1, conv_width=1),   # no conv history
+    dict(vocab=300, d_model=130, n_layers=1, d_inner=200, d_state=17, dt_rank=33, conv_width=8),
+]
+
+
+@pytest.mark.parametrize("cfg", EDGE_MODELS, ids=["W1_N64_R1", "W8_N17_R33"])
+@pytest.mark.parametrize("S", [1, 33])
+def test_model_decode_edge_shapes(ssm, cfg, S):
+    """Edge shapes: conv width 1 (no history), 64 states, rank-1 step size,
+    widths that are not multiples of 4 (scalar loads), conv width 8."""
+    errs, eh, ec = _run(ssm, cfg, 14, S, 5)
+    assert max(errs) <= MODEL_TOL, errs
+    assert eh <= MODEL_TOL and ec <= MODEL_TOL, (eh, ec)
+
+
 def test_model_decode_mamba_mini_single_stream(ssm):
     """Mamba-mini (6 blocks, d 384, D_inner 1536, N 16, dt rank 24, conv 4,
     4096-token tied head), one stream, 16 tokens of decode."""
