@@ -100,6 +100,8 @@ def main():
                     help="untimed launches first; the GPU needs ~10 ms of work to reach steady clocks")
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle's CPU timing")
     ap.add_argument("--no-extra", action="store_true", help="time only the headline workload")
+    ap.add_argument("--no-model-decode", action="store_true",
+                    help="skip the whole-model decode extras (their many small launches make counter passes slow)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     args = ap.parse_args()
@@ -418,6 +420,8 @@ def bench_extras(torch, np, si, ssm, dev, args):
     del h, cs, toks, ys, prm
     torch.cuda.empty_cache()
 
+    if args.no_model_decode:
+        return ex
     # the whole Mamba-mini model (random-init weights), one token per stream
     # per step: embedding, 6 blocks (LayerNorm, in_proj + conv, x_proj,
     # dt_proj, the selective step, out_proj + residual), final LayerNorm and
