@@ -56,15 +56,20 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     IOT *Y = static_cast<IOT *>(a.y);
     const int64_t D = a.D, N = a.N, S = a.S;
     const int W = a.W;
-    const int64_t total = a.nblk * S * D * LPC;
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    // lanes past the end take the last unit's values and store nothing
-    const bool active = gid < total;
-    const int64_t gc = active ? gid : (total - 1);
-    const int q = (int)(gc % LPC);
-    const int64_t d = (gc / LPC) % D;
-    const int64_t s = (gc / (LPC * D)) % S;
-    const int64_t k = gc / (LPC * D * S);
+    // Workgroups walk the (block, stream) rows in order, bpr workgroups of
+    // 256 lanes per row of D*LPC lanes.  The row and the lane within it come
+    // from 32-bit divisions of workgroup-uniform values (once per wavefront);
+    // lanes past the row's end take its last channel's values and store
+    // nothing.
+    const uint32_t bpr = (uint32_t)((D * LPC + 255) / 256);
+    const uint32_t row = blockIdx.x / bpr;                  // k * S + s
+    const uint32_t rk = row / (uint32_t)S;
+    const int64_t k = rk, s = row - rk * (uint32_t)S;
+    const int64_t gl = (int64_t)(blockIdx.x - row * bpr) * 256 + threadIdx.x;
+    const bool active = gl < D * LPC;
+    const int64_t gc = active ? gl : (D * LPC - 1);
+    const int q = (int)(gc & (LPC - 1));
+    const int64_t d = gc / LPC;
     const int64_t sd = (k * S + s) * D + d;      // [nblk, S, D]
     const int64_t kd = k * D + d;                // [nblk, D]
     const int n0 = q * kSPL;
@@ -173,10 +178,15 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
 }
 
+// One run of workgroups per (block, stream) row: ceil(D*LPC / 256) each.
+template <int LPC>
+unsigned step_blocks(const StepArgs &a) {
+    return (unsigned)(a.nblk * a.S * ((a.D * LPC + 255) / 256));
+}
+
 template <typename IOT, typename HT, int LPC, int VL>
 hipError_t launch_g(const StepArgs &a, hipStream_t s) {
-    const int64_t threads = a.nblk * a.S * a.D * LPC;
-    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    const unsigned blocks = step_blocks<LPC>(a);
     const bool conv = a.W > 0;
 #define SSM_STEP_CASE(DI, CV, MW)                                                                        \
     if (a.disc == DI && conv == CV && (!CV || a.W <= MW)) {                                              \
@@ -209,14 +219,16 @@ hipError_t launch_io(const StepArgs &a, hipStream_t s) {
 hipError_t launch_step_dtproj(const StepArgs &a, hipStream_t s) {
     if (a.nblk * a.S * a.D == 0) return hipSuccess;
     if (a.bf16 || a.state_bf16 || a.disc != DISC_DB || a.W != 0) return hipErrorInvalidValue;
-    auto go = [&](auto kern, int lpc) {
-        const int64_t threads = a.nblk * a.S * a.D * lpc;
-        hipLaunchKernelGGL(kern, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, a);
-        return hipGetLastError();
-    };
-    if (a.N <= 16) return go(step_kernel<float, float, 4, 1, DISC_DB, false, 1, true>, 4);
-    if (a.N <= 32) return go(step_kernel<float, float, 8, 2, DISC_DB, false, 1, true>, 8);
-    return go(step_kernel<float, float, 16, 4, DISC_DB, false, 1, true>, 16);
+    if (a.N <= 16)
+        hipLaunchKernelGGL((step_kernel<float, float, 4, 1, DISC_DB, false, 1, true>), dim3(step_blocks<4>(a)),
+                           dim3(256), 0, s, a);
+    else if (a.N <= 32)
+        hipLaunchKernelGGL((step_kernel<float, float, 8, 2, DISC_DB, false, 1, true>), dim3(step_blocks<8>(a)),
+                           dim3(256), 0, s, a);
+    else
+        hipLaunchKernelGGL((step_kernel<float, float, 16, 4, DISC_DB, false, 1, true>), dim3(step_blocks<16>(a)),
+                           dim3(256), 0, s, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
