@@ -209,7 +209,7 @@ __device__ __forceinline__ void lds_read_k(const float *p, float (&o)[K]) {
 // One block = four wavefronts = 16 channels of one batch row and one time
 // chunk.  Wavefront w, lane-quad position j of channel ch owns states
 // n = (4w + j)*SPL .. +SPL-1.
-template <typename IOT, int SPL, int DISC, bool CONV, int MODE>
+template <typename IOT, int SPL, int DISC, bool CONV, int MODE, int CW = 0>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     constexpr int T = kTile;
     constexpr int NP = 16 * SPL;
@@ -318,14 +318,17 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     auto transform = [&](int nv) {
         float uu[kRows];
         if constexpr (CONV) {
-            float win[kRows + 7];
+            // taps right-aligned in 8 slots; with a known width only the
+            // last CW are nonzero (the zero taps add exactly nothing)
+            constexpr int K0 = CW > 0 ? 8 - CW : 0;
+            float win[kRows + 7 - K0];
 #pragma unroll
-            for (int i = 0; i < kRows + 7; ++i) win[i] = s_x[(rp * kRows + 1 + i) * kXS + tc];
+            for (int i = 0; i < kRows + 7 - K0; ++i) win[i] = s_x[(rp * kRows + 1 + K0 + i) * kXS + tc];
 #pragma unroll
             for (int i = 0; i < kRows; ++i) {
                 float acc = cb;
 #pragma unroll
-                for (int kk = 0; kk < 8; ++kk) acc = fmaf(wk[kk], win[i + kk], acc);
+                for (int kk = K0; kk < 8; ++kk) acc = fmaf(wk[kk], win[i + kk - K0], acc);
                 uu[i] = silu_f(acc);
             }
         } else {
@@ -555,8 +558,13 @@ template <typename IOT, int SPL, int DISC, bool CONV, int MODE>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int64_t blocks = (int64_t)p.groups * p.Kgrid * p.B;
     if (blocks <= 0) return hipSuccess;
-    hipLaunchKernelGGL((scan_fwd_kernel<IOT, SPL, DISC, CONV, MODE>),
-                       dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    // the 4-tap conv of the Mamba blocks gets its own instance
+    if (CONV && p.W == 4)
+        hipLaunchKernelGGL((scan_fwd_kernel<IOT, SPL, DISC, CONV, MODE, 4>),
+                           dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_fwd_kernel<IOT, SPL, DISC, CONV, MODE>),
+                           dim3((unsigned)blocks), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
