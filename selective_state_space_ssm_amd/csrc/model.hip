@@ -47,6 +47,7 @@ namespace {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLnEps = 1e-5f;
+constexpr int kMaxConvW = 8;   // widest conv the in_proj epilogue carries
 
 enum { EPI_STORE = 0, EPI_INPROJ = 1, EPI_XPROJ = 2, EPI_RESID = 3 };
 
@@ -103,8 +104,15 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     const int wn = wv % WN, wk = wv / WN;
     const int64_t ntn = (a.N + NW * WN - 1) / (NW * WN);
-    const int64_t m0 = (int64_t)(blockIdx.x / ntn) * 16;
-    const int64_t n0 = (int64_t)(blockIdx.x % ntn) * (NW * WN) + wn * NW;
+    // XCD-aware order: the hardware deals workgroups round-robin over the 8
+    // XCDs; after the remap each XCD holds a contiguous run of logical
+    // workgroups, taken column-tile-major, so an XCD streams only its share
+    // of the weights through its own L2 (every XCD reads the small A)
+    const int64_t mtn = (a.M + 15) / 16;
+    const int64_t lb = xcd_remap((int64_t)blockIdx.x, (int64_t)gridDim.x, 8);
+    const int64_t ntile = lb / mtn;
+    const int64_t m0 = (lb % mtn) * 16;
+    const int64_t n0 = ntile * (NW * WN) + wn * NW;
     const int li = lane & 15, g = lane >> 4;
     const int64_t am = m0 + li;
     const bool arow = am < a.M;
@@ -142,7 +150,7 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
             // the residual stream starts as the embedding row; the workgroups
             // of one row tile each copy a slice of its 16 rows (column tile ct
             // takes k in [ct*ch, (ct+1)*ch)), wavefront 0, a lane per value
-            const int64_t ct = blockIdx.x % ntn, ch = (a.K + ntn - 1) / ntn;
+            const int64_t ct = ntile, ch = (a.K + ntn - 1) / ntn;
             const int64_t k0 = ct * ch, k1 = min(a.K, k0 + ch);
             if (wv == 0) {
                 for (int64_t e = lane; e < 16 * (k1 - k0); e += 64) {
@@ -251,47 +259,101 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
             rsr[r] = __shfl(rs, 4 * g + r, 64);
         }
     }
-    // lane holds rows m0 + 4g + r, column n0 + 16 tn + li
+    // lane holds rows m0 + 4g + r, column n0 + 16 tn + li.  Everything the
+    // epilogue reads (the residual, the conv history and taps) is loaded for
+    // all of the lane's outputs before the first store: the compiler cannot
+    // move a load of one output's column above another output's store.
+    float v[TN][4];
+    bool ok[TN][4];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
         const int64_t n = n0 + 16 * tn + li;
-        if (n >= a.N) continue;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t m = m0 + 4 * g + r;
-            if (m >= a.M) break;
-            float v = acc[tn][r];
-            if constexpr (LNA) v = rsr[r] * (v - mur[r] * cs[tn]) + ds[tn];
-            if constexpr (EPI == EPI_STORE) {
-                a.C[m * a.ldc + n] = v;
-            } else if constexpr (EPI == EPI_RESID) {
-                a.C[m * a.ldc + n] += v;
-            } else if constexpr (EPI == EPI_XPROJ) {
-                if (n < a.R)
-                    a.dtl[m * a.R + n] = v;
-                else if (n < a.R + a.Ns)
-                    a.Bv[m * a.Ns + (n - a.R)] = v;
-                else
-                    a.Cv[m * a.Ns + (n - a.R - a.Ns)] = v;
-            } else {   // EPI_INPROJ
-                const int64_t Di = a.Di;
+            ok[tn][r] = n < a.N && m0 + 4 * g + r < a.M;
+            v[tn][r] = acc[tn][r];
+            if constexpr (LNA) v[tn][r] = rsr[r] * (v[tn][r] - mur[r] * cs[tn]) + ds[tn];
+        }
+    }
+    if constexpr (EPI == EPI_RESID) {
+        float old[TN][4];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                old[tn][r] = ok[tn][r] ? a.C[(m0 + 4 * g + r) * a.ldc + n0 + 16 * tn + li] : 0.0f;
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (ok[tn][r]) a.C[(m0 + 4 * g + r) * a.ldc + n0 + 16 * tn + li] = old[tn][r] + v[tn][r];
+    } else if constexpr (EPI == EPI_INPROJ) {
+        // causal conv over [history, xin] for the xin half: bias, then taps
+        // oldest to newest; the history shifts by one input (this thread
+        // owns the (stream, channel) column); the z half is stored as is
+        constexpr int MH = kMaxConvW - 1;
+        const int64_t Di = a.Di;
+        const int W = a.Wc;
+        float hv[TN][4][MH], cwv[TN][kMaxConvW], cbv[TN];
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int64_t n = n0 + 16 * tn + li;
+            const bool xin = n < Di && n < a.N;
+#pragma unroll
+            for (int j = 0; j < kMaxConvW; ++j) cwv[tn][j] = (xin && j < W) ? a.cw[n * W + j] : 0.0f;
+            cbv[tn] = (xin && a.cb) ? a.cb[n] : 0.0f;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float *hp = a.hist + (m0 + 4 * g + r) * (int64_t)(W - 1) * Di + n;
+#pragma unroll
+                for (int j = 0; j < MH; ++j) hv[tn][r][j] = (xin && ok[tn][r] && j < W - 1) ? hp[j * Di] : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int64_t n = n0 + 16 * tn + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (!ok[tn][r]) continue;
+                const int64_t m = m0 + 4 * g + r;
                 if (n < Di) {
-                    // causal conv over [history, xin]: bias, then taps oldest to
-                    // newest; the history shifts by one input (this thread owns
-                    // the (stream, channel) column)
-                    const int W = a.Wc;
-                    float cacc = a.cb ? a.cb[n] : 0.0f;
+                    float cacc = cbv[tn];
+#pragma unroll
+                    for (int j = 0; j < MH; ++j)
+                        if (j < W - 1) cacc = fmaf(cwv[tn][j], hv[tn][r][j], cacc);
+                    float cwl = cwv[tn][0];
+#pragma unroll
+                    for (int j = 1; j < kMaxConvW; ++j)
+                        if (j == W - 1) cwl = cwv[tn][j];
+                    cacc = fmaf(cwl, v[tn][r], cacc);
                     float *hp = a.hist + m * (int64_t)(W - 1) * Di + n;
-                    for (int j = 0; j < W - 1; ++j) {
-                        const float hv = hp[j * Di];   // slot j is read before slot j is rewritten
-                        cacc = fmaf(a.cw[n * W + j], hv, cacc);
-                        if (j > 0) hp[(j - 1) * Di] = hv;
-                    }
-                    cacc = fmaf(a.cw[n * W + (W - 1)], v, cacc);
-                    if (W > 1) hp[(W - 2) * Di] = v;
+#pragma unroll
+                    for (int j = 0; j + 1 < MH; ++j)
+                        if (j + 1 < W - 1) hp[j * Di] = hv[tn][r][j + 1];
+                    if (W > 1) hp[(W - 2) * Di] = v[tn][r];
                     a.u[m * Di + n] = silu_f(cacc);
                 } else {
-                    a.z[m * Di + (n - Di)] = v;
+                    a.z[m * Di + (n - Di)] = v[tn][r];
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+            const int64_t n = n0 + 16 * tn + li;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if (!ok[tn][r]) continue;
+                const int64_t m = m0 + 4 * g + r;
+                if constexpr (EPI == EPI_STORE) {
+                    a.C[m * a.ldc + n] = v[tn][r];
+                } else {   // EPI_XPROJ
+                    if (n < a.R)
+                        a.dtl[m * a.R + n] = v[tn][r];
+                    else if (n < a.R + a.Ns)
+                        a.Bv[m * a.Ns + (n - a.R)] = v[tn][r];
+                    else
+                        a.Cv[m * a.Ns + (n - a.R - a.Ns)] = v[tn][r];
                 }
             }
         }
