@@ -94,10 +94,12 @@ __device__ __forceinline__ float4 vec_load(const float *p, int64_t k, int64_t ke
 // Workgroup = WN x WK wavefronts.  A wavefront owns TN column tiles of 16
 // (one A load feeds TN products), the workgroup WN such groups, and each
 // reduction is split in WK shares (summed through LDS in a fixed order).
-// Each wavefront keeps U reduction steps of loads in flight.
+// The reduction runs in groups of U steps held in two register sets: the
+// loads of the next group are issued before the products of the current one,
+// so each wavefront has 2U steps of loads in flight.
 template <int EPI, int WN, int WK, int TN, bool VEC, bool LNA, bool EMBED>
 __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
-    constexpr int U = 4;
+    constexpr int U = 2;
     constexpr int NW = 16 * TN;                        // columns per wavefront
     __shared__ floatx4 red[WK > 1 ? WN * WK : 1][TN][64];
     __shared__ float4 red2[(WK > 1 && LNA) ? WN * WK : 1][TN][64];
@@ -172,22 +174,26 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
     floatx4 acc[TN];
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) acc[tn] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    for (int64_t k0 = kb; k0 < ke; k0 += 16 * U) {
+    struct Frag {
         float4 xa[U], xw[U][TN], lw[U], lb[U];
+    };
+    auto load = [&](Frag &f, int64_t k0) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             const int64_t kk = k0 + 16 * j + 4 * g;
-            xa[j] = vec_load<VEC>(arow ? Ap : nullptr, kk, ke, 0.0f);
+            f.xa[j] = vec_load<VEC>(arow ? Ap : nullptr, kk, ke, 0.0f);
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) xw[j][tn] = vec_load<VEC>(wrow[tn] ? Wp[tn] : nullptr, kk, ke, 0.0f);
+            for (int tn = 0; tn < TN; ++tn) f.xw[j][tn] = vec_load<VEC>(wrow[tn] ? Wp[tn] : nullptr, kk, ke, 0.0f);
             if constexpr (LNA) {
-                lw[j] = vec_load<VEC>(a.lnw, kk, ke, 1.0f);
-                lb[j] = vec_load<VEC>(a.lnb, kk, ke, 0.0f);
+                f.lw[j] = vec_load<VEC>(a.lnw, kk, ke, 1.0f);
+                f.lb[j] = vec_load<VEC>(a.lnb, kk, ke, 0.0f);
             }
         }
+    };
+    auto comp = [&](const Frag &f, int64_t k0) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const float av[4] = {xa[j].x, xa[j].y, xa[j].z, xa[j].w};
+            const float av[4] = {f.xa[j].x, f.xa[j].y, f.xa[j].z, f.xa[j].w};
             if constexpr (LNA) {
                 const int64_t kk = k0 + 16 * j + 4 * g;
 #pragma unroll
@@ -201,10 +207,10 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
             }
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
-                float bv[4] = {xw[j][tn].x, xw[j][tn].y, xw[j][tn].z, xw[j][tn].w};
+                float bv[4] = {f.xw[j][tn].x, f.xw[j][tn].y, f.xw[j][tn].z, f.xw[j][tn].w};
                 if constexpr (LNA) {
-                    const float wq[4] = {lw[j].x, lw[j].y, lw[j].z, lw[j].w};
-                    const float bq[4] = {lb[j].x, lb[j].y, lb[j].z, lb[j].w};
+                    const float wq[4] = {f.lw[j].x, f.lw[j].y, f.lw[j].z, f.lw[j].w};
+                    const float bq[4] = {f.lb[j].x, f.lb[j].y, f.lb[j].z, f.lb[j].w};
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         ds[tn] = fmaf(bq[q], bv[q], ds[tn]);
@@ -217,6 +223,19 @@ __global__ __launch_bounds__(64 * WN * WK) void linear_kernel(LinArgs a) {
                     acc[tn] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[q], bv[q], acc[tn], 0, 0, 0);
             }
         }
+    };
+    Frag f0, f1;
+    int64_t k0 = kb;
+    if (k0 < ke) load(f0, k0);
+    while (k0 < ke) {
+        const int64_t k1 = k0 + 16 * U;
+        if (k1 < ke) load(f1, k1);
+        comp(f0, k0);
+        if (k1 >= ke) break;
+        const int64_t k2 = k1 + 16 * U;
+        if (k2 < ke) load(f0, k2);
+        comp(f1, k1);
+        k0 = k2;
     }
     if constexpr (WK > 1) {
 #pragma unroll
