@@ -7,8 +7,8 @@
 //
 // Work decomposition.  A block of four wavefronts owns 16 channels of one
 // batch row and one time chunk; wavefront w keeps states 4w .. 4w+3 of every
-// channel (one state per lane at N = 16, four lanes per channel), so config
-// shapes with B*D/16 = 768 blocks put three wavefronts on every SIMD.
+// channel (one state per lane at N = 16), so shapes with B*D/16 = 768 blocks
+// put three wavefronts on every SIMD.
 // Tokens are processed in tiles of 64:
 //  - fetch: the next tile's x, dt_raw, z and its B, C rows are loaded into
 //    registers while the current tile is scanned (one tile of prefetch);
@@ -19,8 +19,10 @@
 //    dt*u, the gate SiLU(z) and Dskip*u into LDS;
 //  - scan: per token a lane reads its channel's (dt, dt*u) and its B, C
 //    values from LDS and updates its state with one exp2; the readout
-//    <h, C> is summed in the lane quad with DPP and across the four
-//    wavefronts through LDS, in the fixed order ((w0 + w1) + (w2 + w3)).
+//    <h, C> is summed over a channel's four lanes of the wavefront (four
+//    16-lane rows, with the gfx950 row swaps v_permlane16/32_swap; for the
+//    constant decay a lane quad, with DPP) and across the four wavefronts
+//    through LDS, both in the order ((0 + 1) + (2 + 3)).
 // The recurrence itself stays strictly sequential in time inside a chunk.
 //
 // Decay source ("the s6 cell", section "one cell, two architectures": one
@@ -172,6 +174,29 @@ __device__ __forceinline__ void store_bc(const RawTile<IOT, NP> &r, float *sB, f
     }
 }
 
+// Sums over the four 16-lane rows of a wavefront, with the gfx950 row swaps:
+// v_permlane16_swap(x, y) returns the rows (x0, y0, x2, y2) and
+// (x1, y1, x3, y3), v_permlane32_swap(x, y) the rows (x0, x1, y0, y1) and
+// (x2, x3, y2, y3).  Both sums associate as ((row0 + row1) + (row2 + row3)).
+__device__ __forceinline__ void swap16(float x, float y, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float y, float &a, float &b) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+}
+// p[i] is this lane's partial for token i; row k receives the sum over the
+// four rows of p[k] (for the lane's position in the row).
+__device__ __forceinline__ float rows_transpose_sum(const float (&p)[4]) {
+    float a0, a1, b0, b1, c0, c1;
+    swap16(p[0], p[1], a0, a1);   // rows: p0.r0 p1.r0 p0.r2 p1.r2 | p0.r1 p1.r1 p0.r3 p1.r3
+    swap16(p[2], p[3], b0, b1);
+    swap32(a0 + a1, b0 + b1, c0, c1);
+    return c0 + c1;
+}
 // Quad transpose-reduce: lane j of each lane quad holds partial sums p[i]
 // for four consecutive tokens; on return lane j holds the quad's sum for
 // token j, associated as ((lane0 + lane1) + (lane2 + lane3)).
@@ -187,6 +212,13 @@ __device__ __forceinline__ float quad_transpose_sum(const float (&p)[4], int j) 
     const float mine = high ? v[1] : v[0];
     const float send = high ? v[0] : v[1];
     return mine + dpp_f<kDppQuadSwap2>(send);
+}
+// Every row receives the sum over the four rows.
+__device__ __forceinline__ float rows_sum(float v) {
+    float a, b, c, e;
+    swap16(v, v, a, b);
+    swap32(a + b, a + b, c, e);
+    return c + e;
 }
 
 template <int K>
@@ -207,8 +239,10 @@ __device__ __forceinline__ void lds_read_k(const float *p, float (&o)[K]) {
 }
 
 // One block = four wavefronts = 16 channels of one batch row and one time
-// chunk.  Wavefront w, lane-quad position j of channel ch owns states
-// n = (4w + j)*SPL .. +SPL-1.
+// chunk.  In wavefront w, lane ch + 16 j (row j, position ch) owns states
+// n = (4w + j)*SPL .. +SPL-1 of channel ch.  The constant decay, whose scan
+// has no exp to hide the row swaps' latency behind, keeps the four lanes of
+// a channel in a quad instead (lane 4 ch + j) and sums them with DPP.
 template <typename IOT, int SPL, int DISC, bool CONV, int MODE, int CW = 0>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     constexpr int T = kTile;
@@ -248,7 +282,9 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
 
     // scan role
     const int wv = tid >> 6, lane = tid & 63;
-    const int ch = lane >> 2, j = lane & 3;
+    constexpr bool kRowsOfStates = DISC != DISC_CONST;
+    const int ch = kRowsOfStates ? (lane & 15) : (lane >> 2);
+    const int j = kRowsOfStates ? (lane >> 4) : (lane & 3);
     const int64_t d = d0 + ch;
     const bool dvalid = d < D;
     const int64_t dc = dvalid ? d : (D - 1);
@@ -346,15 +382,16 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
         (void)nv;
     };
 
-    auto stage = [&](int it) {
-        const int64_t ts = t0 + (int64_t)it * T;
-        const int nv = (int)min((int64_t)T, t1 - ts);
+    auto stage_x = [&]() {
         if constexpr (CONV) {
 #pragma unroll
             for (int i = 0; i < kRows; ++i) s_x[(8 + rp * kRows + i) * kXS + tc] = raw.f(raw.x[i]);
         }
+    };
+    auto stage = [&](int it) {
+        const int64_t ts = t0 + (int64_t)it * T;
+        const int nv = (int)min((int64_t)T, t1 - ts);
         store_bc<IOT, NP, FINAL>(raw, s_B, s_C, tid, N);
-        __syncthreads();
         transform(nv);
         __syncthreads();
     };
@@ -387,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             if constexpr (FINAL) part = fmaf(s_C[(n0 + s2) * kTS + t], h[s2], part);
         }
         if constexpr (FINAL) {
-            s_yp[wv][ch][t] = group_sum<4>(part);   // all lanes of the quad write the same value
+            s_yp[wv][ch][t] = kRowsOfStates ? rows_sum(part) : group_sum<4>(part);   // every lane of the channel writes it
         } else {
             ssum += dl;
         }
@@ -425,7 +462,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             }
         }
         if constexpr (FINAL) {
-            s_yp[wv][ch][t + j] = quad_transpose_sum(part, j);
+            s_yp[wv][ch][t + j] = kRowsOfStates ? rows_transpose_sum(part) : quad_transpose_sum(part, j);
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) ssum += dl[i];
@@ -441,9 +478,15 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
                 for (int i = 0; i < 8; ++i) s_x[i * kXS + tc] = x_before(t0 - 8 + i);
             }
         }
+        stage_x();
+        __syncthreads();
         stage(0);
         if (ntiles > 1) fetch(1);
     }
+    // Two barriers per tile.  The first ends the scan of tile it (its readout
+    // partials are complete) and publishes the next tile's raw conv rows,
+    // written after the scan; the second publishes the next tile's B, C and
+    // transformed rows, written after the readout.
     for (int it = 0; it < ntiles; ++it) {
         const int64_t ts = t0 + (int64_t)it * T;
         const int nv = (int)min((int64_t)T, t1 - ts);
@@ -454,6 +497,19 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             int t = 0;
             for (; t + 4 <= nv; t += 4) scan_group(t);
             for (; t < nv; ++t) scan_step(t);
+        }
+        if (it + 1 < ntiles) {
+            if constexpr (CONV) {
+                // the last 8 rows become the next tile's history rows; each
+                // thread moves the rows it staged itself (no other thread
+                // touches them before the next barrier)
+                if (rp >= kHaloRp) {
+#pragma unroll
+                    for (int i = 0; i < kRows; ++i)
+                        s_x[(rp * kRows + i - (T - 8)) * kXS + tc] = s_x[(8 + rp * kRows + i) * kXS + tc];
+                }
+            }
+            stage_x();
         }
         __syncthreads();
         // readout: ((w0 + w1) + (w2 + w3)) + Dskip*u, then the gate
@@ -483,16 +539,6 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             }
         };
         if (it + 1 < ntiles) {
-            if constexpr (CONV) {
-                // the last 8 rows become the next tile's history rows; each
-                // thread moves the rows it staged itself (no other thread
-                // touches them before the next barrier)
-                if (rp >= kHaloRp) {
-#pragma unroll
-                    for (int i = 0; i < kRows; ++i)
-                        s_x[(rp * kRows + i - (T - 8)) * kXS + tc] = s_x[(8 + rp * kRows + i) * kXS + tc];
-                }
-            }
             stage(it + 1);
             if (it + 2 < ntiles) fetch(it + 2);
             store_y();
