@@ -392,17 +392,23 @@ hipError_t launch_lin_cfg(const LinArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Plenty of 16 x 16 tiles (many streams): a wavefront takes two column tiles
-// and a workgroup four wavefronts side by side.  Otherwise one column tile
-// per workgroup and the reduction split over up to 16 wavefronts (shares of
-// at least 96), so that few-stream products stream their weights from many
-// CUs with several loads in flight per lane.
+// Launch shape by the number of 16 x 16 output tiles (chosen by a sweep of
+// the Mamba-mini products at 1 and 256 streams):
+//  - plenty of tiles (in_proj and the head at 256 streams): two column
+//    tiles per wavefront, two wavefronts side by side, the reduction split
+//    in two;
+//  - a few hundred tiles over a long reduction (out_proj at 256 streams):
+//    two column tiles per wavefront, the reduction split over 8;
+//  - otherwise one column tile per workgroup and the reduction split over up
+//    to 16 wavefronts (shares of at least 24), so that few-stream products
+//    stream their weights from many CUs with several loads in flight.
 template <int EPI, bool LNA = false, bool EMBED = false>
 hipError_t launch_lin(const LinArgs &a, hipStream_t s) {
     const int64_t tiles = ((a.M + 15) / 16) * ((a.N + 15) / 16);
-    if (tiles >= 2048) return launch_lin_cfg<EPI, 4, 1, 2, LNA, EMBED>(a, s);
+    if (tiles >= 2048) return launch_lin_cfg<EPI, 2, 2, 2, LNA, EMBED>(a, s);
     if (tiles >= 1024) return launch_lin_cfg<EPI, 4, 1, 1, LNA, EMBED>(a, s);
-    const int64_t share = a.K / 96;
+    if (tiles >= 256 && a.K >= 768) return launch_lin_cfg<EPI, 1, 8, 2, LNA, EMBED>(a, s);
+    const int64_t share = a.K / 24;
     if (share >= 16) return launch_lin_cfg<EPI, 1, 16, 1, LNA, EMBED>(a, s);
     if (share >= 8) return launch_lin_cfg<EPI, 1, 8, 1, LNA, EMBED>(a, s);
     if (share >= 4) return launch_lin_cfg<EPI, 1, 4, 1, LNA, EMBED>(a, s);
