@@ -107,7 +107,7 @@ const char *ssm_status_string(ssm_status s) {
         case SSM_OK: return "success";
         case SSM_ERR_NULL_ARG: return "a required pointer is NULL";
         case SSM_ERR_BAD_SHAPE: return "a size is out of range or inconsistent";
-        case SSM_ERR_UNSUPPORTED: return "request not supported by this build";
+        case SSM_ERR_UNSUPPORTED: return "request not supported by this library";
         case SSM_ERR_WORKSPACE: return "workspace missing or smaller than the queried size";
         case SSM_ERR_ALIGNMENT: return "a tensor does not start on a 16-byte boundary";
         case SSM_ERR_ALIAS: return "buffers overlap in a way the call does not allow";
