@@ -111,6 +111,16 @@ def test_model_decode_mamba_mini_256_streams(ssm):
     assert eh <= MODEL_TOL and ec <= MODEL_TOL, (eh, ec)
 
 
+def test_model_decode_mamba_mini_96_streams(ssm):
+    """Mamba-mini at 96 streams: in_proj (1152 output tiles of 16 x 16) and
+    the head (1536) take the launch shape for 1024-2047 tiles, which neither
+    the 1-stream nor the 256-stream decode reaches; 3 tokens, every stream
+    compared."""
+    errs, eh, ec = _run(ssm, si.MAMBA_MINI, 2, 96, 3)
+    assert max(errs) <= MODEL_TOL, errs
+    assert eh <= MODEL_TOL and ec <= MODEL_TOL, (eh, ec)
+
+
 def test_model_bad_token_poisons_only_its_stream(ssm):
     """A token outside the vocabulary gives NaN logits and state for its own
     stream; the other streams decode normally."""
