@@ -283,7 +283,7 @@ def _step_oracle_loop(p, steps, disc=DB, gate=True, state_bf16=False):
 
 
 @pytest.mark.parametrize("disc", [DB, ZOH])
-@pytest.mark.parametrize("S,D,N,W", [(4, 40, 16, 4), (3, 8, 3, 3), (2, 16, 33, 2), (5, 24, 16, 1)])
+@pytest.mark.parametrize("S,D,N,W", [(4, 40, 16, 4), (3, 8, 3, 3), (2, 16, 33, 2), (5, 24, 16, 1), (3, 20, 24, 4)])
 def test_step_parity(ssm, disc, S, D, N, W):
     """Token-by-token streaming with one block against the oracle's step."""
     p = _rand(14, S, 12, D, N, W)
@@ -387,7 +387,8 @@ def test_step_bf16(ssm):
 
 
 @pytest.mark.parametrize("S,D,N,W,io", [(4, 40, 16, 4, torch.float32), (2, 16, 33, 2, torch.float32),
-                                        (3, 24, 64, 4, torch.float32), (4, 32, 16, 4, torch.bfloat16)])
+                                        (3, 24, 64, 4, torch.float32), (4, 32, 16, 4, torch.bfloat16),
+                                        (2, 20, 24, 3, torch.float32)])
 @pytest.mark.parametrize("disc", [DB, ZOH])
 def test_step_bf16_state(ssm, S, D, N, W, io, disc):
     """Streaming with the state stored in bf16 (updated in float32, rounded
