@@ -69,7 +69,8 @@ extern "C" {
 typedef int32_t ssm_status;
 #define SSM_OK 0
 #define SSM_ERR_NULL_ARG 1     /* a required pointer is NULL */
-#define SSM_ERR_BAD_SHAPE 2    /* a size is out of range or inconsistent */
+#define SSM_ERR_BAD_SHAPE 2    /* a size is out of range or inconsistent, or needs a launch grid
+                                  above 2^31 - 1 workgroups */
 #define SSM_ERR_UNSUPPORTED 3  /* a valid request the library does not implement */
 #define SSM_ERR_WORKSPACE 4    /* workspace NULL or smaller than the queried size */
 #define SSM_ERR_ALIGNMENT 5    /* a tensor does not start on a 16-byte boundary */

@@ -35,6 +35,17 @@ bool elems(std::initializer_list<int64_t> dims, int64_t *out) {
     return true;
 }
 
+// The largest launch grid (in workgroups, or 256-thread groups) any kernel of
+// the library takes; shapes that would need more are rejected with
+// SSM_ERR_BAD_SHAPE before any HIP call (kernels index rows and workgroups in
+// 32 bits).
+constexpr int64_t kMaxGrid = 0x7fffffff;
+bool grid_ok(std::initializer_list<int64_t> dims) {
+    int64_t n;
+    return elems(dims, &n) && n <= kMaxGrid;
+}
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
 struct Range {
     const void *p;
     int64_t bytes;
@@ -127,6 +138,7 @@ ssm_status conv1d_causal(const ssm_conv_desc *desc, const void *x, const float *
     const int64_t B = desc->batch, L = desc->seqlen, D = desc->dim, W = desc->width;
     int64_t nx, nst;
     if (!elems({B, L, D}, &nx) || !elems({B, W - 1, D}, &nst)) return SSM_ERR_BAD_SHAPE;
+    if (!grid_ok({B, std::max<int64_t>(L, 1), cdiv(D, 256)})) return SSM_ERR_BAD_SHAPE;
     if (!w || (L > 0 && (!x || !y))) return SSM_ERR_NULL_ARG;
     for (const void *p : {(const void *)x, (const void *)w, (const void *)b, (const void *)state_in,
                           (const void *)state_out, (const void *)y})
@@ -171,6 +183,10 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
                           (const void *)workspace})
         if (!aligned16(p)) return SSM_ERR_ALIGNMENT;
     const int64_t chunk = resolve_chunk(desc);
+    {
+        const int64_t K = cdiv(std::max<int64_t>(L, 1), chunk);   // chunks along time
+        if (!grid_ok({Bn, cdiv(D, 16), K}) || !grid_ok({Bn, cdiv(D * N, 256)})) return SSM_ERR_BAD_SHAPE;
+    }
     const size_t need = ssm::scan_fwd_workspace_bytes(Bn, L, D, N, W, chunk);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
     const int64_t es = io_size(desc->io_dtype);
@@ -240,6 +256,12 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
                           (const void *)dconv_state_in, (const void *)workspace})
         if (!aligned16(p)) return SSM_ERR_ALIGNMENT;
     const int64_t chunk = ssm::scan_bwd_chunk(Bn, L, D, N, desc->chunk_len);
+    {
+        const int64_t KC = cdiv(std::max<int64_t>(L, 1), chunk);   // chunks along time
+        if (!grid_ok({Bn, cdiv(D, 48), KC}) || !grid_ok({Bn, cdiv(std::max<int64_t>(L, 1) * N, 256)}) ||
+            !grid_ok({Bn, KC, cdiv(8 * D, 256)}) || !grid_ok({Bn, cdiv(D * N, 256)}))
+            return SSM_ERR_BAD_SHAPE;
+    }
     const size_t need = ssm::scan_bwd_workspace_bytes(Bn, L, D, N, chunk);
     if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
     const int64_t es = io_size(desc->io_dtype);
@@ -301,6 +323,7 @@ ssm_status ssm_step(const ssm_step_desc *desc, void *h, float *conv_state, const
     if (!elems({K, S, D, N}, &nh) || !elems({K, S, D}, &nsd) || !elems({K, S, N}, &nsn) ||
         !elems({K, S, (int64_t)(W > 0 ? W - 1 : 0), D}, &nst))
         return SSM_ERR_BAD_SHAPE;
+    if (!grid_ok({K, S, cdiv(D * 16, 256)})) return SSM_ERR_BAD_SHAPE;
     const bool live = has_step_size(desc->disc);
     if (!live) dt_raw = nullptr, dt_bias = nullptr;   // not read
     if (!h || !x || (live && !dt_raw) || !B || !C || !A_log || !y || (W > 0 && !conv_w) ||
@@ -353,6 +376,9 @@ ssm_status check_model_desc(const ssm_model_desc *d) {
         !elems({(int64_t)d->vocab, d->d_model}, &n) || !elems({2 * Di, d->d_model}, &n) ||
         !elems({(int64_t)d->dt_rank + 2 * d->d_state, Di}, &n))
         return SSM_ERR_BAD_SHAPE;
+    const int64_t widest = std::max<int64_t>({2 * Di, (int64_t)d->vocab, (int64_t)d->d_model,
+                                              (int64_t)d->dt_rank + 2 * d->d_state});
+    if (!grid_ok({cdiv(S, 16), cdiv(widest, 16)}) || !grid_ok({S, cdiv(Di * 16, 256)})) return SSM_ERR_BAD_SHAPE;
     return SSM_OK;
 }
 

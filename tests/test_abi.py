@@ -215,6 +215,23 @@ def test_step_validation(ssm):
     assert L.ssm_step(ctypes.byref(good), *p4, None) == ssm.SSM_ERR_ALIGNMENT
 
 
+def test_launch_grid_limit(ssm):
+    """Shapes whose launch grid would pass 2^31 - 1 workgroups are rejected
+    before any HIP call: 2^32 streams of one channel and one state (a state of
+    16 GB, which fits an MI355X), a conv over 2^40 rows, a forward split into
+    one-token chunks over 2^40 tokens."""
+    L = ssm.lib()
+    ptrs = [_addr(i) for i in range(13)]
+    big = ssm.ssm_step_desc(1, 2 ** 32, 1, 1, 0, 0, 0, 0)
+    assert L.ssm_step(ctypes.byref(big), *ptrs, None) == ssm.SSM_ERR_BAD_SHAPE
+    ok = ssm.ssm_step_desc(1, 2 ** 20, 1, 1, 0, 0, 0, 0)
+    assert L.ssm_step(ctypes.byref(ok), *ptrs, None) != ssm.SSM_ERR_BAD_SHAPE
+    conv = ssm.ssm_conv_desc(1, 2 ** 40, 1, 4, 1, 0, 0)
+    assert L.conv1d_causal(ctypes.byref(conv), *[_addr(i) for i in range(6)], None) == ssm.SSM_ERR_BAD_SHAPE
+    assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 40, D=16, N=1, chunk=1)) == ssm.SSM_ERR_BAD_SHAPE
+    assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 20, D=16, N=1, chunk=1)) != ssm.SSM_ERR_BAD_SHAPE
+
+
 def test_conv_validation(ssm):
     L = ssm.lib()
     d = ssm.ssm_conv_desc(2, 16, 32, 4, 1, 0, 0)
