@@ -87,12 +87,13 @@ typedef int32_t ssm_status;
 
 #define SSM_MAX_DSTATE 64
 #define SSM_MAX_CONV_WIDTH 8
+#define SSM_MAX_SCAN_DIM (1 << 24)   /* channels of a sequence scan: the kernels' tile offsets are 32-bit */
 
 /* Descriptor of a sequence scan (forward or backward). */
 typedef struct ssm_scan_desc {
     int64_t batch;       /* B >= 1 */
     int64_t seqlen;      /* L >= 0 */
-    int64_t dim;         /* D >= 1, inner channels */
+    int64_t dim;         /* D in [1, SSM_MAX_SCAN_DIM], inner channels */
     int64_t dstate;      /* N in [1, SSM_MAX_DSTATE] */
     int32_t conv_width;  /* 0: x already is the scan input u; 1..8: fused causal conv + SiLU */
     int32_t io_dtype;    /* SSM_F32 or SSM_BF16 */

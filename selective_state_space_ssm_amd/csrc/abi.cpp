@@ -89,7 +89,8 @@ bool has_step_size(int32_t d) { return d != SSM_DECAY_CONST; }
 ssm_status check_scan_desc(const ssm_scan_desc *d) {
     if (!d) return SSM_ERR_NULL_ARG;
     if (!valid_io(d->io_dtype) || !valid_disc(d->disc)) return SSM_ERR_UNSUPPORTED;
-    if (d->batch < 1 || d->seqlen < 0 || d->dim < 1 || d->dstate < 1 || d->dstate > SSM_MAX_DSTATE)
+    if (d->batch < 1 || d->seqlen < 0 || d->dim < 1 || d->dim > SSM_MAX_SCAN_DIM || d->dstate < 1 ||
+        d->dstate > SSM_MAX_DSTATE)
         return SSM_ERR_BAD_SHAPE;
     if (d->conv_width < 0 || d->conv_width > SSM_MAX_CONV_WIDTH) return SSM_ERR_BAD_SHAPE;
     if (d->chunk_len < -1) return SSM_ERR_BAD_SHAPE;

@@ -230,6 +230,9 @@ def test_launch_grid_limit(ssm):
     assert L.conv1d_causal(ctypes.byref(conv), *[_addr(i) for i in range(6)], None) == ssm.SSM_ERR_BAD_SHAPE
     assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 40, D=16, N=1, chunk=1)) == ssm.SSM_ERR_BAD_SHAPE
     assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 20, D=16, N=1, chunk=1)) != ssm.SSM_ERR_BAD_SHAPE
+    # channels past the sequence kernels' 32-bit tile offsets
+    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24 + 1, N=1)) == ssm.SSM_ERR_BAD_SHAPE
+    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24, N=1)) != ssm.SSM_ERR_BAD_SHAPE
 
 
 def test_conv_validation(ssm):
