@@ -148,7 +148,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     constexpr int BL = (BE + kThreads - 1) / kThreads;
     __shared__ float s_u[XUEP], s_dt[XEP], s_z[XEP], s_dy[XEP];
     __shared__ float s_B[BE], s_C[BE];
-    __shared__ float s_rB[T][kCPB][NP], s_rC[T][kCPB][NP];   // per-channel dB, dC terms
+    // per-channel dB, dC terms; each token's slab padded by 16 words so that the
+    // two tokens a 32-lane half reads land on opposite bank halves
+    __shared__ float s_rB[T][kCPB * NP + 16], s_rC[T][kCPB * NP + 16];
+    auto termB = [&](int i, int c, int n) -> float & { return s_rB[i][c * NP + n]; };
+    auto termC = [&](int i, int c, int n) -> float & { return s_rC[i][c * NP + n]; };
     __shared__ float s_gx[CONV ? (T + 7) * kXR : 1];       // conv-output gradient, tile + 7 following
     __shared__ float s_wk[CONV ? kCPB * 8 : 1];              // conv taps, right-aligned in 8 slots
     // outputs of the finished tile, written to memory one tile later (below)
@@ -617,8 +621,8 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                         else
                             g[s] = a * gj;
                         // dB, dC terms of this channel; summed over channels below
-                        s_rB[i][cl][l + 16 * s] = bpart;
-                        s_rC[i][cl][l + 16 * s] = cpart;
+                        termB(i, cl, l + 16 * s) = bpart;
+                        termC(i, cl, l + 16 * s) = cpart;
                     }
                     pdt[kk] = pt;
                     pdu[kk] = pu;
@@ -677,18 +681,21 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             // written after the next barrier, when nobody reads rows T..T+6
             gshift = (tid < 7 * kCPB) ? s_gx[(tid / kCPB) * kXR + tid % kCPB] : 0.0f;
         }
-        // dB, dC partials of this workgroup: its 48 channels in order
-        for (int e = tid; e < T * NP; e += kThreads) {
-            const int i = e / NP, n = e % NP;
+        // dB, dC partials of this workgroup over its 48 channels: B and C on
+        // separate threads, each sum as four chains (chain r takes channels
+        // r, r+4, ... in order), added as ((r0 + r1) + (r2 + r3))
+        for (int e = tid; e < 2 * T * NP; e += kThreads) {
+            const bool isC = e >= T * NP;
+            const int e2 = isC ? e - T * NP : e;
+            const int i = e2 / NP, n = e2 % NP;
             if (n < N && ts + i < Le) {
-                float sb = 0.0f, sc = 0.0f;
-#pragma unroll 8
-                for (int c2 = 0; c2 < kCPB; ++c2) {
-                    sb += s_rB[i][c2][n];
-                    sc += s_rC[i][c2][n];
+                float a4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int c2 = 0; c2 < kCPB; c2 += 4) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) a4[r] += isC ? termC(i, c2 + r, n) : termB(i, c2 + r, n);
                 }
-                s_oB[e] = sb;
-                s_oC[e] = sc;
+                (isC ? s_oC : s_oB)[e2] = (a4[0] + a4[1]) + (a4[2] + a4[3]);
             }
         }
     }
