@@ -760,6 +760,8 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float *pB, const floa
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= total) return;
     float sb = 0.0f, sc = 0.0f;
+    // in order of g; unrolled so that several partials are in flight
+#pragma unroll 8
     for (int g = 0; g < G; ++g) {
         sb += pB[(int64_t)g * total + i];
         sc += pC[(int64_t)g * total + i];
