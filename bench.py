@@ -72,6 +72,99 @@ def bwd_bytes(B, L, D, N, es, gate=True, W=0):
     return reads + writes + params
 
 
+PROBE_LIB = os.path.join(ROOT, "selective_state_space_ssm_amd", "libssm_probe.so")
+PROBE_KINDS = {"v_fma_f32": (0, 1), "v_mul_f32": (1, 1), "v_exp_f32": (2, 1),
+               "v_exp_f32 + 4 v_fma_f32": (3, 5), "v_add_f32 row_ror:8 (DPP)": (4, 1),
+               "v_permlane16_swap_b32": (5, 1)}
+NUM_SIMDS = 256 * 4          # MI355X: 256 CUs of 4 SIMDs
+SIMD_LANES_PER_CYCLE = 16    # a wave64 fp32 VALU instruction issues over 4 cycles
+
+
+def probe_lib():
+    import ctypes
+    if not os.path.exists(PROBE_LIB):
+        raise ImportError("libssm_probe.so is not built (run selective_state_space_ssm_amd/build.py)")
+    lib = ctypes.CDLL(PROBE_LIB)
+    p, i32, i64, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float
+    lib.probe_rate.argtypes = [i32, i32, i32, f32, f32, p, p, p]
+    lib.probe_rate.restype = i32
+    lib.probe_copy.argtypes = [p, p, i64, i32, p]
+    lib.probe_copy.restype = i32
+    return lib
+
+
+def isa_rates(torch):
+    """Issue rates of single VALU instructions on every SIMD (8 wavefronts per
+    SIMD, 8 independent chains per lane), the shader clock they ran at, and
+    the wave64 cycles per instruction that follow.  Kernels from
+    libssm_probe.so, built with the scan library's flags."""
+    import ctypes
+    lib = probe_lib()
+    blocks, chains = 256 * 8, 8
+    out = torch.empty(blocks * 256, device="cuda")
+    clk = torch.zeros(blocks * 4, dtype=torch.int64, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    for name, (kind, ops) in PROBE_KINDS.items():
+        iters = 4096 if ops == 1 else 1024
+
+        def launch():
+            rc = lib.probe_rate(kind, blocks, iters, ctypes.c_float(0.9999), ctypes.c_float(1e-4),
+                                ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(clk.data_ptr()), stream)
+            if rc != 0:
+                raise RuntimeError("probe_rate(%s) failed: %d" % (name, rc))
+
+        for _ in range(3):
+            launch()
+        tm = EventTimer(torch)
+        for _ in range(5):
+            tm.run(launch)
+        ms = tm.mean_ms()
+        lane_ops = blocks * 256 * iters * chains * ops
+        rate = lane_ops / (ms * 1e-3)
+        c = clk.view(blocks, 4).cpu().double()
+        ratio = float(((c[:, 1] - c[:, 0]) / (c[:, 3] - c[:, 2])).median())
+        res[name] = {"lane_ops_per_s": rate, "us": round(ms * 1e3, 2), "memtime_per_realtime_tick": round(ratio, 3)}
+    # clock from the FMA rate: one wave64 instruction per SIMD every 4 cycles
+    fma = res["v_fma_f32"]["lane_ops_per_s"]
+    clock = fma / (NUM_SIMDS * SIMD_LANES_PER_CYCLE)
+    for name, r in res.items():
+        r["wave64_cycles_per_instr"] = round(NUM_SIMDS * 64 * clock / r["lane_ops_per_s"], 3)
+    return {"rates": res, "clock_GHz_if_fma_is_4_cycles": round(clock / 1e9, 4),
+            "note": "lane_ops_per_s counts every instruction (the mix counts 5 per exp); "
+                    "memtime_per_realtime_tick is s_memtime over the 100 MHz s_memrealtime counter"}
+
+
+def copy_ceiling(torch, nbytes=1 << 30, reps=10):
+    """A plain streaming copy of `nbytes` (read + write, far beyond the 256 MB
+    last-level cache) timed with the headline's event protocol: the practical
+    HBM ceiling next to the specification.  Returns GB/s counted as bytes
+    read + bytes written."""
+    import ctypes
+    lib = probe_lib()
+    a = torch.ones(nbytes // 4, device="cuda")
+    b = torch.empty_like(a)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        rc = lib.probe_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), nbytes // 16, 4096, stream)
+        if rc != 0:
+            raise RuntimeError("probe_copy failed: %d" % rc)
+
+    for _ in range(3):
+        launch()
+    tm = EventTimer(torch)
+    for _ in range(reps):
+        tm.run(launch)
+    ms = tm.mean_ms()
+    ok = bool(torch.equal(a[:1024], b[:1024])) and bool(torch.equal(a[-1024:], b[-1024:]))
+    del a, b
+    torch.cuda.empty_cache()
+    if not ok:
+        raise RuntimeError("copy probe produced wrong data")
+    return 2 * nbytes / (ms * 1e-3) / 1e9, ms
+
+
 class EventTimer:
     """HIP-event durations of individual launches on the current stream."""
 
@@ -104,6 +197,8 @@ def main():
                     help="skip the whole-model decode extras (their many small launches make counter passes slow)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only measure instruction rates, clock and the copy ceiling, print them as JSON")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -119,6 +214,11 @@ def main():
 
     ssm.lib()
     torch.cuda.set_device(0)
+    if args.probe:
+        gbs, ms = copy_ceiling(torch)
+        print(json.dumps({"copy_GBps": round(gbs, 1), "copy_us": round(ms * 1e3, 1), "isa": isa_rates(torch)}),
+              flush=True)
+        return
     dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda", dt)
 
     # ------------------------------------------------------------ headline
@@ -172,10 +272,22 @@ def main():
     }
     del reps
     torch.cuda.empty_cache()
+    # the practical ceiling: a plain copy timed the same way
+    try:
+        cgbs, _ = copy_ceiling(torch)
+        out["roofline"]["copy_GBps"] = round(cgbs, 1)
+        out["roofline"]["frac_of_copy"] = round(achieved / cgbs, 4)
+        log("plain copy: %.1f GB/s; forward at %.1f%% of it" % (cgbs, 100 * achieved / cgbs))
+    except Exception as e:
+        log("copy probe failed: %r" % (e,))
 
     # ------------------------------------------------------------ extras
     extra = {}
     if not args.no_extra:
+        try:
+            extra["isa_rates"] = isa_rates(torch)
+        except Exception as e:
+            log("instruction-rate probe failed: %r" % (e,))
         try:
             extra.update(bench_extras(torch, np, si, ssm, dev, args))
         except Exception as e:  # report, keep the headline line

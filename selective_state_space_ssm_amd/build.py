@@ -1,8 +1,12 @@
-"""Build the gfx950 HIP library libssm_amd.so in-tree with hipcc.
+"""Build the gfx950 HIP libraries in-tree with hipcc.
+
+libssm_amd.so: the scan library (the C ABI of include/ssm.h).
+libssm_probe.so: measurement kernels (instruction rates, clock, a plain
+copy) that bench.py uses to calibrate the bounds; built with the same flags
+so that its rates are the ones the scan kernels see.
 
 Every translation unit under csrc/ is compiled for gfx950 only, with packed
-fp32 instructions disabled, and linked into one shared library next to this
-file.  Objects go to _build/ (not tracked).
+fp32 instructions disabled.  Objects go to _build/ (not tracked).
 """
 from __future__ import annotations
 
@@ -18,6 +22,8 @@ LIB = os.path.join(HERE, "libssm_amd.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
 SOURCES = ["abi.cpp", "conv1d.hip", "scan_fwd.hip", "scan_bwd.hip", "step.hip", "model.hip"]
+PROBE_SOURCES = ["probe.hip"]
+PROBE_LIB = os.path.join(HERE, "libssm_probe.so")
 ARCH = "gfx950"
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
@@ -46,20 +52,27 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile and link; returns the path of libssm_amd.so."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = min(len(SOURCES), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib) -> str:
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s\n%s" % (" ".join(cmd), r.stderr[-4000:]))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile and link both libraries; returns the path of libssm_amd.so."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = min(len(srcs), max(1, int(os.environ.get("MAX_JOBS", os.cpu_count() or 4))))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", PROBE_LIB)
     return LIB
 
 

@@ -12,8 +12,11 @@
 // Kernels, in launch order for one token of S streams (4 per block + 1):
 //   per block
 //     linear<INPROJ>   LayerNorm(x) @ in_proj^T on the matrix cores: the
-//                      LayerNorm is applied to the A rows as they are loaded
-//                      (row statistics first, in the kernel); block 0 takes
+//                      LayerNorm is folded into the product algebraically
+//                      (the raw rows times the weights scaled by the norm's
+//                      weight, then the row mean and 1/std applied in the
+//                      epilogue with per-column sums of the scaled weights and
+//                      of the norm's bias times the weights); block 0 takes
 //                      its rows from emb[token] and starts the residual
 //                      stream; the epilogue runs the conv step on the xin half
 //                      (history shift in place, SiLU) and stores z;
@@ -30,8 +33,9 @@
 // wavefronts, the shares summed through LDS in a fixed order.  Each lane
 // loads 4 consecutive k of one A row and one W row (16 bytes); MFMA call q
 // takes element q of every lane, so lane group g supplies k = k0 + 4g + q to
-// both operands and the 16 k of a step are all covered.  Four steps of loads
-// are issued before their MFMAs.  At one stream the products are
+// both operands and the 16 k of a step are all covered.  The reduction runs
+// in groups of two 16-k steps held in two register sets: the next group's
+// loads are issued before the current group's MFMAs.  At one stream the products are
 // matrix-vector: the weights are streamed once, and splitting the reduction
 // over up to 16 wavefronts spreads them over many CUs.
 #include <math.h>

@@ -224,15 +224,21 @@ def test_launch_grid_limit(ssm):
     ptrs = [_addr(i) for i in range(13)]
     big = ssm.ssm_step_desc(1, 2 ** 32, 1, 1, 0, 0, 0, 0)
     assert L.ssm_step(ctypes.byref(big), *ptrs, None) == ssm.SSM_ERR_BAD_SHAPE
+    # an accepted grid must still stop at a later host check: y misaligned
+    # (these fake addresses must never reach a kernel on a machine with a GPU)
     ok = ssm.ssm_step_desc(1, 2 ** 20, 1, 1, 0, 0, 0, 0)
-    assert L.ssm_step(ctypes.byref(ok), *ptrs, None) != ssm.SSM_ERR_BAD_SHAPE
+    p_ok = list(ptrs)
+    p_ok[12] = _addr(12, 4)
+    assert L.ssm_step(ctypes.byref(ok), *p_ok, None) == ssm.SSM_ERR_ALIGNMENT
     conv = ssm.ssm_conv_desc(1, 2 ** 40, 1, 4, 1, 0, 0)
     assert L.conv1d_causal(ctypes.byref(conv), *[_addr(i) for i in range(6)], None) == ssm.SSM_ERR_BAD_SHAPE
     assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 40, D=16, N=1, chunk=1)) == ssm.SSM_ERR_BAD_SHAPE
-    assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 20, D=16, N=1, chunk=1)) != ssm.SSM_ERR_BAD_SHAPE
+    # accepted: stops at the missing workspace the split needs
+    assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 20, D=16, N=1, chunk=1)) == ssm.SSM_ERR_WORKSPACE
     # channels past the sequence kernels' 32-bit tile offsets
     assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24 + 1, N=1)) == ssm.SSM_ERR_BAD_SHAPE
-    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24, N=1)) != ssm.SSM_ERR_BAD_SHAPE
+    # accepted: stops at y overlapping x
+    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24, N=1), y=_addr(0)) == ssm.SSM_ERR_ALIAS
 
 
 def test_conv_validation(ssm):
@@ -297,3 +303,4 @@ def test_model_decode_validation(ssm):
     assert _model_call(ssm, good, layer_over={"A_log": A + 0x50000004}) == ssm.SSM_ERR_ALIGNMENT
     assert _model_call(ssm, good, logits=_addr(1, 64)) == ssm.SSM_ERR_ALIAS     # logits inside emb
     assert _model_call(ssm, good, h=_addr(8, 256)) == ssm.SSM_ERR_ALIAS         # state inside the workspace
+

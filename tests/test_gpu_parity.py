@@ -436,17 +436,21 @@ def test_step_bf16_state_first_step_exact_rounding(ssm):
 def test_streaming_decode_six_blocks(ssm):
     """Batched streaming decode: 6 blocks x 256 streams x 1536 channels x 16
     states, 3-token conv history, 1,024 consecutive steps, one launch per
-    block and step.  Every stream of every block is stepped on the GPU;
-    the oracle replays a sample of 6 streams over all steps."""
+    block and step.  Every stream of every block is stepped on the GPU.
+    Block 0 is replayed by the oracle over all 256 streams, and its y is
+    compared at every step; the other blocks are replayed for a sample of 6
+    streams, y compared at steps 0, 511 and 1023.  The final state and
+    history are compared for every replayed stream."""
     nblk, S, D, N, W, steps = 6, 256, 1536, 16, 4, 1024
     sample = [0, 37, 101, 128, 200, 255]
     prm = si.stream_params(nblk, D, N, W)
     P = {k: dev(v) for k, v in prm.items()}
     h = torch.zeros(nblk, S, D, N, device="cuda")
     cs = torch.zeros(nblk, S, W - 1, D, device="cuda")
-    ho = np.zeros((nblk, len(sample), D, N))
-    co = np.zeros((nblk, len(sample), W - 1, D))
-    y_last_ref = None
+    rows = [list(range(S))] + [sample] * (nblk - 1)
+    ho = [np.zeros((len(r), D, N)) for r in rows]
+    co = [np.zeros((len(r), W - 1, D)) for r in rows]
+    worst = 0.0
     for t in range(steps):
         for k in range(nblk):
             inp = si.stream_token_torch(k, t, S, D, N, "cuda")
@@ -454,16 +458,20 @@ def test_streaming_decode_six_blocks(ssm):
                              inp["B"][None], inp["C"][None], conv_state=cs[k:k + 1], z=inp["z"][None],
                              conv_w=P["conv_w"][k:k + 1], conv_b=P["conv_b"][k:k + 1],
                              dt_bias=P["dt_bias"][k:k + 1], Dskip=P["Dskip"][k:k + 1])
-            sl = {kk: host(v[sample]) for kk, v in inp.items()}
+            sl = {kk: host(v[rows[k]]) for kk, v in inp.items()}
             yr = oracle.step(ho[k], co[k], sl["x"], sl["dt_raw"], sl["B"], sl["C"], prm["A_log"][k], z=sl["z"],
                              conv_w=prm["conv_w"][k], conv_b=prm["conv_b"][k], dt_bias=prm["dt_bias"][k],
                              Dskip=prm["Dskip"][k])
-            if t in (0, 511, steps - 1):
-                assert rel_linf(y[0][sample], yr) <= FP32_TOL, (t, k)
+            if k == 0 or t in (0, 511, steps - 1):
+                e = rel_linf(y[0][rows[k]], yr)
+                worst = max(worst, e)
+                assert e <= FP32_TOL, (t, k, e)
+        if t % 256 == 255:
+            print("decode step %d done, worst y error so far %.2e" % (t + 1, worst), flush=True)
     torch.cuda.synchronize()
     for k in range(nblk):
-        assert rel_linf(h[k][sample], ho[k]) <= FP32_TOL
-        np.testing.assert_array_equal(host(cs[k][sample]), co[k])
+        assert rel_linf(h[k][rows[k]], ho[k]) <= FP32_TOL, k
+        np.testing.assert_array_equal(host(cs[k][rows[k]]), co[k])
 
 
 # --------------------------------------------------------------------------- backward
@@ -551,6 +559,21 @@ def test_bwd_forward_backward_workload(ssm):
     p = si.mamba_block(8, 2048, 1536, 16, 4, workload=si.WL_FWDBWD, with_dy=True)
     q = dict(p, h0=np.zeros((8, 1536, 16), np.float32), dhT=np.zeros((8, 1536, 16), np.float32))
     _bwd_check(ssm, q, torch.float32, DB, h0=False, dhT=False, conv=True)
+
+
+def test_bwd_forward_backward_workload_u_in(ssm):
+    """The forward + backward workload in its literal form: batch 8,
+    L=2,048, D_inner=1536, N=16, fp32, the scan input u = SiLU(conv4(x))
+    computed beforehand (by the oracle's conv, rounded to float32) and given
+    with conv_width 0, gated.  Gradients w.r.t. u, dt (as d_dt_raw and
+    d_dt_bias), A_log, B, C, Dskip and z against the oracle's scan backward
+    (TensorViz explorer, verified by the local recipe: the selection maps
+    receive gradients)."""
+    p = si.mamba_block(8, 2048, 1536, 16, 4, workload=si.WL_FWDBWD, with_dy=True)
+    u, _ = oracle.conv1d_causal(p["x"], p["conv_w"], p["conv_b"])
+    q = dict(p, x=u.astype(np.float32), h0=np.zeros((8, 1536, 16), np.float32),
+             dhT=np.zeros((8, 1536, 16), np.float32))
+    _bwd_check(ssm, q, torch.float32, DB, h0=False, dhT=False, conv=False)
 
 
 # --------------------------------------------------------------------------- backward with the conv prologue

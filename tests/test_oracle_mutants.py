@@ -2,7 +2,9 @@
 
 Each case plants one mistake in a copy of ssm_oracle.c (on the CPU, in a
 temporary directory), builds it, and runs the pin suite against that build in
-a subprocess.  The suite must fail for every mutant.
+a subprocess.  The suite must fail for every mutant.  The whole-model oracle
+(mamba_model.py) gets the same treatment for the order of its projection
+splits.
 """
 import os
 import subprocess
@@ -69,3 +71,62 @@ def test_pins_catch_mutant(name, tmp_path):
                         "-x", "-q", "-p", "no:cacheprovider"], cwd=ROOT, env=env,
                        capture_output=True, text=True, timeout=600)
     assert r.returncode == 1, "pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])
+
+
+MODEL_SRC = os.path.join(ROOT, "oracle", "mamba_model.py")
+
+# Each entry: a list of (old, new) replacements applied together, so that a
+# mix-up made the same way in both the token step and the sequence form
+# (which the streaming == sequence pin cannot see) is planted.
+MODEL_MUTANTS = {
+    "swap_xin_z": [("xin, z = xz[:, :Di], xz[:, Di:]", "z, xin = xz[:, :Di], xz[:, Di:]"),
+                   ("xin, z = xz[..., :Di], xz[..., Di:]", "z, xin = xz[..., :Di], xz[..., Di:]")],
+    "swap_dt_C": [("dt_low, Bm, Cm = xp[:, :R], xp[:, R:R + N], xp[:, R + N:]",
+                   "Cm, Bm, dt_low = xp[:, :R], xp[:, R:R + N], xp[:, R + N:]"),
+                  ("dt_raw = xp[..., :R] @", "dt_raw = xp[..., R + N:] @"),
+                  ("xp[..., R:R + N], xp[..., R + N:],", "xp[..., R:R + N], xp[..., :R],")],
+    "swap_dt_B": [("dt_low, Bm, Cm = xp[:, :R], xp[:, R:R + N], xp[:, R + N:]",
+                   "Bm, dt_low, Cm = xp[:, :R], xp[:, R:R + N], xp[:, R + N:]"),
+                  ("dt_raw = xp[..., :R] @", "dt_raw = xp[..., R:R + N] @"),
+                  ("xp[..., R:R + N], xp[..., R + N:],", "xp[..., :R], xp[..., R + N:],")],
+    "swap_B_C": [("dt_low, Bm, Cm = xp[:, :R], xp[:, R:R + N], xp[:, R + N:]",
+                  "dt_low, Cm, Bm = xp[:, :R], xp[:, R:R + N], xp[:, R + N:]"),
+                 ("xp[..., R:R + N], xp[..., R + N:],", "xp[..., R + N:], xp[..., R:R + N],")],
+}
+
+
+def _run_model_pins(src, tmp_path, oracle_lib):
+    """Run the whole-model pins against a copy of the model oracle whose
+    source is `src`; returns the pytest subprocess result."""
+    import shutil
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "oracle", "__init__.py"), pkg / "__init__.py")
+    (pkg / "mamba_model.py").write_text(src)
+    # the copy loads the built C oracle; the copied package is found first
+    # (python -m puts the working directory at the head of sys.path)
+    env = dict(os.environ, SSM_ORACLE_LIB=oracle_lib.build(force=False), OMP_NUM_THREADS="2",
+               PYTHONPATH=os.pathsep.join([str(tmp_path), ROOT]))
+    return subprocess.run([sys.executable, "-m", "pytest", os.path.join(HERE, "test_oracle_model_pins.py"),
+                           "-x", "-q", "-p", "no:cacheprovider", "--rootdir", ROOT], cwd=str(tmp_path),
+                          env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_model_pins_pass_on_an_unmutated_copy(tmp_path, oracle_lib):
+    """Control: the copy mechanism itself passes the pins, so a failure
+    below is the planted mix-up."""
+    r = _run_model_pins(open(MODEL_SRC).read(), tmp_path, oracle_lib)
+    assert r.returncode == 0, r.stdout[-2000:]
+
+
+@pytest.mark.parametrize("name", sorted(MODEL_MUTANTS))
+def test_model_pins_catch_mutant(name, tmp_path, oracle_lib):
+    """Plant one mix-up of the projections' split order in a copy of the
+    whole-model oracle and run its pins against that copy."""
+    src = open(MODEL_SRC).read()
+    for old, new in MODEL_MUTANTS[name]:
+        assert src.count(old) == 1, "mutation site not unique / missing: %s: %s" % (name, old)
+        src = src.replace(old, new)
+    r = _run_model_pins(src, tmp_path, oracle_lib)
+    assert r.returncode == 1 and " failed" in r.stdout, \
+        "model pins did not catch mutant %s:\n%s" % (name, r.stdout[-2000:])
