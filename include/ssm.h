@@ -76,6 +76,7 @@ typedef int32_t ssm_status;
 #define SSM_ERR_ALIGNMENT 5    /* a tensor does not start on a 16-byte boundary */
 #define SSM_ERR_ALIAS 6        /* buffers overlap in a way the call does not allow */
 #define SSM_ERR_HIP 7          /* a HIP launch failed */
+#define SSM_ERR_SCRATCH_LIMIT 8  /* the request needs more than the static scratch buffer holds */
 
 #define SSM_F32 0
 #define SSM_BF16 1
@@ -88,6 +89,7 @@ typedef int32_t ssm_status;
 #define SSM_MAX_DSTATE 64
 #define SSM_MAX_CONV_WIDTH 8
 #define SSM_MAX_SCAN_DIM (1 << 24)   /* channels of a sequence scan: the kernels' tile offsets are 32-bit */
+#define SSM_STATIC_SCRATCH_BYTES (16u << 20)   /* ssm_scan_fwd_static's device buffer, per GPU */
 
 /* Descriptor of a sequence scan (forward or backward). */
 typedef struct ssm_scan_desc {
@@ -216,6 +218,34 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
                         const float *conv_state_in, float *conv_state_out,
                         const float *h0, float *hT, void *y,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ssm_scan_fwd_static -- ssm_scan_fwd without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments,
+ * results and errors are those of ssm_scan_fwd; the chunk summaries of a
+ * time split go to a buffer of SSM_STATIC_SCRATCH_BYTES that the library
+ * holds on every GPU it runs on (a static device array, kept until the
+ * process ends).  The call allocates nothing.
+ *   Returns SSM_ERR_SCRATCH_LIMIT, before any HIP call, when
+ *   ssm_scan_fwd_workspace_size for the same descriptor exceeds
+ *   SSM_STATIC_SCRATCH_BYTES (pass a shorter chunk_len, or -1, or use
+ *   ssm_scan_fwd with a workspace).
+ *   Every call on one GPU shares that GPU's buffer: calls that overlap on a
+ *   GPU (on different streams, or from different host threads without
+ *   ordering) race on it and must be serialised by the caller.  Calls on one
+ *   stream are ordered and safe.  The buffer keeps the last call's contents;
+ *   every value a call reads from it is written earlier in the same call.
+ *   The first call on a device looks up the buffer's device address (a HIP
+ *   call that is not capturable): make one call on each device before any
+ *   graph capture.
+ */
+ssm_status ssm_scan_fwd_static(const ssm_scan_desc *desc, const void *x, const void *dt_raw,
+                               const float *dt_bias, const float *A_log, const void *B,
+                               const void *C, const float *Dskip, const void *z,
+                               const float *conv_w, const float *conv_b,
+                               const float *conv_state_in, float *conv_state_out,
+                               const float *h0, float *hT, void *y, void *stream);
 
 /* Bytes of device workspace ssm_scan_bwd needs for this descriptor. */
 ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes);

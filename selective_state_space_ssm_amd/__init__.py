@@ -27,6 +27,8 @@ SSM_ERR_WORKSPACE = 4
 SSM_ERR_ALIGNMENT = 5
 SSM_ERR_ALIAS = 6
 SSM_ERR_HIP = 7
+SSM_ERR_SCRATCH_LIMIT = 8
+SSM_STATIC_SCRATCH_BYTES = 16 << 20   # the library's static device buffer (ssm_scan_fwd_static)
 
 SSM_F32 = 0
 SSM_BF16 = 1
@@ -37,7 +39,7 @@ SSM_DECAY_CONST = 2   # decay fixed per (channel, state); no step size, dt_raw m
 EXPORTED_SYMBOLS = (
     "ssm_version", "ssm_status_string", "conv1d_causal", "ssm_scan_fwd_workspace_size",
     "ssm_scan_fwd", "ssm_scan_bwd_workspace_size", "ssm_scan_bwd", "ssm_step",
-    "ssm_model_decode_workspace_size", "ssm_model_decode_step",
+    "ssm_model_decode_workspace_size", "ssm_model_decode_step", "ssm_scan_fwd_static",
 )
 
 
@@ -101,6 +103,8 @@ def lib():
         L.ssm_scan_fwd_workspace_size.argtypes = [ctypes.POINTER(ssm_scan_desc), ctypes.POINTER(sz)]
         L.ssm_scan_fwd.restype = i32
         L.ssm_scan_fwd.argtypes = [ctypes.POINTER(ssm_scan_desc)] + [p] * 16 + [sz, p]
+        L.ssm_scan_fwd_static.restype = i32
+        L.ssm_scan_fwd_static.argtypes = [ctypes.POINTER(ssm_scan_desc)] + [p] * 16
         L.ssm_scan_bwd_workspace_size.restype = i32
         L.ssm_scan_bwd_workspace_size.argtypes = [ctypes.POINTER(ssm_scan_desc), ctypes.POINTER(sz)]
         L.ssm_scan_bwd.restype = i32
@@ -224,6 +228,28 @@ def ssm_scan_fwd(x, dt_raw, A_log, B, C, dt_bias=None, Dskip=None, z=None, conv_
         _f32(conv_w, "conv_w"), _f32(conv_b, "conv_b"), _f32(conv_state_in, "conv_state_in"),
         _f32(conv_state_out, "conv_state_out"), _f32(h0, "h0"), _f32(hT, "hT"), _ptr(y, t, "y"),
         _ptr(ws, None, "workspace"), ctypes.c_size_t(ws.numel() if ws is not None else 0),
+        _stream(stream)))
+    return y
+
+
+def ssm_scan_fwd_static(x, dt_raw, A_log, B, C, dt_bias=None, Dskip=None, z=None, conv_w=None, conv_b=None,
+                        conv_state_in=None, conv_state_out=None, h0=None, hT=None, y=None,
+                        disc=SSM_DISC_DELTA_B, chunk_len=0, stream=None):
+    """ssm_scan_fwd without a workspace: a time split keeps its chunk summaries
+    in the library's static device buffer (SSM_STATIC_SCRATCH_BYTES per GPU).
+    Allocates nothing when y is given.  Calls that overlap on one GPU race on
+    that buffer.  Returns y."""
+    N = A_log.shape[1]
+    W = conv_w.shape[1] if conv_w is not None else 0
+    desc = _scan_desc(x, N, W, disc, chunk_len)
+    if y is None:
+        y = torch.empty_like(x)
+    t = x.dtype
+    _check("ssm_scan_fwd_static", lib().ssm_scan_fwd_static(
+        ctypes.byref(desc), _ptr(x, t, "x"), _ptr(dt_raw, t, "dt_raw"), _f32(dt_bias, "dt_bias"),
+        _f32(A_log, "A_log"), _ptr(B, t, "B"), _ptr(C, t, "C"), _f32(Dskip, "Dskip"), _ptr(z, t, "z"),
+        _f32(conv_w, "conv_w"), _f32(conv_b, "conv_b"), _f32(conv_state_in, "conv_state_in"),
+        _f32(conv_state_out, "conv_state_out"), _f32(h0, "h0"), _f32(hT, "hT"), _ptr(y, t, "y"),
         _stream(stream)))
     return y
 

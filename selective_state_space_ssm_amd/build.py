@@ -21,7 +21,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libssm_amd.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["abi.cpp", "conv1d.hip", "scan_fwd.hip", "scan_bwd.hip", "step.hip", "model.hip"]
+SOURCES = ["abi.cpp", "conv1d.hip", "scan_fwd.hip", "scan_bwd.hip", "step.hip", "model.hip", "scratch.hip"]
 PROBE_SOURCES = ["probe.hip"]
 PROBE_LIB = os.path.join(HERE, "libssm_probe.so")
 ARCH = "gfx950"

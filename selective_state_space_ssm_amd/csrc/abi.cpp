@@ -124,6 +124,7 @@ const char *ssm_status_string(ssm_status s) {
         case SSM_ERR_ALIGNMENT: return "a tensor does not start on a 16-byte boundary";
         case SSM_ERR_ALIAS: return "buffers overlap in a way the call does not allow";
         case SSM_ERR_HIP: return "a HIP launch failed";
+        case SSM_ERR_SCRATCH_LIMIT: return "the request needs more than the library's static scratch buffer holds";
         default: return "unknown status";
     }
 }
@@ -164,11 +165,17 @@ ssm_status ssm_scan_fwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes)
     return SSM_OK;
 }
 
-ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt_raw, const float *dt_bias,
-                        const float *A_log, const void *B, const void *C, const float *Dskip, const void *z,
-                        const float *conv_w, const float *conv_b, const float *conv_state_in,
-                        float *conv_state_out, const float *h0, float *hT, void *y, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ssm_scan_fwd, and with use_static its variant that takes the chunk
+// summaries' buffer from the library's static scratch instead of `workspace`.
+ssm_status scan_fwd_impl(const ssm_scan_desc *desc, const void *x, const void *dt_raw, const float *dt_bias,
+                         const float *A_log, const void *B, const void *C, const float *Dskip, const void *z,
+                         const float *conv_w, const float *conv_b, const float *conv_state_in,
+                         float *conv_state_out, const float *h0, float *hT, void *y, void *workspace,
+                         size_t workspace_bytes, void *stream, bool use_static) {
     ssm_status st = check_scan_desc(desc);
     if (st != SSM_OK) return st;
     const int64_t Bn = desc->batch, L = desc->seqlen, D = desc->dim, N = desc->dstate;
@@ -189,7 +196,12 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
         if (!grid_ok({Bn, cdiv(D, 16), K}) || !grid_ok({Bn, cdiv(D * N, 256)})) return SSM_ERR_BAD_SHAPE;
     }
     const size_t need = ssm::scan_fwd_workspace_bytes(Bn, L, D, N, W, chunk);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return SSM_ERR_WORKSPACE;
+    if (use_static) {
+        if (need > SSM_STATIC_SCRATCH_BYTES) return SSM_ERR_SCRATCH_LIMIT;
+        workspace = nullptr;   // not part of the caller's buffers
+    } else if (need > 0 && (!workspace || workspace_bytes < need)) {
+        return SSM_ERR_WORKSPACE;
+    }
     const int64_t es = io_size(desc->io_dtype);
     const int64_t nbld = Bn * L * D, nbln = Bn * L * N, nbdn = Bn * D * N, nst = Bn * (W > 0 ? W - 1 : 0) * D;
     AliasCheck ac;
@@ -208,9 +220,13 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
     ac.outs = {{y, nbld * es},
                {hT, hT ? nbdn * 4 : 0},
                {conv_state_out, (W > 0 && conv_state_out) ? nst * 4 : 0},
-               {workspace, need > 0 ? (int64_t)need : 0}};
+               {workspace, (need > 0 && workspace) ? (int64_t)need : 0}};
     ac.allowed = {{h0, hT}, {conv_state_in, conv_state_out}};
     if (!ac.ok()) return SSM_ERR_ALIAS;
+    if (use_static && need > 0) {
+        // this device's copy of the static buffer (first call: a symbol lookup)
+        if (ssm::static_scratch(&workspace) != hipSuccess) return SSM_ERR_HIP;
+    }
     ssm::ScanFwdArgs a{};
     a.B = Bn; a.L = L; a.D = D; a.N = N; a.W = W; a.bf16 = desc->io_dtype == SSM_BF16; a.disc = desc->disc;
     a.chunk_len = chunk;
@@ -219,6 +235,28 @@ ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt
     a.conv_state_in = W > 0 ? conv_state_in : nullptr; a.conv_state_out = W > 0 ? conv_state_out : nullptr;
     a.h0 = h0; a.hT = hT; a.y = y; a.ws = workspace;
     return hip_status(ssm::launch_scan_fwd(a, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssm_status ssm_scan_fwd(const ssm_scan_desc *desc, const void *x, const void *dt_raw, const float *dt_bias,
+                        const float *A_log, const void *B, const void *C, const float *Dskip, const void *z,
+                        const float *conv_w, const float *conv_b, const float *conv_state_in,
+                        float *conv_state_out, const float *h0, float *hT, void *y, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    return scan_fwd_impl(desc, x, dt_raw, dt_bias, A_log, B, C, Dskip, z, conv_w, conv_b, conv_state_in,
+                         conv_state_out, h0, hT, y, workspace, workspace_bytes, stream, false);
+}
+
+ssm_status ssm_scan_fwd_static(const ssm_scan_desc *desc, const void *x, const void *dt_raw,
+                               const float *dt_bias, const float *A_log, const void *B, const void *C,
+                               const float *Dskip, const void *z, const float *conv_w, const float *conv_b,
+                               const float *conv_state_in, float *conv_state_out, const float *h0, float *hT,
+                               void *y, void *stream) {
+    return scan_fwd_impl(desc, x, dt_raw, dt_bias, A_log, B, C, Dskip, z, conv_w, conv_b, conv_state_in,
+                         conv_state_out, h0, hT, y, nullptr, 0, stream, true);
 }
 
 ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes) {

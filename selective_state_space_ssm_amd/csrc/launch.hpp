@@ -126,6 +126,11 @@ struct ModelArgs {
 size_t model_workspace_bytes(int64_t S, int64_t dm, int64_t Di, int64_t N, int64_t R);
 hipError_t launch_model_decode(const ModelArgs &a, hipStream_t s);
 
+// The device address of this device's copy of the library's static scratch
+// buffer (SSM_STATIC_SCRATCH_BYTES, scratch.hip), looked up on the first call
+// on each device with that device current.
+hipError_t static_scratch(void **ptr);
+
 // Byte offset helper for workspace carving (256-byte aligned regions).
 inline size_t ws_align(size_t n) { return (n + 255) & ~(size_t)255; }
 

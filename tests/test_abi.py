@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol(ssm):
 
 def test_version_and_status_strings(ssm):
     assert ssm.ssm_version() // 100 == 2
-    for code in range(0, 8):
+    for code in range(0, 9):
         s = ssm.ssm_status_string(code)
         assert isinstance(s, str) and len(s) > 3
     assert ssm.ssm_status_string(99) == "unknown status"
@@ -304,3 +304,29 @@ def test_model_decode_validation(ssm):
     assert _model_call(ssm, good, logits=_addr(1, 64)) == ssm.SSM_ERR_ALIAS     # logits inside emb
     assert _model_call(ssm, good, h=_addr(8, 256)) == ssm.SSM_ERR_ALIAS         # state inside the workspace
 
+
+def _fwd_static(ssm, desc, **over):
+    names = ["x", "dt_raw", "dt_bias", "A_log", "B", "C", "Dskip", "z", "conv_w", "conv_b",
+             "conv_state_in", "conv_state_out", "h0", "hT", "y"]
+    args = {n: _addr(i) for i, n in enumerate(names)}
+    for n in ("dt_bias", "Dskip", "z", "conv_w", "conv_b", "conv_state_in", "conv_state_out", "h0", "hT"):
+        args[n] = None
+    args.update(over)
+    return ssm.lib().ssm_scan_fwd_static(ctypes.byref(desc), *[args[n] for n in names], None)
+
+
+def test_scan_fwd_static_rejects_requests_beyond_its_buffer(ssm):
+    """The no-allocation forward refuses, before any HIP call, a time split
+    whose chunk summaries exceed the static buffer, and validates its other
+    arguments as ssm_scan_fwd does (these fake addresses never reach a
+    kernel: every case stops at a host check)."""
+    assert ssm.SSM_ERR_SCRATCH_LIMIT == 8
+    big = _desc(ssm, B=64, L=4096, D=1536, N=16, chunk=64)
+    assert ssm.ssm_scan_fwd_workspace_size(big) > ssm.SSM_STATIC_SCRATCH_BYTES
+    assert _fwd_static(ssm, big) == ssm.SSM_ERR_SCRATCH_LIMIT
+    fits = _desc(ssm, B=1, L=4096, D=64, N=16, chunk=256)
+    assert 0 < ssm.ssm_scan_fwd_workspace_size(fits) <= ssm.SSM_STATIC_SCRATCH_BYTES
+    assert _fwd_static(ssm, fits, y=_addr(0, 64)) == ssm.SSM_ERR_ALIAS          # y inside x
+    assert _fwd_static(ssm, fits, x=None) == ssm.SSM_ERR_NULL_ARG
+    assert _fwd_static(ssm, fits, B=_addr(4, 4)) == ssm.SSM_ERR_ALIGNMENT
+    assert _fwd_static(ssm, _desc(ssm, N=65)) == ssm.SSM_ERR_BAD_SHAPE
