@@ -45,6 +45,8 @@
 // chunk's affine maps; MODE_FINAL then re-scans every chunk from its exact
 // starting state H_k and writes y.  Time order inside a chunk is untouched.
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "launch.hpp"
 #include "ssm_device.hpp"
@@ -219,6 +221,17 @@ __device__ __forceinline__ float rows_sum(float v) {
     swap16(v, v, a, b);
     swap32(a + b, a + b, c, e);
     return c + e;
+}
+
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (a loop whose
+// index is a constant expression, e.g. a DPP lane selector).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <int K>
@@ -429,6 +442,48 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             ssum += dl;
         }
     };
+    // Sixteen tokens t0 .. t0+15 of the row layout.  B and C are the same for
+    // every lane of a 16-lane row (one state, sixteen channels): lane ch of a
+    // row reads the row's B and C of token t0 + ch once, and token t0 + k
+    // takes them from lane k with a row broadcast (DPP row_newbcast), which
+    // the compiler folds into the multiply that consumes them.  Only
+    // (dt, dt*u), which differ per channel, are read from LDS per token.
+    auto scan_block16 = [&](int t0) {
+        float bv[SPL], cv[SPL];
+#pragma unroll
+        for (int s2 = 0; s2 < SPL; ++s2) {
+            bv[s2] = s_B[(n0 + s2) * kTS + t0 + ch];
+            cv[s2] = s_C[(n0 + s2) * kTS + t0 + ch];
+        }
+        static_for<4>([&](auto gI) {
+            constexpr int g = decltype(gI)::value;
+            const int t = t0 + 4 * g;
+            const float4 d01 = *reinterpret_cast<const float4 *>(&s_dl[ch][t]);
+            const float4 d23 = *reinterpret_cast<const float4 *>(&s_dl[ch][t + 2]);
+            const float dl[4] = {d01.x, d01.z, d23.x, d23.z};
+            const float dy[4] = {d01.y, d01.w, d23.y, d23.w};
+            float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s2 = 0; s2 < SPL; ++s2) {
+                static_for<4>([&](auto iI) {
+                    constexpr int i = decltype(iI)::value;
+                    const float bq = row_bcast<4 * g + i>(bv[s2]);
+                    const float a = hw_exp2(dl[i] * A2[s2]);
+                    float w;
+                    if constexpr (DISC == DISC_DB)
+                        w = dy[i] * bq;
+                    else
+                        w = expm1f(dl[i] * An[s2]) * Ainv[s2] * bq * dy[i];
+                    h[s2] = fmaf(a, h[s2], w);
+                    // the first state's term is a product (a multiply takes the
+                    // broadcast operand directly; fmaf(c, h, 0) does not)
+                    const float cq = row_bcast<4 * g + i>(cv[s2]);
+                    part[i] = (s2 == 0) ? cq * h[s2] : fmaf(cq, h[s2], part[i]);
+                });
+            }
+            s_yp[wv][ch][t + j] = rows_transpose_sum(part);
+        });
+    };
     // four tokens t .. t+3: 16-byte LDS reads, one transposed quad reduction
     auto scan_group = [&](int t) {
         const float4 d01 = *reinterpret_cast<const float4 *>(&s_dl[ch][t]);
@@ -491,8 +546,13 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
         const int64_t ts = t0 + (int64_t)it * T;
         const int nv = (int)min((int64_t)T, t1 - ts);
         if (nv == T) {
+            if constexpr (FINAL && kRowsOfStates) {
 #pragma unroll
-            for (int t = 0; t < T; t += 4) scan_group(t);
+                for (int t = 0; t < T; t += 16) scan_block16(t);
+            } else {
+#pragma unroll
+                for (int t = 0; t < T; t += 4) scan_group(t);
+            }
         } else {
             int t = 0;
             for (; t + 4 <= nv; t += 4) scan_group(t);
