@@ -105,7 +105,7 @@ int64_t resolve_chunk(const ssm_scan_desc *d) {
     const int64_t L = d->seqlen;
     if (d->chunk_len == -1 || L <= 1) return std::max<int64_t>(L, 1);
     if (d->chunk_len > 0) return std::min<int64_t>(d->chunk_len, L);
-    return ssm::scan_fwd_auto_chunk(d->batch, L, d->dim, d->dstate);
+    return ssm::scan_fwd_auto_chunk(d->batch, L, d->dim, d->dstate, d->conv_width, d->disc);
 }
 
 }  // namespace

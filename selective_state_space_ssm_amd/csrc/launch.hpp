@@ -38,8 +38,9 @@ struct ScanFwdArgs {
     void *y;
     void *ws;
 };
-// Time-chunk length the library picks for this shape (>= L: no split).
-int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N);
+// Time-chunk length the library picks for this shape (>= L: no split); W is
+// the fused conv width (0: none) and disc the decay form.
+int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N, int W, int disc);
 size_t scan_fwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int W,
                                 int64_t chunk_len);
 hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s);

@@ -660,6 +660,263 @@ __global__ __launch_bounds__(256) void carry_kernel(const float *A_log, const fl
         for (int64_t j = i; j < conv_count; j += (int64_t)gridDim.x * blockDim.x) conv_copy[j] = conv_in[j];
 }
 
+// ------------------------------------------------ one-wavefront chunk scan
+// A split in time (above) supplies the parallelism of long sequences, so
+// their chunks run in single-wavefront workgroups with four states per lane
+// and no workgroup barrier.  Used for N = 16, no fused conv, the dt*B and ZOH
+// forms, and D a multiple of 16.  The wavefront owns 16 channels of one
+// batch row and one chunk:
+//  - scan role: lane (ch, r) = (lane & 15, lane >> 4) keeps states
+//    4r .. 4r+3 of channel ch.  A 16-lane row shares its states over sixteen
+//    channels, so the B and C of token t0 + kk reach the row from lane kk by
+//    DPP row broadcast; lane (kk, r) loads B[t0 + kk][4r .. 4r+3] (and C)
+//    straight from memory, 16 tokens x 16 states contiguous per wavefront;
+//  - io role: lane (cp, rq) = (lane & 7, lane >> 3) loads, transforms and
+//    stores channels 2cp and 2cp+1 of tokens rq + 8i, two channels per access;
+//  - the per-token transform (softplus, dt*u, the gate, D*u) goes from the io
+//    role to the scan role through LDS, [channel][token];
+//  - the readout adds a lane's four states in registers and the four rows
+//    with the row swaps, leaving token t + r of channel ch in lane (ch, r),
+//    which finishes y; y goes back to the io role through LDS for the store.
+// Tiles are 32 tokens; the next tile's loads are issued before the current
+// tile's scan, and the current tile's stores after them.  Tokens past the
+// chunk get dt = dt*u = 0, which leaves the state unchanged, and are not
+// stored.
+constexpr int kLT = 32;            // tokens per tile
+constexpr int kLDP = kLT + 2;      // padded [channel][token] row of float2
+constexpr int kLYS = 18;           // [token][channel] row of the y tile
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Two adjacent channels of one token (io role) and four adjacent states of one
+// token (B, C), as raw io bits, with their conversions.
+template <typename IOT> struct LongIO;
+template <> struct LongIO<float> {
+    typedef u32x2 pair_t;
+    typedef u32x4 quad_t;
+    __device__ __forceinline__ static pair_t ld2(buf_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0); }
+    __device__ __forceinline__ static quad_t ld4(buf_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b128(r, o, 0, 0); }
+    __device__ __forceinline__ static float e2(pair_t v, int c) { return __uint_as_float(c ? v.y : v.x); }
+    __device__ __forceinline__ static float e4(quad_t v, int s) {
+        return __uint_as_float(s == 0 ? v.x : s == 1 ? v.y : s == 2 ? v.z : v.w);
+    }
+    __device__ __forceinline__ static void st2(buf_t r, uint32_t o, float a, float b) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(a), __float_as_uint(b)}, r, o, 0, 0);
+    }
+};
+template <> struct LongIO<bf16_t> {
+    typedef uint32_t pair_t;
+    typedef u32x2 quad_t;
+    __device__ __forceinline__ static pair_t ld2(buf_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0); }
+    __device__ __forceinline__ static quad_t ld4(buf_t r, uint32_t o) { return __builtin_amdgcn_raw_buffer_load_b64(r, o, 0, 0); }
+    __device__ __forceinline__ static float e2(pair_t v, int c) { return __uint_as_float(c ? (v & 0xffff0000u) : (v << 16)); }
+    __device__ __forceinline__ static float e4(quad_t v, int s) {
+        const uint32_t w = s < 2 ? v.x : v.y;
+        return __uint_as_float((s & 1) ? (w & 0xffff0000u) : (w << 16));
+    }
+    __device__ __forceinline__ static void st2(buf_t r, uint32_t o, float a, float b) {
+        __builtin_amdgcn_raw_buffer_store_b32((uint32_t)bf16_rne(a) | ((uint32_t)bf16_rne(b) << 16), r, o, 0, 0);
+    }
+};
+
+// acc + (lane K of the row's c) * h, as one v_fmac_f32_dpp with a row
+// broadcast (the compiler folds a DPP operand into VOP2 multiplies but not
+// into the three-operand FMA).  The s_nop gives the two wait states a DPP
+// read needs after a VALU write of its source register.
+template <int K>
+__device__ __forceinline__ float fmac_row_bcast(float acc, float c, float h) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc) : "v"(c), "v"(h), "n"(K));
+    return acc;
+}
+
+template <typename IOT, int DISC, int MODE>
+__global__ __launch_bounds__(64) void scan_long_kernel(FwdParams p) {
+    constexpr int T = kLT;
+    constexpr bool FINAL = MODE == MODE_FINAL;
+    typedef LongIO<IOT> IO;
+    __shared__ __align__(16) float2 s_dl[16][kLDP];                  // {dt, dt*u} (ZOH: {dt, u})
+    __shared__ __align__(16) float2 s_gd[FINAL ? 16 : 1][kLDP];      // {gate, Dskip*u}
+    __shared__ __align__(16) float s_y[FINAL ? T : 1][kLYS];
+
+    const IOT *X = static_cast<const IOT *>(p.x);
+    const IOT *DT = static_cast<const IOT *>(p.dt);
+    const IOT *Bp = static_cast<const IOT *>(p.Bm);
+    const IOT *Cp = static_cast<const IOT *>(p.Cm);
+    const IOT *Z = FINAL ? static_cast<const IOT *>(p.z) : nullptr;
+    IOT *Y = static_cast<IOT *>(p.y);
+
+    const int lane = threadIdx.x;
+    const int64_t bid = xcd_remap((int64_t)blockIdx.x, (int64_t)gridDim.x, kNumXcd);
+    const int64_t g = bid % p.groups;
+    const int64_t rest = bid / p.groups;
+    const int k = (int)(rest % p.Kgrid);
+    const int64_t b = rest / p.Kgrid;
+    const int64_t D = p.D, L = p.L;
+    const int64_t d0 = g * 16;
+    const int64_t t0 = (int64_t)k * p.chunk;
+    const int64_t t1 = min(L, t0 + p.chunk);
+    const int ntiles = (int)((t1 - t0 + T - 1) / T);
+
+    const int ch = lane & 15, r = lane >> 4;     // scan role
+    const int cp = lane & 7, rq = lane >> 3;     // io role
+    const int64_t d = d0 + ch;
+    const uint32_t es = sizeof(IOT);
+
+    float h[4] = {0.0f, 0.0f, 0.0f, 0.0f}, A2[4], An[4], Ainv[4];
+    if (p.init != nullptr) {
+        const float4 v = *reinterpret_cast<const float4 *>(p.init + b * p.init_bstride + (int64_t)k * p.init_kstride +
+                                                           d * 16 + 4 * r);
+        h[0] = v.x; h[1] = v.y; h[2] = v.z; h[3] = v.w;
+    }
+    {
+        const float4 al = *reinterpret_cast<const float4 *>(p.A_log + d * 16 + 4 * r);
+        const float alv[4] = {al.x, al.y, al.z, al.w};
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const float A = neg_exp_f(alv[s2]);
+            A2[s2] = A * kLog2e;
+            An[s2] = A;
+            Ainv[s2] = 1.0f / A;
+        }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) asm volatile("" : "+v"(h[s2]) : "v"(A2[s2]));
+    float dtb[2], Dd[2];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+        dtb[c] = p.dt_bias ? p.dt_bias[d0 + 2 * cp + c] : 0.0f;
+        Dd[c] = (FINAL && p.Dskip) ? p.Dskip[d0 + 2 * cp + c] : 0.0f;
+    }
+
+    // one tile's raw loads (io role: x, dt, z; scan role: B, C of two 16-token blocks)
+    typename IO::pair_t rx[4], rdt[4], rz[4];
+    typename IO::quad_t rB[2], rC[2];
+    const uint32_t xo = (uint32_t)((int64_t)rq * D + 2 * cp) * es;    // + i * 8 rows
+    const uint32_t xs = (uint32_t)(8 * D) * es;
+    const uint32_t bo = (uint32_t)(ch * 16 + 4 * r) * es;              // + j * 16 tokens
+    const uint32_t bs = (uint32_t)(16 * 16) * es;
+    auto fetch = [&](int it) {
+        const int64_t ts = t0 + (int64_t)it * T;
+        const int64_t left = t1 - ts;
+        const uint64_t xr = (uint64_t)(left * D - d0) * es;
+        const buf_t bX = make_buf(X + (b * L + ts) * D + d0, xr);
+        const buf_t bD = make_buf(DT + (b * L + ts) * D + d0, xr);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            rx[i] = IO::ld2(bX, xo + i * xs);
+            rdt[i] = IO::ld2(bD, xo + i * xs);
+        }
+        if (Z != nullptr) {
+            const buf_t bZ = make_buf(Z + (b * L + ts) * D + d0, xr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rz[i] = IO::ld2(bZ, xo + i * xs);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rz[i] = typename IO::pair_t{};
+        }
+        const uint64_t br = (uint64_t)(left * 16) * es;
+        const buf_t bB = make_buf(Bp + (b * L + ts) * 16, br);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) rB[j] = IO::ld4(bB, bo + j * bs);
+        if constexpr (FINAL) {
+            const buf_t bC = make_buf(Cp + (b * L + ts) * 16, br);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) rC[j] = IO::ld4(bC, bo + j * bs);
+        }
+    };
+
+    float ssum = 0.0f;
+    float bv[2][4], cv[2][4];
+    if (ntiles > 0) fetch(0);
+    for (int it = 0; it < ntiles; ++it) {
+        const int64_t ts = t0 + (int64_t)it * T;
+        const int nv = (int)min((int64_t)T, t1 - ts);
+        // transform (io role) into LDS; B, C out of the raw registers
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int tt = rq + 8 * i;
+            const bool v = tt < nv;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float u = IO::e2(rx[i], c);
+                const float dl = v ? softplus_f(IO::e2(rdt[i], c) + dtb[c]) : 0.0f;
+                const float dy = (DISC == DISC_DB) ? dl * u : (v ? u : 0.0f);
+                s_dl[2 * cp + c][tt] = make_float2(dl, dy);
+                if constexpr (FINAL)
+                    s_gd[2 * cp + c][tt] = make_float2((Z != nullptr) ? silu_f(IO::e2(rz[i], c)) : 1.0f, Dd[c] * u);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                bv[j][s2] = IO::e4(rB[j], s2);
+                cv[j][s2] = FINAL ? IO::e4(rC[j], s2) : 0.0f;
+            }
+        if (it + 1 < ntiles) fetch(it + 1);
+        __syncthreads();
+        // scan role: two blocks of 16 tokens
+        static_for<2>([&](auto jI) {
+            constexpr int j = decltype(jI)::value;
+            static_for<4>([&](auto gI) {
+                constexpr int g4 = decltype(gI)::value;
+                const int t = 16 * j + 4 * g4;
+                const float4 d01 = *reinterpret_cast<const float4 *>(&s_dl[ch][t]);
+                const float4 d23 = *reinterpret_cast<const float4 *>(&s_dl[ch][t + 2]);
+                const float dl[4] = {d01.x, d01.z, d23.x, d23.z};
+                const float dy[4] = {d01.y, d01.w, d23.y, d23.w};
+                float part[4];
+                static_for<4>([&](auto iI) {
+                    constexpr int i = decltype(iI)::value;
+                    constexpr int kk = 4 * g4 + i;
+#pragma unroll
+                    for (int s2 = 0; s2 < 4; ++s2) {
+                        const float bq = row_bcast<kk>(bv[j][s2]);
+                        const float a = hw_exp2(dl[i] * A2[s2]);
+                        float w;
+                        if constexpr (DISC == DISC_DB)
+                            w = dy[i] * bq;
+                        else
+                            w = expm1f(dl[i] * An[s2]) * Ainv[s2] * bq * dy[i];
+                        h[s2] = fmaf(a, h[s2], w);
+                        if constexpr (FINAL)
+                            part[i] = (s2 == 0) ? row_bcast<kk>(cv[j][s2]) * h[s2]
+                                                : fmac_row_bcast<kk>(part[i], cv[j][s2], h[s2]);
+                    }
+                });
+                if constexpr (FINAL) {
+                    // token t + r of channel ch, over all sixteen states
+                    const float ys = rows_transpose_sum(part);
+                    const float2 gd = s_gd[ch][t + r];
+                    s_y[t + r][ch] = (ys + gd.y) * gd.x;
+                } else {
+                    ssum += (dl[0] + dl[1]) + (dl[2] + dl[3]);
+                }
+            });
+        });
+        if constexpr (FINAL) {
+            __syncthreads();
+            const buf_t bY = make_buf(Y + (b * L + ts) * D + d0, (uint64_t)((int64_t)nv * D - d0) * es);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int tt = rq + 8 * i;
+                IO::st2(bY, xo + i * xs, s_y[tt][2 * cp], s_y[tt][2 * cp + 1]);
+            }
+        }
+    }
+
+    if constexpr (FINAL) {
+        if (k == p.K - 1 && p.hT != nullptr)
+            *reinterpret_cast<float4 *>(p.hT + (b * D + d) * 16 + 4 * r) = make_float4(h[0], h[1], h[2], h[3]);
+    } else {
+        const int64_t o = (b * p.K + k) * D + d;
+        *reinterpret_cast<float4 *>(p.agg_h + o * 16 + 4 * r) = make_float4(h[0], h[1], h[2], h[3]);
+        if (r == 0) p.agg_s[o] = ssum;
+    }
+}
+
 template <typename IOT, int SPL, int DISC, bool CONV, int MODE>
 hipError_t launch_one(const FwdParams &p, hipStream_t s) {
     const int64_t blocks = (int64_t)p.groups * p.Kgrid * p.B;
@@ -706,6 +963,29 @@ hipError_t dispatch(const FwdParams &p, int bf16, int disc, bool conv, int mode,
     return dispatch_spl<float>(p, disc, conv, mode, s);
 }
 
+// The one-wavefront chunk scan covers N = 16, no fused conv, the input-driven
+// decay, and whole 16-channel groups.
+bool long_ok(int64_t D, int64_t N, int W, int disc) {
+    return N == 16 && W == 0 && (disc == DISC_DB || disc == DISC_ZOH) && D % 16 == 0;
+}
+
+template <typename IOT, int DISC>
+hipError_t launch_long_t(const FwdParams &p, int mode, hipStream_t s) {
+    const int64_t blocks = (int64_t)p.groups * p.Kgrid * p.B;
+    if (blocks <= 0) return hipSuccess;
+    if (mode == MODE_FINAL)
+        hipLaunchKernelGGL((scan_long_kernel<IOT, DISC, MODE_FINAL>), dim3((unsigned)blocks), dim3(64), 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_long_kernel<IOT, DISC, MODE_LOCAL>), dim3((unsigned)blocks), dim3(64), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t dispatch_long(const FwdParams &p, int bf16, int disc, int mode, hipStream_t s) {
+    if (bf16) return disc == DISC_DB ? launch_long_t<bf16_t, DISC_DB>(p, mode, s)
+                                     : launch_long_t<bf16_t, DISC_ZOH>(p, mode, s);
+    return disc == DISC_DB ? launch_long_t<float, DISC_DB>(p, mode, s) : launch_long_t<float, DISC_ZOH>(p, mode, s);
+}
+
 struct FwdWs {
     float *agg_h, *agg_s, *conv_copy;
 };
@@ -729,10 +1009,22 @@ int64_t num_chunks(int64_t L, int64_t chunk) {
 
 }  // namespace
 
-int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N) {
-    (void)N;
-    // aim for three four-wavefront blocks per CU (256 CUs)
+int64_t scan_fwd_auto_chunk(int64_t B, int64_t L, int64_t D, int64_t N, int W, int disc) {
     const int64_t blocks = B * ((D + kCPW - 1) / kCPW);
+    if (long_ok(D, N, W, disc) && blocks <= 256 && L >= 512) {
+        // one-wavefront chunks: at most three wavefronts per SIMD (1024 SIMDs;
+        // a grid past a whole number of wavefronts per SIMD leaves some SIMDs
+        // a round behind, so the count rounds down), chunks of at least 256
+        // tokens, a multiple of 64
+        int64_t K = 3072 / blocks;
+        K = std::min<int64_t>(K, L / 256);
+        if (K > 1) {
+            int64_t chunk = (L + K - 1) / K;
+            chunk = (chunk + 63) / 64 * 64;
+            if (chunk < L) return chunk;
+        }
+    }
+    // aim for three four-wavefront blocks per CU (256 CUs)
     if (blocks >= 512 || L <= 2 * kTile) return L > 0 ? L : 1;
     int64_t K = (768 + blocks - 1) / blocks;
     K = std::min<int64_t>(K, (L + 4 * kTile - 1) / (4 * kTile));
@@ -764,7 +1056,8 @@ hipError_t launch_scan_chunk_starts(const ScanFwdArgs &a, int64_t chunk, float *
     p.agg_h = agg_h; p.agg_s = agg_s;
     p.Kgrid = (int)K - 1;
     p.conv_hist = a.conv_state_in;
-    hipError_t e = dispatch(p, a.bf16, a.disc, a.W > 0, MODE_LOCAL, s);
+    hipError_t e = long_ok(a.D, a.N, a.W, a.disc) ? dispatch_long(p, a.bf16, a.disc, MODE_LOCAL, s)
+                                                  : dispatch(p, a.bf16, a.disc, a.W > 0, MODE_LOCAL, s);
     if (e != hipSuccess) return e;
     const int64_t total = a.B * a.D * a.N;
     hipLaunchKernelGGL(carry_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, a.A_log, a.h0,
@@ -798,7 +1091,9 @@ hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s) {
     p.Kgrid = (int)K - 1;
     p.init = nullptr; p.init_bstride = 0; p.init_kstride = 0;
     p.conv_hist = a.conv_state_in;
-    hipError_t e = dispatch(p, a.bf16, a.disc, conv, MODE_LOCAL, s);
+    const bool lng = long_ok(a.D, a.N, a.W, a.disc);
+    hipError_t e = lng ? dispatch_long(p, a.bf16, a.disc, MODE_LOCAL, s)
+                       : dispatch(p, a.bf16, a.disc, conv, MODE_LOCAL, s);
     if (e != hipSuccess) return e;
     // level 2: carries across chunks
     const int64_t total = a.B * a.D * a.N;
@@ -813,7 +1108,7 @@ hipError_t launch_scan_fwd(const ScanFwdArgs &a, hipStream_t s) {
     p.Kgrid = (int)K;
     p.init = w.agg_h; p.init_bstride = K * a.D * a.N; p.init_kstride = a.D * a.N;
     p.conv_hist = conv_count ? w.conv_copy : nullptr;
-    return dispatch(p, a.bf16, a.disc, conv, MODE_FINAL, s);
+    return lng ? dispatch_long(p, a.bf16, a.disc, MODE_FINAL, s) : dispatch(p, a.bf16, a.disc, conv, MODE_FINAL, s);
 }
 
 }  // namespace ssm

@@ -161,6 +161,45 @@ def test_fwd_chunked_matches_oracle(ssm, chunk, conv):
         np.testing.assert_array_equal(host(cso), csr)
 
 
+@pytest.mark.parametrize("L,chunk", [(333, 1), (333, 7), (333, 32), (333, 37), (333, 100), (1500, 0),
+                                     (64, 32), (40, 64)])
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_fwd_one_wavefront_chunks(ssm, L, chunk, disc):
+    """The time split of N = 16 scans without a fused conv runs one-wavefront
+    chunk scans (four states per lane): chunk lengths that leave ragged
+    32-token tiles and a partial last chunk, and the library's own choice
+    (L 1500 -> chunks of 320), against the sequential oracle."""
+    p = _rand(41, 2, L, 48, 16)
+    y, hT, _ = _fwd_gpu(ssm, p, torch.float32, conv=False, chunk=chunk, disc=disc)
+    yr, hr, _, _ = _fwd_oracle(p, conv=False, disc=disc)
+    assert rel_linf(y, yr) <= FP32_TOL
+    assert rel_linf(hT, hr) <= FP32_TOL
+
+
+@pytest.mark.parametrize("gate,h0,bf16", [(False, False, False), (True, False, True), (False, True, True)])
+def test_fwd_one_wavefront_chunks_options(ssm, gate, h0, bf16):
+    """One-wavefront chunks without the gate, from a zero or given state, in
+    bf16 I/O; Dskip zero in the first case."""
+    p = _rand(42, 3, 777, 32, 16, bf16=bf16)
+    if not gate:
+        p["Dskip"] = np.zeros_like(p["Dskip"])
+    dt = torch.bfloat16 if bf16 else torch.float32
+    y, hT, _ = _fwd_gpu(ssm, p, dt, conv=False, gate=gate, h0=h0, chunk=96)
+    yr, hr, _, _ = _fwd_oracle(p, conv=False, gate=gate, h0=h0)
+    assert rel_linf(y, yr) <= tol(dt)
+    assert rel_linf(hT, hr) <= tol(dt)
+
+
+def test_fwd_one_wavefront_chunks_match_unsplit(ssm):
+    """Split (one-wavefront chunks) and unsplit forwards agree to rounding."""
+    p = _rand(43, 1, 2048, 64, 16, slow=True)
+    a = _fwd_gpu(ssm, p, torch.float32, conv=False, chunk=-1)
+    b = _fwd_gpu(ssm, p, torch.float32, conv=False, chunk=256)
+    c = _fwd_gpu(ssm, p, torch.float32, conv=False, chunk=256)
+    assert rel_linf(b[0], a[0]) <= FP32_TOL and rel_linf(b[1], a[1]) <= FP32_TOL
+    assert torch.equal(b[0], c[0]) and torch.equal(b[1], c[1])
+
+
 def test_fwd_split_sequence_equals_whole(ssm):
     """fwd(x[:k]) then fwd(x[k:]) from the carried state and conv history
     gives the single call's outputs bit for bit."""
