@@ -106,6 +106,54 @@ __device__ __forceinline__ float tok_bcast(const float (&v)[TP], int i) {
     }
 }
 
+// One state-step of the reverse sweep in the dt*B form, token K of its
+// 16-token half (K = the row lane that holds the token's values dyv, dt*u
+// and dt, which every instruction reading them takes as a row-broadcast DPP
+// operand):
+//   gj = g + C dyv,  daa = gj h_prev a,  pt (+)= daa A,  pu (+)= gj B,
+//   bpart = gj dt u,  dA += daa dt,  cpart = h dyv,  g = a gj
+// with the operation order of the plain expressions (each result is the
+// same float).  Written out because the compiler keeps a broadcast read by
+// several instructions in a register of its own instead of folding it into
+// each of them.  The leading s_nop covers the two wait states a DPP read
+// needs after a VALU write of its source.
+template <int K, bool FIRST>
+__device__ __forceinline__ void rev_step_db(float &g, float &dA, float &pt, float &pu, float &bpart, float &cpart,
+                                            float cq, float bq, float hp, float hn, float a, float An,
+                                            float dyv, float du, float dl) {
+    float t;
+    if constexpr (FIRST)
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %[g], %[dyv], %[cq] row_newbcast:%[k] row_mask:0xf bank_mask:0xf\n\t"
+            "v_mul_f32_dpp %[cp], %[dyv], %[hn] row_newbcast:%[k] row_mask:0xf bank_mask:0xf\n\t"
+            "v_mul_f32_e32 %[t], %[g], %[hp]\n\t"
+            "v_mul_f32_dpp %[bp], %[du], %[g] row_newbcast:%[k] row_mask:0xf bank_mask:0xf\n\t"
+            "v_mul_f32_e32 %[pu], %[g], %[bq]\n\t"
+            "v_mul_f32_e32 %[t], %[t], %[a]\n\t"
+            "v_mul_f32_e32 %[g], %[g], %[a]\n\t"
+            "v_mul_f32_e32 %[pt], %[t], %[An]\n\t"
+            "v_fmac_f32_dpp %[dA], %[dl], %[t] row_newbcast:%[k] row_mask:0xf bank_mask:0xf"
+            : [g] "+v"(g), [dA] "+v"(dA), [t] "=&v"(t), [pt] "=&v"(pt), [pu] "=&v"(pu), [bp] "=&v"(bpart),
+              [cp] "=&v"(cpart)
+            : [dyv] "v"(dyv), [du] "v"(du), [dl] "v"(dl), [cq] "v"(cq), [bq] "v"(bq), [hp] "v"(hp), [hn] "v"(hn),
+              [a] "v"(a), [An] "v"(An), [k] "n"(K));
+    else
+        asm("s_nop 1\n\t"
+            "v_fmac_f32_dpp %[g], %[dyv], %[cq] row_newbcast:%[k] row_mask:0xf bank_mask:0xf\n\t"
+            "v_mul_f32_dpp %[cp], %[dyv], %[hn] row_newbcast:%[k] row_mask:0xf bank_mask:0xf\n\t"
+            "v_mul_f32_e32 %[t], %[g], %[hp]\n\t"
+            "v_mul_f32_dpp %[bp], %[du], %[g] row_newbcast:%[k] row_mask:0xf bank_mask:0xf\n\t"
+            "v_fmac_f32_e32 %[pu], %[g], %[bq]\n\t"
+            "v_mul_f32_e32 %[t], %[t], %[a]\n\t"
+            "v_mul_f32_e32 %[g], %[g], %[a]\n\t"
+            "v_fmac_f32_e32 %[pt], %[t], %[An]\n\t"
+            "v_fmac_f32_dpp %[dA], %[dl], %[t] row_newbcast:%[k] row_mask:0xf bank_mask:0xf"
+            : [g] "+v"(g), [dA] "+v"(dA), [t] "=&v"(t), [pt] "+v"(pt), [pu] "+v"(pu), [bp] "=&v"(bpart),
+              [cp] "=&v"(cpart)
+            : [dyv] "v"(dyv), [du] "v"(du), [dl] "v"(dl), [cq] "v"(cq), [bq] "v"(bq), [hp] "v"(hp), [hn] "v"(hn),
+              [a] "v"(a), [An] "v"(An), [k] "n"(K));
+}
+
 struct BwdParams {
     const void *u, *dt;      // u: the conv input x when the conv prologue is on
     const float *dt_bias, *A_log;
@@ -134,7 +182,7 @@ struct BwdParams {
     int G;                   // channel workgroups per batch row
 };
 
-template <typename IOT, int S, int DISC, bool CONV>
+template <typename IOT, int S, int DISC, bool CONV, bool GATE>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     using Gm = BGeo<S>;
     constexpr int NP = Gm::NP, T = Gm::T, TP = Gm::TP;
@@ -186,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     const int64_t d = d0 + cl;
     const bool dvalid = d < D;
     const int64_t dc = dvalid ? d : (D - 1);
-    const bool gate = Z != nullptr;
+    constexpr bool gate = GATE;   // z given (checked by the launcher)
 
     // this lane's states n = l + 16 s
     float A2[S], An[S], Ainv[S], am1[DISC == DISC_CONST ? S : 1];
@@ -568,69 +616,78 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             }
         }
 
-        // reverse sweep, in halves of 16 tokens for the per-token reductions
+        // reverse sweep, in halves of 16 tokens for the per-token reductions.
+        // dt*B form: the dt gradient is sum_n da a A + u sum_n g B, and the u
+        // gradient dt sum_n g B, so a state-step adds da a A to pt and g B to
+        // pu, and the factors u and dt are applied once per token below.
         float tk_gx[TP];
 #pragma unroll
         for (int jj = TP - 1; jj >= 0; --jj) {
             float pdt[16], pdu[16];
-#pragma unroll
-            for (int kk = 15; kk >= 0; --kk) {
+            static_for<16>([&](auto kc) {
+                constexpr int kk = 15 - decltype(kc)::value;
                 const int i = 16 * jj + kk;
                 pdt[kk] = 0.0f;
                 pdu[kk] = 0.0f;
                 if (i < T) {
-                    const float dyv = tokv(tk_dyv, i);
-                    const float dli = tokv(tk_dl, i);
-                    const float uu = tokv(tk_u, i);
-                    const float dui = (DISC == DISC_DB) ? tokv(tk_du, i) : uu;
                     float pt = 0.0f, pu = 0.0f;
+                    if constexpr (DISC == DISC_DB) {
+                        static_for<S>([&](auto sc) {
+                            constexpr int s = decltype(sc)::value;
+                            float bpart, cpart;
+                            rev_step_db<kk, s == 0>(g[s], dA[s], pt, pu, bpart, cpart, s_C[i * NP + l + 16 * s],
+                                                    s_B[i * NP + l + 16 * s], hs[i][s], hs[i + 1][s], as[i][s],
+                                                    An[s], tk_dyv[jj], tk_du[jj], tk_dl[jj]);
+                            // dB, dC terms of this channel; summed over channels below
+                            termB(i, cl, l + 16 * s) = bpart;
+                            termC(i, cl, l + 16 * s) = cpart;
+                        });
+                    } else {
+                        const float dyv = tokv(tk_dyv, i);
+                        const float dli = tokv(tk_dl, i);
+                        const float uu = tokv(tk_u, i);
 #pragma unroll
-                    for (int s = 0; s < S; ++s) {
-                        const float bq = s_B[i * NP + l + 16 * s];
-                        const float cq = s_C[i * NP + l + 16 * s];
-                        const float gj = fmaf(cq, dyv, g[s]);
-                        // as holds a - 1 for the constant decay
-                        const float a = (DISC == DISC_CONST) ? 1.0f + as[i][s] : as[i][s];
-                        const float daa = gj * hs[i][s] * a;
-                        float bpart;
-                        if constexpr (DISC == DISC_DB) {
-                            const float gB = gj * bq;
-                            pt = fmaf(daa, An[s], pt);
-                            pt = fmaf(gB, uu, pt);
-                            pu += gB;
-                            bpart = gj * dui;
-                            dA[s] = fmaf(daa, dli, dA[s]);
-                        } else if constexpr (DISC == DISC_CONST) {
-                            pu = fmaf(gj, bq, pu);
-                            bpart = gj * uu;
-                            dA[s] = fmaf(daa, dli, dA[s]);   // dt = 0 past the end
-                        } else {
-                            const float em1 = expm1f(dli * An[s]);
-                            const float cz = em1 * Ainv[s];
-                            const float gBu = gj * bq * uu;
-                            pt = fmaf(daa, An[s], pt);
-                            pt = fmaf(gBu, a, pt);
-                            pu = fmaf(gj * cz, bq, pu);
-                            bpart = gj * cz * uu;
-                            dA[s] = fmaf(daa, dli, dA[s]);
-                            dA[s] = fmaf(gBu * (dli * a * An[s] - em1), Ainv[s] * Ainv[s], dA[s]);
+                        for (int s = 0; s < S; ++s) {
+                            const float bq = s_B[i * NP + l + 16 * s];
+                            const float cq = s_C[i * NP + l + 16 * s];
+                            const float gj = fmaf(cq, dyv, g[s]);
+                            // as holds a - 1 for the constant decay
+                            const float a = (DISC == DISC_CONST) ? 1.0f + as[i][s] : as[i][s];
+                            const float daa = gj * hs[i][s] * a;
+                            float bpart;
+                            if constexpr (DISC == DISC_CONST) {
+                                pu = fmaf(gj, bq, pu);
+                                bpart = gj * uu;
+                                dA[s] = fmaf(daa, dli, dA[s]);   // dt = 0 past the end
+                            } else {
+                                const float em1 = expm1f(dli * An[s]);
+                                const float cz = em1 * Ainv[s];
+                                const float gBu = gj * bq * uu;
+                                pt = fmaf(daa, An[s], pt);
+                                pt = fmaf(gBu, a, pt);
+                                pu = fmaf(gj * cz, bq, pu);
+                                bpart = gj * cz * uu;
+                                dA[s] = fmaf(daa, dli, dA[s]);
+                                dA[s] = fmaf(gBu * (dli * a * An[s] - em1), Ainv[s] * Ainv[s], dA[s]);
+                            }
+                            const float cpart = hs[i + 1][s] * dyv;
+                            if constexpr (DISC == DISC_CONST)
+                                g[s] = fmaf(as[i][s], gj, gj);
+                            else
+                                g[s] = a * gj;
+                            // dB, dC terms of this channel; summed over channels below
+                            termB(i, cl, l + 16 * s) = bpart;
+                            termC(i, cl, l + 16 * s) = cpart;
                         }
-                        const float cpart = hs[i + 1][s] * dyv;
-                        if constexpr (DISC == DISC_CONST)
-                            g[s] = fmaf(as[i][s], gj, gj);
-                        else
-                            g[s] = a * gj;
-                        // dB, dC terms of this channel; summed over channels below
-                        termB(i, cl, l + 16 * s) = bpart;
-                        termC(i, cl, l + 16 * s) = cpart;
                     }
                     pdt[kk] = pt;
                     pdu[kk] = pu;
                 }
-            }
+            });
             // lane l finishes token l + 16 jj
-            const float ddt = (DISC != DISC_CONST) ? row_transpose_sum(pdt, l) : 0.0f;
+            float ddt = (DISC != DISC_CONST) ? row_transpose_sum(pdt, l) : 0.0f;
             const float dup = row_transpose_sum(pdu, l);
+            if constexpr (DISC == DISC_DB) ddt = fmaf(tk_u[jj], dup, ddt);
             tk_gx[jj] = 0.0f;
             if (tk_v[jj]) {
                 const int tt = l + 16 * jj;
@@ -1054,6 +1111,21 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk,
     return r;
 }
 
+template <typename IOT, int S, int DISC>
+void launch_bwd_main(bool conv, bool gate, dim3 grid, dim3 block, hipStream_t s, const BwdParams &p) {
+    if (conv) {
+        if (gate)
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, true, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, true, false>), grid, block, 0, s, p);
+    } else {
+        if (gate)
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, false, true>), grid, block, 0, s, p);
+        else
+            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, false, false>), grid, block, 0, s, p);
+    }
+}
+
 template <typename IOT, int S>
 hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s) {
     const int64_t KC = num_bwd_chunks(a.L, a.chunk);
@@ -1105,22 +1177,13 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
     p.G = G;
     const int64_t blocks = (int64_t)G * KC * a.B;
     const dim3 grid((unsigned)blocks), block(kThreads);
-    if (a.disc == DISC_ZOH) {
-        if (a.W > 0)
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH, true>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_ZOH, false>), grid, block, 0, s, p);
-    } else if (a.disc == DISC_CONST) {
-        if (a.W > 0)
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_CONST, true>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_CONST, false>), grid, block, 0, s, p);
-    } else {
-        if (a.W > 0)
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB, true>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC_DB, false>), grid, block, 0, s, p);
-    }
+    const bool conv = a.W > 0, gate = a.z != nullptr;
+    if (a.disc == DISC_ZOH)
+        launch_bwd_main<IOT, S, DISC_ZOH>(conv, gate, grid, block, s, p);
+    else if (a.disc == DISC_CONST)
+        launch_bwd_main<IOT, S, DISC_CONST>(conv, gate, grid, block, s, p);
+    else
+        launch_bwd_main<IOT, S, DISC_DB>(conv, gate, grid, block, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (KC > 1 && a.W > 1 && a.dx != nullptr) {

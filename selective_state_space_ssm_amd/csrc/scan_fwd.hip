@@ -223,17 +223,6 @@ __device__ __forceinline__ float rows_sum(float v) {
     return c + e;
 }
 
-// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (a loop whose
-// index is a constant expression, e.g. a DPP lane selector).
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
-    (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
 template <int K>
 __device__ __forceinline__ void lds_read_k(const float *p, float (&o)[K]) {
     if constexpr (K % 4 == 0) {

@@ -6,6 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace ssm {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -196,6 +199,17 @@ __device__ __forceinline__ float neg_exp_f(float a_log) { return -hw_exp2(a_log 
 __device__ __forceinline__ float sigmoid_f(float x) { return hw_rcp(1.0f + hw_exp2(-x * kLog2e)); }
 __device__ __forceinline__ float silu_f(float x) { return x * sigmoid_f(x); }
 
+// Calls f(std::integral_constant<int, I>) for I = 0 .. N-1 (a loop whose
+// index is a constant expression, e.g. a DPP lane selector).
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // ------------------------------------------------------------ DPP reductions
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -239,21 +253,42 @@ __device__ __forceinline__ float row_bcast(float v) {
 // receives the sum over its 16-lane row of p[l].  Pairings: l^15 (row
 // mirror), l^7 (half-row mirror), l^2, l^1; each lane keeps the half of the
 // tokens named by its own lane bit, so token bits end equal to lane bits.
+//
+// The first two pairings split the row at 4-lane bank boundaries (bit 3:
+// lanes 0-7 | 8-15; bit 2: lanes 0-3, 8-11 | 4-7, 12-15), so each half is
+// one DPP add whose bank mask limits the write to the lanes that keep that
+// token (the mask gates only the write, not the lanes the DPP reads from):
+// two instructions per pair instead of two selects and an add.  The DPP
+// read of a register written by the preceding VALU instruction needs two
+// wait states, which the compiler does not see inside asm: each block opens
+// with s_nop 1.  All 64 lanes must be active.
 __device__ __forceinline__ float row_transpose_sum(const float (&p)[16], int l) {
     float v8[8], v4[4], v2[2];
-    const bool b3 = (l & 8) != 0, b2 = (l & 4) != 0, b1 = (l & 2) != 0, b0 = (l & 1) != 0;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const float mine = b3 ? p[k + 8] : p[k];
-        const float send = b3 ? p[k] : p[k + 8];
-        v8[k] = mine + dpp_f<kDppRowMirror>(send);
-    }
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const float mine = b2 ? v8[k + 4] : v8[k];
-        const float send = b2 ? v8[k] : v8[k + 4];
-        v4[k] = mine + dpp_f<kDppRowHalfMirror>(send);
-    }
+#define SSM_BANK_PAIR(CTRL, LO, HI, O, X, Y)                                             \
+    "v_add_f32_dpp %" #O ", %" #X ", %" #X " " CTRL " row_mask:0xf bank_mask:" LO "\n\t" \
+    "v_add_f32_dpp %" #O ", %" #Y ", %" #Y " " CTRL " row_mask:0xf bank_mask:" HI "\n\t"
+    asm("s_nop 1\n\t"
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 0, 8, 16)
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 1, 9, 17)
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 2, 10, 18)
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 3, 11, 19)
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 4, 12, 20)
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 5, 13, 21)
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 6, 14, 22)
+        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 7, 15, 23)
+        : "=&v"(v8[0]), "=&v"(v8[1]), "=&v"(v8[2]), "=&v"(v8[3]),
+          "=&v"(v8[4]), "=&v"(v8[5]), "=&v"(v8[6]), "=&v"(v8[7])
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]),
+          "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
+    asm("s_nop 1\n\t"
+        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 0, 4, 8)
+        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 1, 5, 9)
+        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 2, 6, 10)
+        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 3, 7, 11)
+        : "=&v"(v4[0]), "=&v"(v4[1]), "=&v"(v4[2]), "=&v"(v4[3])
+        : "v"(v8[0]), "v"(v8[1]), "v"(v8[2]), "v"(v8[3]), "v"(v8[4]), "v"(v8[5]), "v"(v8[6]), "v"(v8[7]));
+#undef SSM_BANK_PAIR
+    const bool b1 = (l & 2) != 0, b0 = (l & 1) != 0;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
         const float mine = b1 ? v4[k + 2] : v4[k];
