@@ -194,13 +194,15 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     constexpr int XL = (XE + kThreads - 1) / kThreads;   // staged per thread
     constexpr int XUL = (XUE + kThreads - 1) / kThreads;
     constexpr int BL = (BE + kThreads - 1) / kThreads;
+    constexpr int RPL = kThreads / kCPB;   // tile rows of one whole-workgroup load
     __shared__ float s_u[XUEP], s_dt[XEP], s_z[XEP], s_dy[XEP];
     __shared__ float s_B[BE], s_C[BE];
     // per-channel dB, dC terms; each token's slab padded by 16 words so that the
     // two tokens a 32-lane half reads land on opposite bank halves
-    __shared__ float s_rB[T][kCPB * NP + 16], s_rC[T][kCPB * NP + 16];
-    auto termB = [&](int i, int c, int n) -> float & { return s_rB[i][c * NP + n]; };
-    auto termC = [&](int i, int c, int n) -> float & { return s_rC[i][c * NP + n]; };
+    constexpr int TSL = kCPB * NP + 16;
+    __shared__ float s_rB[T * TSL], s_rC[T * TSL];
+    auto termB = [&](int i, int c, int n) -> float & { return s_rB[i * TSL + c * NP + n]; };
+    auto termC = [&](int i, int c, int n) -> float & { return s_rC[i * TSL + c * NP + n]; };
     __shared__ float s_gx[CONV ? (T + 7) * kXR : 1];       // conv-output gradient, tile + 7 following
     __shared__ float s_wk[CONV ? kCPB * 8 : 1];              // conv taps, right-aligned in 8 slots
     // outputs of the finished tile, written to memory one tile later (below)
@@ -379,34 +381,36 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     // per-token quantities of this lane's tokens tt = l + 16 jj of the tile;
     // tokens past L get dt = u = 0, which leaves the state unchanged
     float tk_dl[TP], tk_du[TP], tk_u[TP], tk_xc[TP];
-    auto transform_fwd = [&](int64_t ts) {
+    // (su, sdt: the staged rows, the tile starting at row r0)
+    auto transform_at = [&](const float *su, const float *sdt, int r0, int64_t ts) {
 #pragma unroll
         for (int jj = 0; jj < TP; ++jj) {
             const int tt = l + 16 * jj;
             const bool v = tt < T && ts + tt < Le;
-            const int tc = min(tt, T - 1);
+            const int tc = r0 + min(tt, T - 1);
             const int e = tc * kXR + cl;
             float uu;
             if constexpr (CONV) {
                 float acc = cb;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], s_u[(tc + i) * kXR + cl], acc);
+                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], su[(tc + i) * kXR + cl], acc);
                 tk_xc[jj] = acc;
                 uu = v ? silu_f(acc) : 0.0f;
             } else {
                 tk_xc[jj] = 0.0f;
-                uu = v ? s_u[e] : 0.0f;
+                uu = v ? su[e] : 0.0f;
             }
             float dl;
             if constexpr (DISC == DISC_CONST)
                 dl = v ? 1.0f : 0.0f;
             else
-                dl = v ? softplus_f(s_dt[e] + dtb) : 0.0f;
+                dl = v ? softplus_f(sdt[e] + dtb) : 0.0f;
             tk_dl[jj] = dl;
             tk_u[jj] = uu;
             tk_du[jj] = (DISC == DISC_DB) ? dl * uu : uu;
         }
     };
+    auto transform_fwd = [&](int64_t ts) { transform_at(s_u, s_dt, 0, ts); };
     // token i's per-token value, broadcast across the row from lane i mod 16
     auto tokv = [&](const float (&v)[TP], int i) -> float { return tok_bcast<TP>(v, i); };
 
@@ -415,15 +419,85 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < S; ++s)
         h[s] = (p.h0 != nullptr && sv[s]) ? p.h0[b * p.h0_bs + kc * p.h0_ks + dc * N + l + 16 * s] : 0.0f;
-    // A wait for loaded data also waits for every store still in flight, so
-    // each store is issued right after a wait and has a whole tile of work
-    // to complete before the next one.
-    auto store_ckpt = [&](int k) {
-        if (dvalid) {
+    // The checkpoint of a tile is one buffer store per state slot on every
+    // lane (lanes without a state, or past D, store out of range, which
+    // drops the write): the same number of memory operations per tile on
+    // every path, so that the compiler's waits for a prefetched tile stay
+    // exact.
+    const uint32_t ck_oob = (uint32_t)(D * N) * 4u;
+    auto store_ckpt = [&](int k) {   // tiles past the chunk store nothing
+        const buf_t bK = make_buf(p.ckpt + (b * Kt + tile0 + k) * D * N, (uint64_t)(D * N) * 4u);
 #pragma unroll
-            for (int s = 0; s < S; ++s)
-                if (sv[s]) p.ckpt[((b * Kt + tile0 + k) * D + d) * N + l + 16 * s] = h[s];
+        for (int s = 0; s < S; ++s)
+            buf_st(bK, (k < K && dvalid && sv[s]) ? (uint32_t)(d * N + l + 16 * s) * 4u : ck_oob, p.ckpt, h[s]);
+    };
+    // The walk stages T1 = 64 tokens (T1P tiles) per step, in the channel-sum
+    // slabs of the sweep below (not in use yet), and fetches the next step
+    // while walking this one: a step of several tiles pays the barriers, the
+    // descriptor arithmetic and the memory latency once.  Staging writes are
+    // whole-workgroup loads without lane masks (the slack rows are never
+    // read); past the end of the chunk, and for a conv sequence's first step
+    // (whose history rows come from conv_state_in and are loaded when staged),
+    // the fetch reads through an empty range.
+    constexpr int T1 = 64, T1P = T1 / T;
+    constexpr int X1UL = ((T1 + XH) * kCPB + kThreads - 1) / kThreads;
+    constexpr int X1L = (T1 * kCPB + kThreads - 1) / kThreads;
+    constexpr int B1L = (T1 * NP + kThreads - 1) / kThreads;
+    float *const s1_u = s_rB;                             // row r: token ts + r - XH
+    float *const s1_dt = s_rB + X1UL * RPL * kXR;         // row r: token ts + r
+    float *const s1_B = s_rC;                             // [T1][NP]
+    static_assert((X1UL + X1L) * RPL * kXR <= T * TSL && B1L * kThreads <= T * TSL, "walk staging fits the slabs");
+    static_assert(kThreads % NP == 0, "B rows of a whole-workgroup load");
+    raw_t qu[2][X1UL], qdt[2][X1L], qB[2][B1L];
+    auto fetch1 = [&](int m, raw_t (&xu)[X1UL], raw_t (&xdt)[X1L], raw_t (&xB)[B1L]) {
+        // addresses only: with an empty range nothing at them is touched
+        const int64_t ts = (int64_t)(tile0 + m * T1P) * T;
+        const int64_t rows = max(Le - ts, (int64_t)0);
+        const bool empty = rows == 0 || (CONV && ts < XH);
+        const int64_t row0 = (b * L + ts) * D + d0;
+        const buf_t bU = make_buf(U + (row0 - XH * D), empty ? 0 : (uint64_t)((rows + XH) * D - d0) * es);
+#pragma unroll
+        for (int q = 0; q < X1UL; ++q) xu[q] = buf_ld_raw(bU, xoff + q * xstep, U);
+        if constexpr (DISC != DISC_CONST) {
+            const buf_t bDT = make_buf(DT + row0, rows ? (uint64_t)(rows * D - d0) * es : 0);
+#pragma unroll
+            for (int q = 0; q < X1L; ++q) xdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
         }
+        const buf_t bB = make_buf(Bp + (b * L + ts) * N, (uint64_t)(rows * N) * es);
+#pragma unroll
+        for (int q = 0; q < B1L; ++q) xB[q] = buf_ld_raw(bB, boff + q * bstep, Bp);
+    };
+    auto stage1 = [&](int m, const raw_t (&xu)[X1UL], const raw_t (&xdt)[X1L], const raw_t (&xB)[B1L]) {
+        const int64_t ts = (int64_t)(tile0 + m * T1P) * T;
+        if (CONV && ts < XH) {
+            for (int e = tid; e < (T1 + XH) * kCPB; e += kThreads) {
+                const int rr = e / kCPB, cc = e % kCPB;
+                const int64_t t = ts + rr - XH;
+                float v = 0.0f;
+                if (t < Le && d0 + cc < D) {
+                    if (t >= 0)
+                        v = to_f32(U[(b * L + t) * D + d0 + cc]);
+                    else if (p.conv_hist != nullptr && t >= -(int64_t)(W - 1))
+                        v = p.conv_hist[(b * (W - 1) + (W - 1) + t) * D + d0 + cc];
+                }
+                s1_u[rr * kXR + cc] = v;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < X1UL; ++q) {
+                const int e = q * kThreads + tid;
+                s1_u[(e / kCPB) * kXR + e % kCPB] = raw_f32(xu[q], U);
+            }
+        }
+        if constexpr (DISC != DISC_CONST) {
+#pragma unroll
+            for (int q = 0; q < X1L; ++q) {
+                const int e = q * kThreads + tid;
+                s1_dt[(e / kCPB) * kXR + e % kCPB] = raw_f32(xdt[q], DT);
+            }
+        }
+#pragma unroll
+        for (int q = 0; q < B1L; ++q) s1_B[q * kThreads + tid] = nval ? raw_f32(xB[q], Bp) : 0.0f;
     };
     // Values loaded before the tile loops and first used inside them are
     // consumed here, before any tile is requested: left pending, they would
@@ -432,39 +506,50 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < S; ++s) asm volatile("" : "+v"(h[s]));
     asm volatile("" : "+v"(dtb), "+v"(Dd), "+v"(cb));
-    if (K > 1) fetch(0, false);
-    for (int k = 0; k < K; ++k) {
-        if (k + 1 == K) {   // the last tile's end state is not needed
-            store_ckpt(k);
-            break;
-        }
-        __syncthreads();
-        stage(false, k);
-        __syncthreads();
-        store_ckpt(k);
-        if (k + 2 < K) fetch(k + 1, false);
-        transform_fwd((int64_t)(tile0 + k) * T);
+    const int M1 = (K + T1P - 1) / T1P;   // steps
+    fetch1(0, qu[0], qdt[0], qB[0]);
+    for (int m0 = 0; m0 < M1; m0 += 2) {
+        static_for<2>([&](auto jc) {
+            constexpr int j = decltype(jc)::value;
+            const int m = m0 + j;
+            if (m < M1) {
+                __syncthreads();
+                stage1(m, qu[j], qdt[j], qB[j]);
+                __syncthreads();
+                fetch1(m + 1, qu[1 - j], qdt[1 - j], qB[1 - j]);
+#pragma unroll 1
+                for (int jt = 0; jt < T1P; ++jt) {
+                    const int k = m * T1P + jt;
+                    store_ckpt(k);
+                    if (k + 1 < K) {   // the last tile's end state is not needed
+                        transform_at(s1_u, s1_dt, jt * T, (int64_t)(tile0 + k) * T);
 #pragma unroll
-        for (int i = 0; i < T; ++i) {
-            const float dli = tokv(tk_dl, i), dui = tokv(tk_du, i);
+                        for (int i = 0; i < T; ++i) {
+                            const float dli = tokv(tk_dl, i), dui = tokv(tk_du, i);
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const float bq = s_B[i * NP + l + 16 * s];
-                if constexpr (DISC == DISC_CONST) {
-                    // dt is 1, or 0 past the end (no decay, no write there)
-                    h[s] += fmaf(dli * am1[s], h[s], dui * bq);
-                } else {
-                    const float a = hw_exp2(dli * A2[s]);
-                    float w;
-                    if constexpr (DISC == DISC_DB)
-                        w = dui * bq;
-                    else
-                        w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
-                    h[s] = fmaf(a, h[s], w);
+                            for (int s = 0; s < S; ++s) {
+                                const float bq = s1_B[(jt * T + i) * NP + l + 16 * s];
+                                if constexpr (DISC == DISC_CONST) {
+                                    // dt is 1, or 0 past the end (no decay, no write there)
+                                    h[s] += fmaf(dli * am1[s], h[s], dui * bq);
+                                } else {
+                                    const float a = hw_exp2(dli * A2[s]);
+                                    float w;
+                                    if constexpr (DISC == DISC_DB)
+                                        w = dui * bq;
+                                    else
+                                        w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
+                                    h[s] = fmaf(a, h[s], w);
+                                }
+                            }
+                        }
+                    }
                 }
             }
-        }
+        });
     }
+    // the slabs are reused by the sweep
+    __syncthreads();
     // the checkpoints are read back by lanes of this workgroup only
     __threadfence_block();
 
