@@ -264,7 +264,8 @@ ssm_status ssm_scan_bwd_workspace_size(const ssm_scan_desc *desc, size_t *bytes)
     if (st != SSM_OK) return st;
     if (!bytes) return SSM_ERR_NULL_ARG;
     const int64_t chunk = ssm::scan_bwd_chunk(desc->batch, desc->seqlen, desc->dim, desc->dstate, desc->chunk_len);
-    *bytes = ssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim, desc->dstate, chunk);
+    *bytes = ssm::scan_bwd_workspace_bytes(desc->batch, desc->seqlen, desc->dim, desc->dstate, chunk,
+                                           desc->conv_width, io_size(desc->io_dtype));
     return SSM_OK;
 }
 
@@ -298,10 +299,11 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
     {
         const int64_t KC = cdiv(std::max<int64_t>(L, 1), chunk);   // chunks along time
         if (!grid_ok({Bn, cdiv(D, 48), KC}) || !grid_ok({Bn, cdiv(std::max<int64_t>(L, 1) * N, 256)}) ||
-            !grid_ok({Bn, KC, cdiv(8 * D, 256)}) || !grid_ok({Bn, cdiv(D * N, 256)}))
+            !grid_ok({Bn, KC, cdiv(8 * D, 256)}) || !grid_ok({Bn, cdiv(D * N, 256)}) ||
+            (W > 0 && !grid_ok({Bn, cdiv(cdiv(std::max<int64_t>(L, 1), 32) * D, 256)})))   // conv, conv backward
             return SSM_ERR_BAD_SHAPE;
     }
-    const size_t need = ssm::scan_bwd_workspace_bytes(Bn, L, D, N, chunk);
+    const size_t need = ssm::scan_bwd_workspace_bytes(Bn, L, D, N, chunk, W, io_size(desc->io_dtype));
     if (!workspace || workspace_bytes < need) return SSM_ERR_WORKSPACE;
     const int64_t es = io_size(desc->io_dtype);
     const int64_t nbld = Bn * L * D, nbln = Bn * L * N, nbdn = Bn * D * N, nst = Bn * (W > 0 ? W - 1 : 0) * D;

@@ -20,6 +20,21 @@ struct ConvArgs {
 };
 hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s);
 
+// Backward of u = SiLU(conv(x)) from du = dLoss/du: dx, the tap and bias
+// gradients and the carried history's gradient (each output may be null).
+struct ConvBwdArgs {
+    int64_t B, L, D;
+    int W;
+    int bf16;
+    const void *x, *du;                  // [B, L, D] io
+    const float *w, *b, *state_in;       // [D, W], [D] (null: 0), [B, W-1, D] (null: zeros)
+    void *dx;                            // [B, L, D] io
+    float *dw, *db, *dstate;             // [D, W], [D], [B, W-1, D]
+    float *ws;                           // conv1d_bwd_workspace_bytes
+};
+size_t conv1d_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D);
+hipError_t launch_conv1d_bwd(const ConvBwdArgs &a, hipStream_t s);
+
 struct ScanFwdArgs {
     int64_t B, L, D, N;
     int W;          // 0: no fused conv
@@ -78,7 +93,8 @@ struct ScanBwdArgs {
 // Time-chunk length of the backward for this shape and request (0: the
 // library's choice, -1: never split, > 0: rounded up to a multiple of 64).
 int64_t scan_bwd_chunk(int64_t B, int64_t L, int64_t D, int64_t N, int64_t requested);
-size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk);
+// W: conv width (0: none), es: bytes per io element
+size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk, int W, int64_t es);
 hipError_t launch_scan_bwd(const ScanBwdArgs &a, hipStream_t s);
 
 struct StepArgs {

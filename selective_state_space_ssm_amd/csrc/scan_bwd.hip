@@ -18,10 +18,8 @@
 //           decays close to 1 accurate
 //   gate:   dyv = dy*z*s,  dz = dy*yv*s*(1 + z*(1-s)),  s = sigmoid(z)
 //   dA_log = A * dA,  d_dt_raw = ddt * sigmoid(dt_raw + dt_bias)
-//   conv:   u = SiLU(xc),  xc_t = cb + sum_k w_k x_{t-(W-1)+k}  ("mamba, live", the
-//           causal conv before the scan): gx_t = du_t * s(1 + xc(1-s)), s = sigmoid(xc);
-//           dx_t = sum_k w_k gx_{t+(W-1)-k},  dw_k += gx_t x_{t-(W-1)+k},  dcb += gx_t;
-//           inputs before t = 0 come from the carried history, which gets dx too
+// With the conv prologue the conv and its backward run as kernels of their
+// own around this one (conv1d.hip, launch_scan_bwd below).
 //
 // Work decomposition.  A workgroup of twelve wavefronts owns 48 channels of
 // one batch row (256 workgroups at batch 8, D = 1536: one per CU).  Each
@@ -41,15 +39,7 @@
 //           is rebuilt for dz), then sweep it backwards.
 // Each tile's inputs are loaded into registers one tile ahead and staged in
 // LDS.  Two small kernels add the per-workgroup dB, dC partials and the
-// per-batch dA_log, dDskip, d_dt_bias (and conv tap and bias) partials, in a
-// fixed order.
-//
-// With the conv prologue the raw input x is staged with 7 rows of history
-// in front of the tile and u is recomputed from it in both phases, with the
-// forward kernel's operation order (right-aligned 8-tap window).  gx, the
-// gradient at the conv output, goes to LDS rows 0..T-1; rows T..T+6 hold the
-// first 7 tokens of the following tile (finished before it), so the dx of
-// every token of the tile reads its 8 gx values from there.
+// per-batch dA_log, dDskip, d_dt_bias partials, in a fixed order.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -79,6 +69,8 @@ constexpr int kXR = 50;
 // s_waitcnt immediate for "all vector memory operations done" (vmcnt 0,
 // expcnt and lgkmcnt left at their maxima)
 constexpr int kWaitVm0 = 0x0F70;
+
+constexpr int up4(int n) { return (n + 3) & ~3; }
 
 // Token i's per-token value of a 16-lane row, broadcast across the row from
 // lane i mod 16 (entry i / 16 of the lane's array).  i is a compile-time
@@ -155,7 +147,7 @@ __device__ __forceinline__ void rev_step_db(float &g, float &dA, float &pt, floa
 }
 
 struct BwdParams {
-    const void *u, *dt;      // u: the conv input x when the conv prologue is on
+    const void *u, *dt;
     const float *dt_bias, *A_log;
     const void *Bm, *Cm;
     const float *Dskip;
@@ -164,50 +156,54 @@ struct BwdParams {
     const float *h0, *dhT;   // start state and end adjoint of each chunk:
     int64_t h0_bs, h0_ks;    //   element (b, k) at b * bs + k * ks (floats)
     int64_t dhT_bs, dhT_ks;
-    const float *conv_w, *conv_b, *conv_hist;   // [D, W], [D], [B, W-1, D]
-    float *dhist;            // [B, W-1, D] gradient of the carried history
-    float *bnd;              // [B, KC, W-1, D] the same for chunks 1.. (their first W-1 inputs' left part)
     float *ckpt;             // [B, Kt, D, N] states at tile starts
     void *du, *ddt, *dz;
     float *dh0;
     float *pB, *pC;          // [G, B, L, N] per-workgroup channel partials
     float *pA;               // [B, KC, D, N] dLoss/dA summed over each chunk
     float *pD, *pT;          // [B, KC, D]    dDskip, d_dt_bias summed over each chunk
-    float *pW, *pCb;         // [B, KC, D, 8] (taps right-aligned), [B, KC, D]: conv taps, bias
     int64_t B, L, D, N;
-    int W;
     int Kt;                  // tiles along the whole sequence
     int64_t chunk;           // tokens per time chunk (a multiple of 64)
     int KC;                  // time chunks
     int G;                   // channel workgroups per batch row
 };
 
-template <typename IOT, int S, int DISC, bool CONV, bool GATE>
+template <typename IOT, int S, int DISC, bool GATE>
 __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     using Gm = BGeo<S>;
     constexpr int NP = Gm::NP, T = Gm::T, TP = Gm::TP;
     constexpr int XE = T * kCPB;          // elements of one [T][48] tile
-    constexpr int XH = CONV ? 7 : 0;      // history rows staged in front of the first input
-    constexpr int XUE = (T + XH) * kCPB;
-    constexpr int XEP = T * kXR, XUEP = (T + XH) * kXR;   // padded LDS sizes
+    constexpr int XEP = T * kXR;          // padded LDS size
     constexpr int BE = T * NP;            // elements of one [T][NP] tile
     constexpr int XL = (XE + kThreads - 1) / kThreads;   // staged per thread
-    constexpr int XUL = (XUE + kThreads - 1) / kThreads;
     constexpr int BL = (BE + kThreads - 1) / kThreads;
     constexpr int RPL = kThreads / kCPB;   // tile rows of one whole-workgroup load
-    __shared__ float s_u[XUEP], s_dt[XEP], s_z[XEP], s_dy[XEP];
-    __shared__ float s_B[BE], s_C[BE];
+    // One LDS block carved by hand: the per-tile arrays first, so that all of
+    // them lie within reach of the 16-bit offset field of the LDS
+    // instructions (one base register per access pattern instead of one per
+    // array), the two channel-sum slabs last.  Offsets in floats, multiples
+    // of 4.
+    constexpr int TSL = kCPB * NP + 16;   // one token's slab of channel terms (see below)
+    constexpr int O_U = 0;
+    constexpr int O_DT = O_U + up4(XEP), O_Z = O_DT + up4(XEP), O_DY = O_Z + up4(XEP);
+    constexpr int O_B = O_DY + up4(XEP), O_C = O_B + up4(BE);
+    constexpr int O_ODX = O_C + up4(BE), O_ODDT = O_ODX + up4(XEP), O_ODZ = O_ODDT + up4(XEP);
+    constexpr int O_OB = O_ODZ + up4(XEP), O_OC = O_OB + up4(BE);
+    constexpr int O_RB = O_OC + up4(BE), O_RC = O_RB + T * TSL, O_END = O_RC + T * TSL;
+    __shared__ __align__(16) float s_lds[O_END];
+    float *const s_u = s_lds + O_U;       // [T][kXR]
+    float *const s_dt = s_lds + O_DT;     // [T][kXR]
+    float *const s_z = s_lds + O_Z, *const s_dy = s_lds + O_DY;
+    float *const s_B = s_lds + O_B, *const s_C = s_lds + O_C;   // [T][NP]
+    // outputs of the finished tile, written to memory one tile later (below)
+    float *const s_odx = s_lds + O_ODX, *const s_oddt = s_lds + O_ODDT, *const s_odz = s_lds + O_ODZ;
+    float *const s_oB = s_lds + O_OB, *const s_oC = s_lds + O_OC;
     // per-channel dB, dC terms; each token's slab padded by 16 words so that the
     // two tokens a 32-lane half reads land on opposite bank halves
-    constexpr int TSL = kCPB * NP + 16;
-    __shared__ float s_rB[T * TSL], s_rC[T * TSL];
+    float *const s_rB = s_lds + O_RB, *const s_rC = s_lds + O_RC;
     auto termB = [&](int i, int c, int n) -> float & { return s_rB[i * TSL + c * NP + n]; };
     auto termC = [&](int i, int c, int n) -> float & { return s_rC[i * TSL + c * NP + n]; };
-    __shared__ float s_gx[CONV ? (T + 7) * kXR : 1];       // conv-output gradient, tile + 7 following
-    __shared__ float s_wk[CONV ? kCPB * 8 : 1];              // conv taps, right-aligned in 8 slots
-    // outputs of the finished tile, written to memory one tile later (below)
-    __shared__ float s_odx[XEP], s_oddt[XEP], s_odz[XEP];
-    __shared__ float s_oB[BE], s_oC[BE];
 
     const IOT *U = static_cast<const IOT *>(p.u);
     const IOT *DT = static_cast<const IOT *>(p.dt);
@@ -253,19 +249,6 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     }
     float dtb = p.dt_bias ? p.dt_bias[dc] : 0.0f;
     float Dd = p.Dskip ? p.Dskip[dc] : 0.0f;
-    // conv taps right-aligned in an 8-tap window (slot 7 multiplies the
-    // current input), kept in LDS; first read after the tile loop's barriers
-    const int W = p.W;
-    float cb = 0.0f;
-    if constexpr (CONV) {
-        if (tid < kCPB * 8) {
-            const int kk = (tid & 7) - (8 - W);
-            const int64_t dd = (d0 + (tid >> 3) < D) ? d0 + (tid >> 3) : D - 1;
-            s_wk[tid] = (kk >= 0) ? p.conv_w[dd * W + kk] : 0.0f;
-        }
-        cb = p.conv_b ? p.conv_b[dc] : 0.0f;
-    }
-    const float *wk = s_wk + cl * 8;
 
     // ---- tile staging: registers one tile ahead, then LDS.  Loads go through
     // buffer descriptors whose range ends at the end of the chunk (tokens past
@@ -273,8 +256,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     // base, and are kept as raw io bits until staged.  Channels past D read
     // neighbouring finite values that only feed lanes whose results are not
     // stored; states past N are zeroed when staged (B and C must be zero
-    // there).  The first tile of a conv sequence, whose history rows come from
-    // conv_state_in, is loaded when staged instead (once per phase).
+    // there).
     static_assert(kThreads % kCPB == 0 && kThreads % NP == 0, "offset strides");
     typedef typename RawOf<IOT>::type raw_t;
     const uint32_t es = sizeof(IOT);
@@ -283,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     const uint32_t boff = (uint32_t)((tid / NP) * (int)N + tid % NP) * es;
     const uint32_t bstep = (uint32_t)((kThreads / NP) * (int)N) * es;
     const uint32_t ckoff = (uint32_t)(dc * N + l) * 4u;
-    raw_t ru[XUL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL];
+    raw_t ru[XL], rdt[XL], rz[XL], rdy[XL], rB[BL], rC[BL];
     uint32_t rck[S];
     auto fetch = [&](int k, bool bwd) {
         const int64_t ts = (int64_t)(tile0 + k) * T;
@@ -294,12 +276,12 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
             for (int s = 0; s < S; ++s) rck[s] = buf_ld_raw(bK, ckoff + 64u * s, p.ckpt);
         }
-        if (!(CONV && ts < XH)) {
-            const buf_t bU = make_buf(U + (b * L + ts - XH) * D + d0, (uint64_t)((rows + XH) * D - d0) * es);
-#pragma unroll
-            for (int q = 0; q < XUL; ++q) ru[q] = buf_ld_raw(bU, xoff + q * xstep, U);
-        }
         const uint64_t xr = (uint64_t)(rows * D - d0) * es;
+        {
+            const buf_t bU = make_buf(U + (b * L + ts) * D + d0, xr);
+#pragma unroll
+            for (int q = 0; q < XL; ++q) ru[q] = buf_ld_raw(bU, xoff + q * xstep, U);
+        }
         if constexpr (DISC != DISC_CONST) {
             const buf_t bDT = make_buf(DT + (b * L + ts) * D + d0, xr);
 #pragma unroll
@@ -334,33 +316,13 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         // below are lane-masked, and a wait inside a masked block would not
         // count for the code after it.
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        const int64_t ts = (int64_t)(tile0 + k) * T;
-        if (CONV && ts < XH) {
-            // row r holds token ts + r - XH; before 0 the carried history
-            for (int e = tid; e < XUE; e += kThreads) {
-                const int rr = e / kCPB, cc = e % kCPB;
-                const int64_t t = ts + rr - XH;
-                float v = 0.0f;
-                if (t < Le && d0 + cc < D) {
-                    if (t >= 0)
-                        v = to_f32(U[(b * L + t) * D + d0 + cc]);
-                    else if (p.conv_hist != nullptr && t >= -(int64_t)(W - 1))
-                        v = p.conv_hist[(b * (W - 1) + (W - 1) + t) * D + d0 + cc];
-                }
-                s_u[rr * kXR + cc] = v;
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < XUL; ++q) {
-                const int e = q * kThreads + tid;
-                if (e < XUE) s_u[(e / kCPB) * kXR + e % kCPB] = raw_f32(ru[q], U);
-            }
-        }
+        (void)k;
 #pragma unroll
         for (int q = 0; q < XL; ++q) {
             const int e = q * kThreads + tid;
             if (e < XE) {
                 const int ep = (e / kCPB) * kXR + e % kCPB;
+                s_u[ep] = raw_f32(ru[q], U);
                 if constexpr (DISC != DISC_CONST) s_dt[ep] = raw_f32(rdt[q], DT);
                 if (bwd) {
                     s_z[ep] = raw_f32(rz[q], Z);
@@ -380,7 +342,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 
     // per-token quantities of this lane's tokens tt = l + 16 jj of the tile;
     // tokens past L get dt = u = 0, which leaves the state unchanged
-    float tk_dl[TP], tk_du[TP], tk_u[TP], tk_xc[TP];
+    float tk_dl[TP], tk_du[TP], tk_u[TP];
     // (su, sdt: the staged rows, the tile starting at row r0)
     auto transform_at = [&](const float *su, const float *sdt, int r0, int64_t ts) {
 #pragma unroll
@@ -389,17 +351,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             const bool v = tt < T && ts + tt < Le;
             const int tc = r0 + min(tt, T - 1);
             const int e = tc * kXR + cl;
-            float uu;
-            if constexpr (CONV) {
-                float acc = cb;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], su[(tc + i) * kXR + cl], acc);
-                tk_xc[jj] = acc;
-                uu = v ? silu_f(acc) : 0.0f;
-            } else {
-                tk_xc[jj] = 0.0f;
-                uu = v ? su[e] : 0.0f;
-            }
+            const float uu = v ? su[e] : 0.0f;
             float dl;
             if constexpr (DISC == DISC_CONST)
                 dl = v ? 1.0f : 0.0f;
@@ -436,30 +388,27 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     // while walking this one: a step of several tiles pays the barriers, the
     // descriptor arithmetic and the memory latency once.  Staging writes are
     // whole-workgroup loads without lane masks (the slack rows are never
-    // read); past the end of the chunk, and for a conv sequence's first step
-    // (whose history rows come from conv_state_in and are loaded when staged),
-    // the fetch reads through an empty range.
+    // read); past the end of the chunk the fetch reads through an empty range.
     constexpr int T1 = 64, T1P = T1 / T;
-    constexpr int X1UL = ((T1 + XH) * kCPB + kThreads - 1) / kThreads;
     constexpr int X1L = (T1 * kCPB + kThreads - 1) / kThreads;
     constexpr int B1L = (T1 * NP + kThreads - 1) / kThreads;
-    float *const s1_u = s_rB;                             // row r: token ts + r - XH
-    float *const s1_dt = s_rB + X1UL * RPL * kXR;         // row r: token ts + r
+    float *const s1_u = s_rB;                             // row r: token ts + r
+    float *const s1_dt = s_rB + X1L * RPL * kXR;
     float *const s1_B = s_rC;                             // [T1][NP]
-    static_assert((X1UL + X1L) * RPL * kXR <= T * TSL && B1L * kThreads <= T * TSL, "walk staging fits the slabs");
+    static_assert(2 * X1L * RPL * kXR <= T * TSL && B1L * kThreads <= T * TSL, "walk staging fits the slabs");
     static_assert(kThreads % NP == 0, "B rows of a whole-workgroup load");
-    raw_t qu[2][X1UL], qdt[2][X1L], qB[2][B1L];
-    auto fetch1 = [&](int m, raw_t (&xu)[X1UL], raw_t (&xdt)[X1L], raw_t (&xB)[B1L]) {
+    raw_t qu[2][X1L], qdt[2][X1L], qB[2][B1L];
+    auto fetch1 = [&](int m, raw_t (&xu)[X1L], raw_t (&xdt)[X1L], raw_t (&xB)[B1L]) {
         // addresses only: with an empty range nothing at them is touched
         const int64_t ts = (int64_t)(tile0 + m * T1P) * T;
         const int64_t rows = max(Le - ts, (int64_t)0);
-        const bool empty = rows == 0 || (CONV && ts < XH);
         const int64_t row0 = (b * L + ts) * D + d0;
-        const buf_t bU = make_buf(U + (row0 - XH * D), empty ? 0 : (uint64_t)((rows + XH) * D - d0) * es);
+        const uint64_t xr = rows ? (uint64_t)(rows * D - d0) * es : 0;
+        const buf_t bU = make_buf(U + row0, xr);
 #pragma unroll
-        for (int q = 0; q < X1UL; ++q) xu[q] = buf_ld_raw(bU, xoff + q * xstep, U);
+        for (int q = 0; q < X1L; ++q) xu[q] = buf_ld_raw(bU, xoff + q * xstep, U);
         if constexpr (DISC != DISC_CONST) {
-            const buf_t bDT = make_buf(DT + row0, rows ? (uint64_t)(rows * D - d0) * es : 0);
+            const buf_t bDT = make_buf(DT + row0, xr);
 #pragma unroll
             for (int q = 0; q < X1L; ++q) xdt[q] = buf_ld_raw(bDT, xoff + q * xstep, DT);
         }
@@ -467,27 +416,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int q = 0; q < B1L; ++q) xB[q] = buf_ld_raw(bB, boff + q * bstep, Bp);
     };
-    auto stage1 = [&](int m, const raw_t (&xu)[X1UL], const raw_t (&xdt)[X1L], const raw_t (&xB)[B1L]) {
-        const int64_t ts = (int64_t)(tile0 + m * T1P) * T;
-        if (CONV && ts < XH) {
-            for (int e = tid; e < (T1 + XH) * kCPB; e += kThreads) {
-                const int rr = e / kCPB, cc = e % kCPB;
-                const int64_t t = ts + rr - XH;
-                float v = 0.0f;
-                if (t < Le && d0 + cc < D) {
-                    if (t >= 0)
-                        v = to_f32(U[(b * L + t) * D + d0 + cc]);
-                    else if (p.conv_hist != nullptr && t >= -(int64_t)(W - 1))
-                        v = p.conv_hist[(b * (W - 1) + (W - 1) + t) * D + d0 + cc];
-                }
-                s1_u[rr * kXR + cc] = v;
-            }
-        } else {
+    auto stage1 = [&](const raw_t (&xu)[X1L], const raw_t (&xdt)[X1L], const raw_t (&xB)[B1L]) {
 #pragma unroll
-            for (int q = 0; q < X1UL; ++q) {
-                const int e = q * kThreads + tid;
-                s1_u[(e / kCPB) * kXR + e % kCPB] = raw_f32(xu[q], U);
-            }
+        for (int q = 0; q < X1L; ++q) {
+            const int e = q * kThreads + tid;
+            s1_u[(e / kCPB) * kXR + e % kCPB] = raw_f32(xu[q], U);
         }
         if constexpr (DISC != DISC_CONST) {
 #pragma unroll
@@ -505,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     // the loop, on every tile.
 #pragma unroll
     for (int s = 0; s < S; ++s) asm volatile("" : "+v"(h[s]));
-    asm volatile("" : "+v"(dtb), "+v"(Dd), "+v"(cb));
+    asm volatile("" : "+v"(dtb), "+v"(Dd));
     const int M1 = (K + T1P - 1) / T1P;   // steps
     fetch1(0, qu[0], qdt[0], qB[0]);
     for (int m0 = 0; m0 < M1; m0 += 2) {
@@ -514,7 +447,7 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             const int m = m0 + j;
             if (m < M1) {
                 __syncthreads();
-                stage1(m, qu[j], qdt[j], qB[j]);
+                stage1(qu[j], qdt[j], qB[j]);
                 __syncthreads();
                 fetch1(m + 1, qu[1 - j], qdt[1 - j], qB[1 - j]);
 #pragma unroll 1
@@ -562,13 +495,6 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         dA[s] = 0.0f;
     }
     float accD = 0.0f, accT = 0.0f;   // over this lane's tokens: dyv*u and d_dt_raw
-    // conv: lane l sums tap slot l & 7 over half of each tile's tokens; the
-    // bias over its own tokens; lane j < W-1 holds history input j's gradient
-    float accW = 0.0f, accCb = 0.0f, dhist = 0.0f, gshift = 0.0f;
-    if constexpr (CONV) {
-        // tokens past the last tile have no gradient
-        for (int e = tid; e < (T + 7) * kXR; e += kThreads) s_gx[e] = 0.0f;
-    }
     // The finished tile's outputs wait in LDS and go to memory, in whole
     // 48-channel rows, after the next tile is staged.
     float odx[XL], oddt[XL], odz[XL], oB[BL], oC[BL];
@@ -622,9 +548,6 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int s = 0; s < S; ++s) hck[s] = sv[s] ? __uint_as_float(rck[s]) : 0.0f;
         if (k + 1 < K) read_out();
-        if constexpr (CONV) {
-            if (k + 1 < K && tid < 7 * kCPB) s_gx[(T + tid / kCPB) * kXR + tid % kCPB] = gshift;
-        }
         __syncthreads();
         if (k + 1 < K) store_out(k + 1);
         if (k > 0) fetch(k - 1, true);
@@ -705,7 +628,6 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         // dt*B form: the dt gradient is sum_n da a A + u sum_n g B, and the u
         // gradient dt sum_n g B, so a state-step adds da a A to pt and g B to
         // pu, and the factors u and dt are applied once per token below.
-        float tk_gx[TP];
 #pragma unroll
         for (int jj = TP - 1; jj >= 0; --jj) {
             float pdt[16], pdu[16];
@@ -773,7 +695,6 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
             float ddt = (DISC != DISC_CONST) ? row_transpose_sum(pdt, l) : 0.0f;
             const float dup = row_transpose_sum(pdu, l);
             if constexpr (DISC == DISC_DB) ddt = fmaf(tk_u[jj], dup, ddt);
-            tk_gx[jj] = 0.0f;
             if (tk_v[jj]) {
                 const int tt = l + 16 * jj;
                 const float dyv = tk_dyv[jj];
@@ -785,44 +706,11 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 const float ddr = ddt * tk_sg[jj];
                 accD = fmaf(dyv, tk_u[jj], accD);
                 accT += ddr;
-                if constexpr (CONV) {
-                    const float xc = tk_xc[jj];
-                    const float sx = sigmoid_f(xc);
-                    tk_gx[jj] = duv * (sx * (1.0f + xc * (1.0f - sx)));
-                } else {
-                    s_odx[tt * kXR + cl] = duv;
-                }
+                s_odx[tt * kXR + cl] = duv;
                 s_oddt[tt * kXR + cl] = ddr;
-            }
-            if constexpr (CONV) {
-                if (l + 16 * jj < T) s_gx[(l + 16 * jj) * kXR + cl] = tk_gx[jj];
             }
         }
         __syncthreads();
-        if constexpr (CONV) {
-            // dx of this lane's tokens from the ring; tap and bias sums
-#pragma unroll
-            for (int jj = 0; jj < TP; ++jj) {
-                const int tt = l + 16 * jj;
-                if (tk_v[jj]) {
-                    float acc = 0.0f;
-#pragma unroll
-                    for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], s_gx[(tt + 7 - i) * kXR + cl], acc);
-                    s_odx[tt * kXR + cl] = acc;
-                    accCb += tk_gx[jj];
-                }
-            }
-            {
-                constexpr int TH = T / 2;
-                const int i = l & 7, t0 = (l >> 3) * TH;
-#pragma unroll
-                for (int j = 0; j < TH; ++j)
-                    accW = fmaf(s_gx[(t0 + j) * kXR + cl], s_u[(t0 + j + i) * kXR + cl], accW);
-            }
-            // rows 0..6 become the following rows of the next (earlier) tile;
-            // written after the next barrier, when nobody reads rows T..T+6
-            gshift = (tid < 7 * kCPB) ? s_gx[(tid / kCPB) * kXR + tid % kCPB] : 0.0f;
-        }
         // dB, dC partials of this workgroup over its 48 channels: B and C on
         // separate threads, each sum as four chains (chain r takes channels
         // r, r+4, ... in order), added as ((r0 + r1) + (r2 + r3))
@@ -846,28 +734,10 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
         read_out();
         store_out(0);
     }
-    if constexpr (CONV) {
-        // gradient of history input j (token j - (W-1)): lane j of the row,
-        // from the first tile's rows (zeros when L = 0)
-        if (l < W - 1) {
-            const int t = l - (W - 1);
-            for (int i = 0; i < 8; ++i) {
-                const int r = t + 7 - i;
-                if (r >= 0) dhist = fmaf(wk[i], s_gx[r * kXR + cl], dhist);
-            }
-        }
-    }
 
-    // per-channel sums over the row's lanes (each holds its own tokens'),
-    // in a fixed order: lane j of the row receives the total of slot j
-    // (slots 0..7 conv taps, 8 conv bias, 9 dDskip, 10 d_dt_bias)
-    float pr[16];
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk) pr[kk] = (kk < 8 && (l & 7) == kk) ? accW : 0.0f;
-    pr[8] = accCb;
-    pr[9] = accD;
-    pr[10] = accT;
-    const float sr = row_transpose_sum(pr, l);
+    // per-channel sums over the row's lanes (each holds its own tokens'), in a
+    // fixed order (a butterfly: every lane of the row gets the same total)
+    const float sD = group_sum<16>(accD), sT = group_sum<16>(accT);
     if (dvalid) {
         const int64_t bk = b * p.KC + kc;   // partials per (batch row, chunk)
 #pragma unroll
@@ -877,21 +747,9 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 p.pA[(bk * D + d) * N + l + 16 * s] = dA[s];
             }
         }
-        if (l == 9) p.pD[bk * D + d] = sr;
-        if (l == 10) p.pT[bk * D + d] = sr;
-        if constexpr (CONV) {
-            if (l < 8) p.pW[(bk * D + d) * 8 + l] = sr;
-            if (l == 8) p.pCb[bk * D + d] = sr;
-            // the first W-1 inputs before the chunk: the carried history for
-            // chunk 0, else the previous chunk's last inputs (added to its dx
-            // by bwd_conv_boundary)
-            if (l < W - 1) {
-                if (kc == 0) {
-                    if (p.dhist != nullptr) p.dhist[(b * (W - 1) + l) * D + d] = dhist;
-                } else {
-                    p.bnd[(bk * (W - 1) + l) * D + d] = dhist;
-                }
-            }
+        if (l == 0) {
+            p.pD[bk * D + d] = sD;
+            p.pT[bk * D + d] = sT;
         }
     }
 }
@@ -913,22 +771,9 @@ __global__ __launch_bounds__(256) void bwd_reduce_bc(const float *pB, const floa
 }
 
 __global__ __launch_bounds__(256) void bwd_reduce_params(const float *A_log, const float *pA, const float *pD,
-                                                         const float *pT, const float *pW, const float *pCb,
-                                                         int64_t B, int64_t D, int64_t N, int W,
-                                                         float *dA_log, float *dD, float *ddtb, float *dw,
-                                                         float *dcb) {
+                                                         const float *pT, int64_t B, int64_t D, int64_t N,
+                                                         float *dA_log, float *dD, float *ddtb) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < D * W && dw) {
-        const int64_t dd = i / W, kk = i % W;
-        float s = 0.0f;
-        for (int64_t b = 0; b < B; ++b) s += pW[(b * D + dd) * 8 + kk + (8 - W)];
-        dw[i] = s;
-    }
-    if (i < D && dcb) {
-        float s = 0.0f;
-        for (int64_t b = 0; b < B; ++b) s += pCb[b * D + i];
-        dcb[i] = s;
-    }
     if (i < D * N && dA_log) {
         float s = 0.0f;
         for (int64_t b = 0; b < B; ++b) s += pA[b * D * N + i];
@@ -1136,25 +981,9 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(const float *A_log, cons
     }
 }
 
-// With the conv prologue, a chunk's last W-1 inputs also feed the next
-// chunk's first outputs; that chunk left the gradient in bnd.
-template <typename IOT>
-__global__ __launch_bounds__(256) void bwd_conv_boundary(IOT *dx, const float *bnd, int64_t B, int64_t L,
-                                                         int64_t D, int W, int KC, int64_t chunk) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int64_t total = B * (KC - 1) * (W - 1) * D;
-    if (i >= total) return;
-    const int64_t dd = i % D, j = (i / D) % (W - 1), r = i / (D * (W - 1));
-    const int64_t kc = 1 + r % (KC - 1), b = r / (KC - 1);
-    const int64_t t = kc * chunk - (W - 1) + j;
-    if (t < 0 || t >= L) return;
-    const int64_t o = (b * L + t) * D + dd;
-    store_io(dx + o, to_f32(dx[o]) + bnd[((b * KC + kc) * (W - 1) + j) * D + dd]);
-}
-
 struct BwdWs {
-    float *ckpt, *pB, *pC, *pA, *pD, *pT, *pW, *pCb;
-    float *agg_h, *agg_s, *RG, *Sdt, *bnd;   // time chunks only
+    float *ckpt, *pB, *pC, *pA, *pD, *pT;
+    float *agg_h, *agg_s, *RG, *Sdt;   // time chunks only
 };
 
 int tile_len(int64_t N) { return N <= 16 ? 16 : (N <= 32 ? 8 : 4); }
@@ -1183,32 +1012,22 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk,
     r.pA = take((size_t)(B * KC * D * N));
     r.pD = take((size_t)(B * KC * D));
     r.pT = take((size_t)(B * KC * D));
-    r.pW = take((size_t)(B * KC * D * 8));
-    r.pCb = take((size_t)(B * KC * D));
     if (KC > 1) {
         r.agg_h = take((size_t)(B * KC * D * N));
         r.agg_s = take((size_t)(B * KC * D));
         r.RG = take((size_t)(B * KC * D * N));
         r.Sdt = take((size_t)(B * KC * D));
-        r.bnd = take((size_t)(B * KC * (SSM_MAX_CONV_WIDTH_DEV - 1) * D));
     }
     if (total) *total = off;
     return r;
 }
 
 template <typename IOT, int S, int DISC>
-void launch_bwd_main(bool conv, bool gate, dim3 grid, dim3 block, hipStream_t s, const BwdParams &p) {
-    if (conv) {
-        if (gate)
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, true, true>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, true, false>), grid, block, 0, s, p);
-    } else {
-        if (gate)
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, false, true>), grid, block, 0, s, p);
-        else
-            hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, false, false>), grid, block, 0, s, p);
-    }
+void launch_bwd_main(bool gate, dim3 grid, dim3 block, hipStream_t s, const BwdParams &p) {
+    if (gate)
+        hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, true>), grid, block, 0, s, p);
+    else
+        hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, false>), grid, block, 0, s, p);
 }
 
 template <typename IOT, int S>
@@ -1222,9 +1041,9 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
     if (KC > 1) {
         // start states of the chunks (forward chunk scan + carry)
         ScanFwdArgs f{};
-        f.B = a.B; f.L = a.L; f.D = a.D; f.N = a.N; f.W = a.W; f.bf16 = a.bf16; f.disc = a.disc;
+        f.B = a.B; f.L = a.L; f.D = a.D; f.N = a.N; f.W = 0; f.bf16 = a.bf16; f.disc = a.disc;
         f.x = a.x; f.dt = a.dt; f.dt_bias = a.dt_bias; f.A_log = a.A_log; f.Bm = a.Bm; f.Cm = a.Cm;
-        f.conv_w = a.conv_w; f.conv_b = a.conv_b; f.conv_state_in = a.conv_state_in; f.h0 = a.h0;
+        f.h0 = a.h0;
         e = launch_scan_chunk_starts(f, a.chunk, w.agg_h, w.agg_s, s);
         if (e != hipSuccess) return e;
         // local end-to-start adjoints of chunks 1.., then the end adjoints
@@ -1249,12 +1068,10 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
     }
     p.u = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;
     p.Bm = a.Bm; p.Cm = a.Cm; p.Dskip = a.Dskip; p.z = a.z; p.dy = a.dy;
-    p.conv_w = a.conv_w; p.conv_b = a.conv_b; p.conv_hist = a.conv_state_in; p.dhist = a.dconv_state_in;
-    p.bnd = w.bnd;
     p.ckpt = w.ckpt;
     p.du = a.dx; p.ddt = a.ddt; p.dz = a.dz; p.dh0 = a.dh0;
-    p.pB = w.pB; p.pC = w.pC; p.pA = w.pA; p.pD = w.pD; p.pT = w.pT; p.pW = w.pW; p.pCb = w.pCb;
-    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N; p.W = a.W;
+    p.pB = w.pB; p.pC = w.pC; p.pA = w.pA; p.pD = w.pD; p.pT = w.pT;
+    p.B = a.B; p.L = a.L; p.D = a.D; p.N = a.N;
     constexpr int T = BGeo<S>::T;
     p.Kt = (int)((a.L + T - 1) / T);
     p.chunk = KC > 1 ? a.chunk : std::max<int64_t>(a.L, 1);
@@ -1262,22 +1079,15 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
     p.G = G;
     const int64_t blocks = (int64_t)G * KC * a.B;
     const dim3 grid((unsigned)blocks), block(kThreads);
-    const bool conv = a.W > 0, gate = a.z != nullptr;
+    const bool gate = a.z != nullptr;
     if (a.disc == DISC_ZOH)
-        launch_bwd_main<IOT, S, DISC_ZOH>(conv, gate, grid, block, s, p);
+        launch_bwd_main<IOT, S, DISC_ZOH>(gate, grid, block, s, p);
     else if (a.disc == DISC_CONST)
-        launch_bwd_main<IOT, S, DISC_CONST>(conv, gate, grid, block, s, p);
+        launch_bwd_main<IOT, S, DISC_CONST>(gate, grid, block, s, p);
     else
-        launch_bwd_main<IOT, S, DISC_DB>(conv, gate, grid, block, s, p);
+        launch_bwd_main<IOT, S, DISC_DB>(gate, grid, block, s, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (KC > 1 && a.W > 1 && a.dx != nullptr) {
-        const int64_t nb = a.B * (KC - 1) * (a.W - 1) * a.D;
-        hipLaunchKernelGGL((bwd_conv_boundary<IOT>), dim3((unsigned)((nb + 255) / 256)), dim3(256), 0, s,
-                           static_cast<IOT *>(a.dx), w.bnd, a.B, a.L, a.D, a.W, (int)KC, a.chunk);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     const int64_t total = a.B * a.L * a.N;
     if ((a.dB || a.dC) && total > 0) {
         hipLaunchKernelGGL((bwd_reduce_bc<IOT>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w.pB,
@@ -1285,10 +1095,9 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int64_t pn = std::max(std::max(a.D * a.N, a.D), a.D * a.W);
+    const int64_t pn = std::max(a.D * a.N, a.D);
     hipLaunchKernelGGL(bwd_reduce_params, dim3((unsigned)((pn + 255) / 256)), dim3(256), 0, s, a.A_log, w.pA,
-                       w.pD, w.pT, w.pW, w.pCb, a.B * KC, a.D, a.N, a.W, a.dA_log, a.dD, a.ddt_bias,
-                       a.W > 0 ? a.dconv_w : nullptr, a.W > 0 ? a.dconv_b : nullptr);
+                       w.pD, w.pT, a.B * KC, a.D, a.N, a.dA_log, a.dD, a.ddt_bias);
     return hipGetLastError();
 }
 
@@ -1316,13 +1125,54 @@ int64_t scan_bwd_chunk(int64_t B, int64_t L, int64_t D, int64_t N, int64_t reque
     return std::min<int64_t>(chunk, whole);
 }
 
-size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk) {
-    size_t total = 0;
-    carve(nullptr, B, L, D, N, chunk, &total);
-    return total;
+// With the conv prologue the workspace starts with u = SiLU(conv(x)) and
+// dLoss/du (io type, [B, L, D] each) and the conv backward's partials; the
+// scan's own workspace follows.
+static size_t conv_part_bytes(int64_t B, int64_t L, int64_t D, int W, int64_t es) {
+    if (W == 0) return 0;
+    return 2 * ws_align((size_t)(B * L * D * es)) + conv1d_bwd_workspace_bytes(B, L, D);
 }
 
+size_t scan_bwd_workspace_bytes(int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk, int W, int64_t es) {
+    size_t total = 0;
+    carve(nullptr, B, L, D, N, chunk, &total);
+    return total + conv_part_bytes(B, L, D, W, es);
+}
+
+// With the conv prologue: u = SiLU(conv(x)) by the conv kernel, the scan
+// backward from u (its dLoss/du into the workspace), then the conv backward
+// (dx, tap, bias and history gradients).  Fused into the sweep, the conv's
+// extra state does not fit the sweep's register budget (the recomputed
+// window, the ring of conv-output gradients and the tap sums); split, each
+// part runs at its own speed, for one more pass over u and du.
 hipError_t launch_scan_bwd(const ScanBwdArgs &a, hipStream_t s) {
+    if (a.W > 0) {
+        const int64_t es = a.bf16 ? 2 : 4;
+        char *base = static_cast<char *>(a.ws);
+        const size_t nu = ws_align((size_t)(a.B * a.L * a.D * es));
+        void *u = base, *du = base + nu;
+        float *cws = reinterpret_cast<float *>(base + 2 * nu);
+        const size_t cbytes = conv1d_bwd_workspace_bytes(a.B, a.L, a.D);
+        ConvArgs c{};
+        c.B = a.B; c.L = a.L; c.D = a.D; c.W = a.W; c.silu = 1; c.bf16 = a.bf16;
+        c.x = a.x; c.w = a.conv_w; c.b = a.conv_b; c.state_in = a.conv_state_in; c.y = u;
+        hipError_t e = launch_conv1d(c, s);
+        if (e != hipSuccess) return e;
+        ScanBwdArgs v = a;
+        v.W = 0; v.x = u; v.dx = du;
+        v.conv_w = nullptr; v.conv_b = nullptr; v.conv_state_in = nullptr;
+        v.dconv_w = nullptr; v.dconv_b = nullptr; v.dconv_state_in = nullptr;
+        v.ws = base + 2 * nu + cbytes;
+        BwdWs w = carve(v.ws, v.B, v.L, v.D, v.N, v.chunk, nullptr);
+        e = a.bf16 ? launch_bwd_s<bf16_t>(v, w, s) : launch_bwd_s<float>(v, w, s);
+        if (e != hipSuccess) return e;
+        ConvBwdArgs g{};
+        g.B = a.B; g.L = a.L; g.D = a.D; g.W = a.W; g.bf16 = a.bf16;
+        g.x = a.x; g.du = du; g.w = a.conv_w; g.b = a.conv_b; g.state_in = a.conv_state_in;
+        g.dx = a.dx; g.dw = a.dconv_w; g.db = a.dconv_b; g.dstate = a.dconv_state_in; g.ws = cws;
+        if (g.dx == nullptr && g.dw == nullptr && g.db == nullptr && g.dstate == nullptr) return hipSuccess;
+        return launch_conv1d_bwd(g, s);
+    }
     BwdWs w = carve(a.ws, a.B, a.L, a.D, a.N, a.chunk, nullptr);
     if (a.bf16) return launch_bwd_s<bf16_t>(a, w, s);
     return launch_bwd_s<float>(a, w, s);

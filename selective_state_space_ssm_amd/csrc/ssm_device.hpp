@@ -267,26 +267,20 @@ __device__ __forceinline__ float row_transpose_sum(const float (&p)[16], int l) 
 #define SSM_BANK_PAIR(CTRL, LO, HI, O, X, Y)                                             \
     "v_add_f32_dpp %" #O ", %" #X ", %" #X " " CTRL " row_mask:0xf bank_mask:" LO "\n\t" \
     "v_add_f32_dpp %" #O ", %" #Y ", %" #Y " " CTRL " row_mask:0xf bank_mask:" HI "\n\t"
-    asm("s_nop 1\n\t"
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 0, 8, 16)
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 1, 9, 17)
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 2, 10, 18)
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 3, 11, 19)
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 4, 12, 20)
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 5, 13, 21)
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 6, 14, 22)
-        SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 7, 15, 23)
-        : "=&v"(v8[0]), "=&v"(v8[1]), "=&v"(v8[2]), "=&v"(v8[3]),
-          "=&v"(v8[4]), "=&v"(v8[5]), "=&v"(v8[6]), "=&v"(v8[7])
-        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]),
-          "v"(p[8]), "v"(p[9]), "v"(p[10]), "v"(p[11]), "v"(p[12]), "v"(p[13]), "v"(p[14]), "v"(p[15]));
-    asm("s_nop 1\n\t"
-        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 0, 4, 8)
-        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 1, 5, 9)
-        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 2, 6, 10)
-        SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 3, 7, 11)
-        : "=&v"(v4[0]), "=&v"(v4[1]), "=&v"(v4[2]), "=&v"(v4[3])
-        : "v"(v8[0]), "v"(v8[1]), "v"(v8[2]), "v"(v8[3]), "v"(v8[4]), "v"(v8[5]), "v"(v8[6]), "v"(v8[7]));
+#pragma unroll
+    for (int k = 0; k < 8; k += 2)
+        asm("s_nop 1\n\t"
+            SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 0, 2, 4)
+            SSM_BANK_PAIR("row_mirror", "0x3", "0xc", 1, 3, 5)
+            : "=&v"(v8[k]), "=&v"(v8[k + 1])
+            : "v"(p[k]), "v"(p[k + 1]), "v"(p[k + 8]), "v"(p[k + 9]));
+#pragma unroll
+    for (int k = 0; k < 4; k += 2)
+        asm("s_nop 1\n\t"
+            SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 0, 2, 4)
+            SSM_BANK_PAIR("row_half_mirror", "0x5", "0xa", 1, 3, 5)
+            : "=&v"(v4[k]), "=&v"(v4[k + 1])
+            : "v"(v8[k]), "v"(v8[k + 1]), "v"(v8[k + 4]), "v"(v8[k + 5]));
 #undef SSM_BANK_PAIR
     const bool b1 = (l & 2) != 0, b0 = (l & 1) != 0;
 #pragma unroll
