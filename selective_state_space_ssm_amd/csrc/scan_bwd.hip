@@ -41,6 +41,7 @@
 // LDS.  Two small kernels add the per-workgroup dB, dC partials and the
 // per-batch dA_log, dDskip, d_dt_bias partials, in a fixed order.
 #include <algorithm>
+#include <vector>
 
 #include "launch.hpp"
 #include "ssm_device.hpp"
@@ -937,18 +938,29 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
             tk_dyv[jj] = gate ? dyr * silu_f(s_z[e]) : dyr;
             sdl += dl;
         }
+        // tokens from last to first; both loop indices are constants (the
+        // broadcast lane and the register of the token's values)
+        static_for<TP>([&](auto jc) {
+            constexpr int jj = TP - 1 - decltype(jc)::value;
+            // the sixteen tokens' C values of this lane's states, read together
+            float cq[16][S];
 #pragma unroll
-        for (int i = T - 1; i >= 0; --i) {
-            const float dli = tok_bcast<TP>(tk_dl, i), dyv = tok_bcast<TP>(tk_dyv, i);
+            for (int kk = 0; kk < 16; ++kk)
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const float gj = fmaf(s_C[i * NP + l + 16 * s], dyv, g[s]);
-                if constexpr (CONSTD)
-                    g[s] = fmaf(dli * A2[s], gj, gj);
-                else
-                    g[s] = hw_exp2(dli * A2[s]) * gj;
-            }
-        }
+                for (int s = 0; s < S; ++s) cq[kk][s] = s_C[(16 * jj + kk) * NP + l + 16 * s];
+            static_for<16>([&](auto kc) {
+                constexpr int kk = 15 - decltype(kc)::value;
+                const float dli = row_bcast<kk>(tk_dl[jj]);
+#pragma unroll
+                for (int s = 0; s < S; ++s) {
+                    const float gj = fmac_row_bcast<kk>(g[s], tk_dyv[jj], cq[kk][s]);   // g + C dyv
+                    if constexpr (CONSTD)
+                        g[s] = fmaf(dli * A2[s], gj, gj);
+                    else
+                        g[s] = hw_exp2(dli * A2[s]) * gj;
+                }
+            });
+        });
     }
     float pr[16];
 #pragma unroll
@@ -993,6 +1005,18 @@ int64_t num_bwd_chunks(int64_t L, int64_t chunk) {
     return (L + chunk - 1) / chunk;
 }
 
+// The chunk start states come from a forward chunk scan over sub-chunks of
+// chunk / r tokens, r chosen so that the forward's one-wavefront pass (one
+// wavefront per 16 channels and sub-chunk) has about three wavefronts per
+// SIMD; chunk k starts at sub-chunk k r.
+int64_t start_subdiv(int64_t B, int64_t D, int64_t chunk, int64_t KC) {
+    if (KC <= 1) return 1;
+    const int64_t waves = B * ((D + 15) / 16) * KC;
+    int64_t r = std::max<int64_t>(1, 3072 / std::max<int64_t>(waves, 1));
+    while (r > 1 && (chunk / 64) % r != 0) --r;
+    return r;
+}
+
 BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk, size_t *total) {
     const int T = tile_len(N);
     const int64_t K = std::max<int64_t>(1, (L + T - 1) / T);
@@ -1013,8 +1037,9 @@ BwdWs carve(void *ws, int64_t B, int64_t L, int64_t D, int64_t N, int64_t chunk,
     r.pD = take((size_t)(B * KC * D));
     r.pT = take((size_t)(B * KC * D));
     if (KC > 1) {
-        r.agg_h = take((size_t)(B * KC * D * N));
-        r.agg_s = take((size_t)(B * KC * D));
+        const int64_t KS = KC * start_subdiv(B, D, chunk, KC);   // sub-chunks of the start-state scan
+        r.agg_h = take((size_t)(B * KS * D * N));
+        r.agg_s = take((size_t)(B * KS * D));
         r.RG = take((size_t)(B * KC * D * N));
         r.Sdt = take((size_t)(B * KC * D));
     }
@@ -1028,6 +1053,31 @@ void launch_bwd_main(bool gate, dim3 grid, dim3 block, hipStream_t s, const BwdP
         hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, true>), grid, block, 0, s, p);
     else
         hipLaunchKernelGGL((scan_bwd_kernel<IOT, S, DISC, false>), grid, block, 0, s, p);
+}
+
+// A second stream of the library's own (default priority, one per host
+// thread and device, created on first use and kept until the process ends),
+// with a fork and a join event: the chunk start states and the local
+// adjoints read only the inputs and are independent of each other, so the
+// first runs there while the second runs on the caller's stream.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+hipError_t side_stream(SideStream **out) {
+    thread_local std::vector<SideStream> per_dev;
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if ((int)per_dev.size() <= dev) per_dev.resize(dev + 1);
+    SideStream &ss = per_dev[dev];
+    if (ss.stream == nullptr) {
+        if ((e = hipStreamCreateWithFlags(&ss.stream, hipStreamNonBlocking)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming)) != hipSuccess) return e;
+        if ((e = hipEventCreateWithFlags(&ss.join, hipEventDisableTiming)) != hipSuccess) return e;
+    }
+    *out = &ss;
+    return hipSuccess;
 }
 
 template <typename IOT, int S>
@@ -1044,8 +1094,14 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
         f.B = a.B; f.L = a.L; f.D = a.D; f.N = a.N; f.W = 0; f.bf16 = a.bf16; f.disc = a.disc;
         f.x = a.x; f.dt = a.dt; f.dt_bias = a.dt_bias; f.A_log = a.A_log; f.Bm = a.Bm; f.Cm = a.Cm;
         f.h0 = a.h0;
-        e = launch_scan_chunk_starts(f, a.chunk, w.agg_h, w.agg_s, s);
+        const int64_t sub = start_subdiv(a.B, a.D, a.chunk, KC);
+        SideStream *ss = nullptr;
+        if ((e = side_stream(&ss)) != hipSuccess) return e;
+        if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
+        e = launch_scan_chunk_starts(f, a.chunk / sub, w.agg_h, w.agg_s, ss->stream);
         if (e != hipSuccess) return e;
+        if ((e = hipEventRecord(ss->join, ss->stream)) != hipSuccess) return e;
         // local end-to-start adjoints of chunks 1.., then the end adjoints
         BwdLocalParams q{};
         q.dt = a.dt; q.Cm = a.Cm; q.z = a.z; q.dy = a.dy; q.dt_bias = a.dt_bias; q.A_log = a.A_log;
@@ -1063,7 +1119,9 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
                            a.dhT, w.RG, w.Sdt, a.B, a.D, a.N, (int)KC);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
-        p.h0 = w.agg_h; p.h0_bs = KC * a.D * a.N; p.h0_ks = a.D * a.N;
+        if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
+        const int64_t KS = num_bwd_chunks(a.L, a.chunk / sub);
+        p.h0 = w.agg_h; p.h0_bs = KS * a.D * a.N; p.h0_ks = sub * a.D * a.N;
         p.dhT = w.RG; p.dhT_bs = KC * a.D * a.N; p.dhT_ks = a.D * a.N;
     }
     p.u = a.x; p.dt = a.dt; p.dt_bias = a.dt_bias; p.A_log = a.A_log;

@@ -709,16 +709,6 @@ template <> struct LongIO<bf16_t> {
     }
 };
 
-// acc + (lane K of the row's c) * h, as one v_fmac_f32_dpp with a row
-// broadcast (the compiler folds a DPP operand into VOP2 multiplies but not
-// into the three-operand FMA).  The s_nop gives the two wait states a DPP
-// read needs after a VALU write of its source register.
-template <int K>
-__device__ __forceinline__ float fmac_row_bcast(float acc, float c, float h) {
-    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-                 : "+v"(acc) : "v"(c), "v"(h), "n"(K));
-    return acc;
-}
 
 template <typename IOT, int DISC, int MODE>
 __global__ __launch_bounds__(64) void scan_long_kernel(FwdParams p) {

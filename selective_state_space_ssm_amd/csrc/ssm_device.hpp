@@ -249,6 +249,17 @@ __device__ __forceinline__ float row_bcast(float v) {
     return dpp_f<0x150 + K>(v);
 }
 
+// acc + (lane K of the row's c) * h, as one v_fmac_f32_dpp with a row
+// broadcast (the compiler folds a DPP operand into VOP2 multiplies but not
+// into the three-operand FMA).  The s_nop gives the two wait states a DPP
+// read needs after a VALU write of its source register.
+template <int K>
+__device__ __forceinline__ float fmac_row_bcast(float acc, float c, float h) {
+    asm volatile("s_nop 1\n\tv_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+                 : "+v"(acc) : "v"(c), "v"(h), "n"(K));
+    return acc;
+}
+
 // Transposed row reduction: p[k] is this lane's partial for token k; lane l
 // receives the sum over its 16-lane row of p[l].  Pairings: l^15 (row
 // mirror), l^7 (half-row mirror), l^2, l^1; each lane keeps the half of the
