@@ -222,16 +222,13 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     const int rw = lane >> 4, l = lane & 15;
     const int cl = wv * 4 + rw;                 // channel within the workgroup
     // Neighbouring channel groups share the 128-byte lines at their edges
-    // (a row of 48 channels is 192 bytes in fp32, 96 in bf16): without a time
-    // split, consecutive groups go to one XCD (the hardware deals workgroups
-    // round-robin over the XCDs), whose L2 then fetches each line once: 0.76x
-    // the fetched bytes at B 8, L 2048, in the same time.  With a time split
-    // the round-robin order is kept; the grouping did not measure faster
-    // there.  32-bit scalar arithmetic: a 64-bit form of the same mapping
-    // cost 8% of the long-sequence sweep.
+    // (a row of 48 channels is 192 bytes in fp32, 96 in bf16): consecutive
+    // groups go to one XCD (the hardware deals workgroups round-robin over
+    // the XCDs), whose L2 then fetches each line once: 0.76x the fetched
+    // bytes at B 8, L 2048, in the same time.  32-bit scalar arithmetic: a
+    // 64-bit form of the same mapping cost 8% of the long-sequence sweep.
     const uint32_t nb = gridDim.x;
-    const uint32_t bid = (p.KC == 1 && nb % kXcds == 0) ? (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds
-                                                        : blockIdx.x;
+    const uint32_t bid = nb % kXcds == 0 ? (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds : blockIdx.x;
     const int64_t grp = bid % (uint32_t)p.G;
     const int64_t kc = (bid / (uint32_t)p.G) % (uint32_t)p.KC;   // time chunk
     const int64_t b = bid / (uint32_t)p.G / (uint32_t)p.KC;
@@ -843,9 +840,11 @@ __global__ __launch_bounds__(kThreads) void bwd_local_kernel(BwdLocalParams p) {
     const int wv = tid >> 6, lane = tid & 63;
     const int rw = lane >> 4, l = lane & 15;
     const int cl = wv * 4 + rw;
-    const int64_t grp = blockIdx.x % p.G;
-    const int64_t kc = 1 + (blockIdx.x / p.G) % (p.KC - 1);
-    const int64_t b = blockIdx.x / p.G / (p.KC - 1);
+    const uint32_t nb = gridDim.x;   // neighbouring channel groups on one XCD, as in scan_bwd_kernel
+    const uint32_t bid = nb % kXcds == 0 ? (blockIdx.x % kXcds) * (nb / kXcds) + blockIdx.x / kXcds : blockIdx.x;
+    const int64_t grp = bid % (uint32_t)p.G;
+    const int64_t kc = 1 + (bid / (uint32_t)p.G) % (uint32_t)(p.KC - 1);
+    const int64_t b = bid / (uint32_t)p.G / (uint32_t)(p.KC - 1);
     const int64_t N = p.N, D = p.D, L = p.L;
     const int64_t t0 = kc * p.chunk, Le = min(L, t0 + p.chunk);
     const int K = (int)((Le - t0 + T - 1) / T);
