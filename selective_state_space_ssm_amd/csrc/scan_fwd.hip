@@ -19,10 +19,14 @@
 //    dt*u, the gate SiLU(z) and Dskip*u into LDS;
 //  - scan: per token a lane reads its channel's (dt, dt*u) and its B, C
 //    values from LDS and updates its state with one exp2; the readout
-//    <h, C> is summed over a channel's four lanes of the wavefront (four
-//    16-lane rows, with the gfx950 row swaps v_permlane16/32_swap; for the
-//    constant decay a lane quad, with DPP) and across the four wavefronts
-//    through LDS, both in the order ((0 + 1) + (2 + 3)).
+//    <h, C> is summed over a channel's four lanes of the wavefront and
+//    across the four wavefronts through LDS.  Inside a wavefront the four
+//    lanes are one per 4-lane bank of a row at one state per lane, summed
+//    with bank-masked DPP adds as ((0 + 3) + (1 + 2)); at several states per
+//    lane they are four 16-lane rows, summed with the gfx950 row swaps
+//    v_permlane16/32_swap as ((0 + 1) + (2 + 3)); for the constant decay a
+//    lane quad, with DPP, as ((0 + 1) + (2 + 3)).  The wavefronts are summed
+//    as ((0 + 1) + (2 + 3)).
 // The recurrence itself stays strictly sequential in time inside a chunk.
 //
 // Decay source ("the s6 cell", section "one cell, two architectures": one
@@ -199,6 +203,45 @@ __device__ __forceinline__ float rows_transpose_sum(const float (&p)[4]) {
     swap32(a0 + a1, b0 + b1, c0, c1);
     return c0 + c1;
 }
+// Sums over the four 4-lane banks of each 16-lane row, with bank-masked DPP
+// adds.  In every row the lanes {c, 7-c, 8+c, 15-c} (c = 0..3) form a group,
+// one lane per bank: row_mirror pairs lanes i and 15-i, row_half_mirror
+// lanes i and 7-i of each half, and both pairings stay inside a group.
+// p[k] is this lane's partial for token k; the lane in bank k receives its
+// group's sum for token k, associated as (bank0 + bank3) + (bank1 + bank2).
+// The first step leaves tokens 0, 1 in banks 0-1 and tokens 2, 3 in banks
+// 2-3, each summed over a mirrored lane pair; the second adds the two pairs.
+// All 64 lanes must be active.  A DPP read needs two wait states after the
+// VALU write of its source (the s_nop; the compiler does not insert them
+// for inline asm).
+__device__ __forceinline__ float banks_transpose_sum(const float (&p)[4]) {
+    float v0, v1, y;
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %0, %4, %4 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+        "v_add_f32_dpp %1, %3, %3 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %1, %5, %5 row_mirror row_mask:0xf bank_mask:0xc"
+        : "=&v"(v0), "=&v"(v1)
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]));
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %1, %1 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %0, %2, %2 row_half_mirror row_mask:0xf bank_mask:0xa"
+        : "=&v"(y)
+        : "v"(v0), "v"(v1));
+    return y;
+}
+// Every lane of a bank group receives the group's sum, in the same
+// association as banks_transpose_sum.
+__device__ __forceinline__ float banks_sum(float v) {
+    v += dpp_f<kDppRowMirror>(v);
+    v += dpp_f<kDppRowHalfMirror>(v);
+    return v;
+}
+// Lane G of each 4-lane bank, broadcast to the bank (DPP quad_perm [G,G,G,G]).
+template <int G>
+__device__ __forceinline__ float bank_bcast(float v) {
+    return dpp_f<G * 0x55>(v);
+}
 // Quad transpose-reduce: lane j of each lane quad holds partial sums p[i]
 // for four consecutive tokens; on return lane j holds the quad's sum for
 // token j, associated as ((lane0 + lane1) + (lane2 + lane3)).
@@ -241,10 +284,16 @@ __device__ __forceinline__ void lds_read_k(const float *p, float (&o)[K]) {
 }
 
 // One block = four wavefronts = 16 channels of one batch row and one time
-// chunk.  In wavefront w, lane ch + 16 j (row j, position ch) owns states
-// n = (4w + j)*SPL .. +SPL-1 of channel ch.  The constant decay, whose scan
-// has no exp to hide the row swaps' latency behind, keeps the four lanes of
-// a channel in a quad instead (lane 4 ch + j) and sums them with DPP.
+// chunk.  Wavefront w holds states n = (4w + j)*SPL .. +SPL-1 of each
+// channel in the lanes of index j:
+//  - one state per lane (N <= 16): j is the lane's 4-lane bank, and channel
+//    4r + c of row r sits in lanes c, 7-c, 8+c, 15-c of the row (banks 0..3),
+//    the groups that banks_transpose_sum reduces with DPP;
+//  - several states per lane: j is the lane's row, channel ch its position
+//    in the row, reduced with the gfx950 row swaps.
+// The constant decay, whose scan has no exp to hide the reduction's latency
+// behind, keeps the four lanes of a channel in a quad instead (lane 4 ch + j)
+// and sums them with DPP.
 template <typename IOT, int SPL, int DISC, bool CONV, int MODE, int CW = 0>
 __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     constexpr int T = kTile;
@@ -285,8 +334,11 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     // scan role
     const int wv = tid >> 6, lane = tid & 63;
     constexpr bool kRowsOfStates = DISC != DISC_CONST;
-    const int ch = kRowsOfStates ? (lane & 15) : (lane >> 2);
-    const int j = kRowsOfStates ? (lane >> 4) : (lane & 3);
+    constexpr bool kBanks = kRowsOfStates && SPL == 1;
+    const int bank = (lane >> 2) & 3, q4 = lane & 3;
+    const int ch = kBanks ? 4 * (lane >> 4) + ((bank & 1) ? 3 - q4 : q4)
+                          : (kRowsOfStates ? (lane & 15) : (lane >> 2));
+    const int j = kBanks ? bank : (kRowsOfStates ? (lane >> 4) : (lane & 3));
     const int64_t d = d0 + ch;
     const bool dvalid = d < D;
     const int64_t dc = dvalid ? d : (D - 1);
@@ -426,24 +478,42 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             if constexpr (FINAL) part = fmaf(s_C[(n0 + s2) * kTS + t], h[s2], part);
         }
         if constexpr (FINAL) {
-            s_yp[wv][ch][t] = kRowsOfStates ? rows_sum(part) : group_sum<4>(part);   // every lane of the channel writes it
+            // every lane of the channel writes it
+            s_yp[wv][ch][t] = kBanks ? banks_sum(part) : (kRowsOfStates ? rows_sum(part) : group_sum<4>(part));
         } else {
             ssum += dl;
         }
     };
-    // Sixteen tokens t0 .. t0+15 of the row layout.  B and C are the same for
-    // every lane of a 16-lane row (one state, sixteen channels): lane ch of a
-    // row reads the row's B and C of token t0 + ch once, and token t0 + k
-    // takes them from lane k with a row broadcast (DPP row_newbcast), which
-    // the compiler folds into the multiply that consumes them.  Only
-    // (dt, dt*u), which differ per channel, are read from LDS per token.
+    // Sixteen tokens t0 .. t0+15.  B and C of a token are the same for every
+    // lane that holds the same state: a 16-lane row in the row layout, a
+    // 4-lane bank in the bank layout.  In the row layout lane k of a row
+    // reads its state's B and C of token t0 + k once and token t0 + k takes
+    // them from lane k with a row broadcast (DPP row_newbcast); in the bank
+    // layout lane q of a bank reads tokens t0 + 4q .. 4q+3 and token
+    // t0 + 4g + i takes element i of lane g with a bank broadcast (DPP
+    // quad_perm).  The compiler folds either broadcast into the multiply that
+    // consumes it.  Only (dt, dt*u), which differ per channel, are read from
+    // LDS per token.
     auto scan_block16 = [&](int t0) {
-        float bv[SPL], cv[SPL];
+        constexpr int NV = kBanks ? 4 : SPL;
+        float bv[NV], cv[NV];
+        if constexpr (kBanks) {
+            lds_read_k<4>(&s_B[n0 * kTS + t0 + 4 * q4], bv);
+            lds_read_k<4>(&s_C[n0 * kTS + t0 + 4 * q4], cv);
+        } else {
 #pragma unroll
-        for (int s2 = 0; s2 < SPL; ++s2) {
-            bv[s2] = s_B[(n0 + s2) * kTS + t0 + ch];
-            cv[s2] = s_C[(n0 + s2) * kTS + t0 + ch];
+            for (int s2 = 0; s2 < SPL; ++s2) {
+                bv[s2] = s_B[(n0 + s2) * kTS + t0 + ch];
+                cv[s2] = s_C[(n0 + s2) * kTS + t0 + ch];
+            }
         }
+        auto bcast = [&](auto gi, const float(&v)[NV], int s2) -> float {
+            constexpr int k = decltype(gi)::value;   // token t0 + k
+            if constexpr (kBanks)
+                return bank_bcast<k / 4>(v[k % 4]);
+            else
+                return row_bcast<k>(v[s2]);
+        };
         static_for<4>([&](auto gI) {
             constexpr int g = decltype(gI)::value;
             const int t = t0 + 4 * g;
@@ -456,7 +526,7 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             for (int s2 = 0; s2 < SPL; ++s2) {
                 static_for<4>([&](auto iI) {
                     constexpr int i = decltype(iI)::value;
-                    const float bq = row_bcast<4 * g + i>(bv[s2]);
+                    const float bq = bcast(std::integral_constant<int, 4 * g + i>(), bv, s2);
                     const float a = hw_exp2(dl[i] * A2[s2]);
                     float w;
                     if constexpr (DISC == DISC_DB)
@@ -466,11 +536,11 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
                     h[s2] = fmaf(a, h[s2], w);
                     // the first state's term is a product (a multiply takes the
                     // broadcast operand directly; fmaf(c, h, 0) does not)
-                    const float cq = row_bcast<4 * g + i>(cv[s2]);
+                    const float cq = bcast(std::integral_constant<int, 4 * g + i>(), cv, s2);
                     part[i] = (s2 == 0) ? cq * h[s2] : fmaf(cq, h[s2], part[i]);
                 });
             }
-            s_yp[wv][ch][t + j] = rows_transpose_sum(part);
+            s_yp[wv][ch][t + j] = kBanks ? banks_transpose_sum(part) : rows_transpose_sum(part);
         });
     };
     // four tokens t .. t+3: 16-byte LDS reads, one transposed quad reduction
@@ -506,7 +576,8 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             }
         }
         if constexpr (FINAL) {
-            s_yp[wv][ch][t + j] = kRowsOfStates ? rows_transpose_sum(part) : quad_transpose_sum(part, j);
+            s_yp[wv][ch][t + j] = kBanks ? banks_transpose_sum(part)
+                                         : (kRowsOfStates ? rows_transpose_sum(part) : quad_transpose_sum(part, j));
         } else {
 #pragma unroll
             for (int i = 0; i < 4; ++i) ssum += dl[i];

@@ -28,9 +28,9 @@
 // Arithmetic follows the sequence kernel operation by operation: the same
 // conv tap order, softplus, decay 2^(dt*A*log2 e) with A = -exp(A_log), and
 // the same readout tree -- chains over the sequence kernel's states per
-// lane, then pairwise within its lane quads, then pairwise across its four
-// wavefronts -- so a token-by-token decode reproduces the full forward bit
-// for bit.
+// lane, then its sum over the four lanes of a wavefront, then pairwise
+// across its four wavefronts -- so a token-by-token decode reproduces the
+// full forward bit for bit.
 #include <algorithm>
 
 #include "launch.hpp"
@@ -150,12 +150,16 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
         part[j / VL] = fmaf(Cq[j], hq[j], part[j / VL]);
     }
     if (active && nvalid > 0) store_k<kSPL>(hp, hq, nvalid, vecN);
-    // the sequence kernel's tree: its chains of VL states, four chains per
-    // lane quad ((c0 + c1) + (c2 + c3)), then its four wavefronts the same
-    // way; here the lane's four states hold 4/VL chains and the rest of the
-    // tree is the pairwise reduction over the channel's LPC lanes
+    // the sequence kernel's tree: its chains of VL states, the four chains
+    // of a wavefront ((c0 + c3) + (c1 + c2)) at one state per chain with an
+    // input-dependent decay, else ((c0 + c1) + (c2 + c3)), then its four
+    // wavefronts as ((w0 + w1) + (w2 + w3)); here the lane's four states hold
+    // 4/VL chains and the rest of the tree is the pairwise reduction over
+    // the channel's LPC lanes
     float ysum;
-    if constexpr (VL == 1)
+    if constexpr (VL == 1 && DISC != DISC_CONST)
+        ysum = (part[0] + part[3]) + (part[1] + part[2]);
+    else if constexpr (VL == 1)
         ysum = (part[0] + part[1]) + (part[2] + part[3]);
     else if constexpr (VL == 2)
         ysum = part[0] + part[1];

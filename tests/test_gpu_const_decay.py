@@ -214,6 +214,20 @@ def test_const_step_parity(ssm, S, D, N, W):
         np.testing.assert_array_equal(host(cs), csr)
 
 
+def test_const_fwd_many_channel_groups(ssm):
+    """A grid of over a thousand blocks with a partial last channel group in
+    each batch row, two whole tiles and a ragged tail; then the streaming step
+    reproduces a 768-block forward bit for bit."""
+    p = _rand(52, 6, 130, 3000, 16, 4)
+    _check_fwd(ssm, p)
+    p = _rand(53, 4, 20, 3072, 16, 4)
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32)
+    ys, h, cs = _step_gpu(ssm, p, 20)
+    assert torch.equal(ys, y)
+    assert torch.equal(h, hT)
+    assert torch.equal(cs, cso)
+
+
 @pytest.mark.parametrize("N", [16, 1, 33])
 def test_const_step_loop_equals_forward(ssm, N):
     """Token-by-token decode with the constant source reproduces the

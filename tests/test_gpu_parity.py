@@ -249,6 +249,46 @@ def test_fwd_deterministic(ssm):
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
 
 
+@pytest.mark.parametrize("disc,bf16,conv,W", [
+    (DB, False, True, 4),
+    (ZOH, False, True, 3),
+    (DB, True, True, 4),
+    (DB, False, False, 4),
+])
+def test_fwd_many_channel_groups(ssm, disc, bf16, conv, W):
+    """A grid of over a thousand blocks: D = 3000 channels (187 whole groups of
+    16 and a last group of 8 in each batch row), L = 130 is two whole tiles
+    and a ragged tail."""
+    p = _rand(70 + disc, 6, 130, 3000, 16, W=W, bf16=bf16)
+    dt = torch.bfloat16 if bf16 else torch.float32
+    y, hT, cso = _fwd_gpu(ssm, p, dt, disc=disc, conv=conv)
+    yr, hr, csr, _ = _fwd_oracle(p, disc=disc, conv=conv)
+    assert rel_linf(y, yr) <= tol(dt)
+    assert rel_linf(hT, hr) <= tol(dt)
+    if conv:
+        np.testing.assert_array_equal(host(cso), csr)
+
+
+def test_step_loop_equals_forward_many_groups(ssm):
+    """The streaming step reproduces the forward bit for bit on a grid of 768
+    blocks (4 batch rows x 192 channel groups)."""
+    p = _rand(75, 4, 20, 3072, 16)
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32)
+    h = dev(p["h0"])[None].contiguous()
+    cs = dev(p["conv_state"])[None].contiguous()
+    ys = []
+    for t in range(20):
+        ys.append(ssm.ssm_step(h, dev(p["x"][:, t])[None], dev(p["dt_raw"][:, t])[None], dev(p["A_log"])[None],
+                               dev(p["B"][:, t])[None], dev(p["C"][:, t])[None], conv_state=cs,
+                               z=dev(p["z"][:, t])[None], conv_w=dev(p["conv_w"])[None],
+                               conv_b=dev(p["conv_b"])[None], dt_bias=dev(p["dt_bias"])[None],
+                               Dskip=dev(p["Dskip"])[None])[0])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(ys, 1), y)
+    assert torch.equal(h[0], hT)
+    assert torch.equal(cs[0], cso)
+
+
 # ------------------------------------------------------------ workloads at full size
 
 def _mamba_fwd(ssm, p, dtype, chunk=0):
