@@ -230,6 +230,26 @@ __device__ __forceinline__ float banks_transpose_sum(const float (&p)[4]) {
         : "v"(v0), "v"(v1));
     return y;
 }
+// Two banks_transpose_sum of four tokens each, interleaved so that no DPP
+// read follows the write of its source closer than two instructions.
+__device__ __forceinline__ void banks_transpose_sum2(const float (&p)[4], const float (&q)[4], float &yp, float &yq) {
+    float a0, a1, b0, b1;
+    asm("s_nop 1\n\t"
+        "v_add_f32_dpp %0, %6, %6 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %0, %8, %8 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+        "v_add_f32_dpp %1, %7, %7 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %1, %9, %9 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+        "v_add_f32_dpp %2, %10, %10 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %2, %12, %12 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+        "v_add_f32_dpp %3, %11, %11 row_mirror row_mask:0xf bank_mask:0x3\n\t"
+        "v_add_f32_dpp %3, %13, %13 row_mirror row_mask:0xf bank_mask:0xc\n\t"
+        "v_add_f32_dpp %4, %0, %0 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %4, %1, %1 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+        "v_add_f32_dpp %5, %2, %2 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+        "v_add_f32_dpp %5, %3, %3 row_half_mirror row_mask:0xf bank_mask:0xa"
+        : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1), "=&v"(yp), "=&v"(yq)
+        : "v"(p[0]), "v"(p[1]), "v"(p[2]), "v"(p[3]), "v"(q[0]), "v"(q[1]), "v"(q[2]), "v"(q[3]));
+}
 // Every lane of a bank group receives the group's sum, in the same
 // association as banks_transpose_sum.
 __device__ __forceinline__ float banks_sum(float v) {
@@ -493,7 +513,8 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
     // t0 + 4g + i takes element i of lane g with a bank broadcast (DPP
     // quad_perm).  The compiler folds either broadcast into the multiply that
     // consumes it.  Only (dt, dt*u), which differ per channel, are read from
-    // LDS per token.
+    // LDS per token.  The bank layout reduces two groups of four tokens at a
+    // time, interleaved, so its DPP reads need no wait states of their own.
     auto scan_block16 = [&](int t0) {
         constexpr int NV = kBanks ? 4 : SPL;
         float bv[NV], cv[NV];
@@ -514,14 +535,17 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
             else
                 return row_bcast<k>(v[s2]);
         };
+        float parts[4][4];
         static_for<4>([&](auto gI) {
             constexpr int g = decltype(gI)::value;
             const int t = t0 + 4 * g;
+            float (&part)[4] = parts[g];
             const float4 d01 = *reinterpret_cast<const float4 *>(&s_dl[ch][t]);
             const float4 d23 = *reinterpret_cast<const float4 *>(&s_dl[ch][t + 2]);
             const float dl[4] = {d01.x, d01.z, d23.x, d23.z};
             const float dy[4] = {d01.y, d01.w, d23.y, d23.w};
-            float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) part[i] = 0.0f;
 #pragma unroll
             for (int s2 = 0; s2 < SPL; ++s2) {
                 static_for<4>([&](auto iI) {
@@ -540,7 +564,14 @@ __global__ __launch_bounds__(kThreads) void scan_fwd_kernel(FwdParams p) {
                     part[i] = (s2 == 0) ? cq * h[s2] : fmaf(cq, h[s2], part[i]);
                 });
             }
-            s_yp[wv][ch][t + j] = kBanks ? banks_transpose_sum(part) : rows_transpose_sum(part);
+            if constexpr (!kBanks) {
+                s_yp[wv][ch][t + j] = rows_transpose_sum(part);
+            } else if constexpr (g % 2 == 1) {
+                float ya, yb;
+                banks_transpose_sum2(parts[g - 1], part, ya, yb);
+                s_yp[wv][ch][t - 4 + j] = ya;
+                s_yp[wv][ch][t + j] = yb;
+            }
         });
     };
     // four tokens t .. t+3: 16-byte LDS reads, one transposed quad reduction
