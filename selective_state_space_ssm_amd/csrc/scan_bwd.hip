@@ -450,6 +450,30 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     for (int s = 0; s < S; ++s) asm volatile("" : "+v"(h[s]));
     asm volatile("" : "+v"(dtb), "+v"(Dd));
     const int M1 = (K + T1P - 1) / T1P;   // steps
+    // A tile's per-token values (lane l: token l + 16 jj) and its B column,
+    // read from the staged step without lane masks: rows past the chunk were
+    // staged as 0, and their tokens get dt = 0 (no decay, no write).
+    auto walk_prep = [&](int jt, int64_t ts, float (&wdl)[TP], float (&wdu)[TP], float (&wbq)[T][S]) {
+#pragma unroll
+        for (int jj = 0; jj < TP; ++jj) {
+            const int tt = l + 16 * jj;
+            const bool v = tt < T && ts + tt < Le;
+            const int e = (jt * T + min(tt, T - 1)) * kXR + cl;
+            const float uu = s1_u[e];
+            float dl;
+            if constexpr (DISC == DISC_CONST)
+                dl = v ? 1.0f : 0.0f;
+            else
+                dl = v ? softplus_f(s1_dt[e] + dtb) : 0.0f;
+            wdl[jj] = dl;
+            wdu[jj] = (DISC == DISC_DB) ? dl * uu : (v ? uu : 0.0f);
+        }
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+#pragma unroll
+            for (int s = 0; s < S; ++s) wbq[i][s] = s1_B[(jt * T + i) * NP + l + 16 * s];
+        }
+    };
     fetch1(0, qu[0], qdt[0], qB[0]);
     for (int m0 = 0; m0 < M1; m0 += 2) {
         static_for<2>([&](auto jc) {
@@ -460,34 +484,40 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
                 stage1(qu[j], qdt[j], qB[j]);
                 __syncthreads();
                 fetch1(m + 1, qu[1 - j], qdt[1 - j], qB[1 - j]);
-#pragma unroll 1
-                for (int jt = 0; jt < T1P; ++jt) {
+                // The step's tiles in one straight run: the next tile's
+                // per-token values and B column are read and computed while
+                // this tile is walked.  Tiles past the chunk walk on dt = 0
+                // and store no checkpoint; the state is not used after the
+                // walk.
+                float wdl[2][TP], wdu[2][TP], wbq[2][T][S];
+                walk_prep(0, (int64_t)(tile0 + m * T1P) * T, wdl[0], wdu[0], wbq[0]);
+                static_for<T1P>([&](auto tc) {
+                    constexpr int jt = decltype(tc)::value, cur = jt & 1;
                     const int k = m * T1P + jt;
                     store_ckpt(k);
-                    if (k + 1 < K) {   // the last tile's end state is not needed
-                        transform_at(s1_u, s1_dt, jt * T, (int64_t)(tile0 + k) * T);
+                    if constexpr (jt + 1 < T1P)
+                        walk_prep(jt + 1, (int64_t)(tile0 + k + 1) * T, wdl[1 - cur], wdu[1 - cur], wbq[1 - cur]);
 #pragma unroll
-                        for (int i = 0; i < T; ++i) {
-                            const float dli = tokv(tk_dl, i), dui = tokv(tk_du, i);
+                    for (int i = 0; i < T; ++i) {
+                        const float dli = tokv(wdl[cur], i), dui = tokv(wdu[cur], i);
 #pragma unroll
-                            for (int s = 0; s < S; ++s) {
-                                const float bq = s1_B[(jt * T + i) * NP + l + 16 * s];
-                                if constexpr (DISC == DISC_CONST) {
-                                    // dt is 1, or 0 past the end (no decay, no write there)
-                                    h[s] += fmaf(dli * am1[s], h[s], dui * bq);
-                                } else {
-                                    const float a = hw_exp2(dli * A2[s]);
-                                    float w;
-                                    if constexpr (DISC == DISC_DB)
-                                        w = dui * bq;
-                                    else
-                                        w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
-                                    h[s] = fmaf(a, h[s], w);
-                                }
+                        for (int s = 0; s < S; ++s) {
+                            const float bq = wbq[cur][i][s];
+                            if constexpr (DISC == DISC_CONST) {
+                                // dt is 1, or 0 past the end (no decay, no write there)
+                                h[s] += fmaf(dli * am1[s], h[s], dui * bq);
+                            } else {
+                                const float a = hw_exp2(dli * A2[s]);
+                                float w;
+                                if constexpr (DISC == DISC_DB)
+                                    w = dui * bq;
+                                else
+                                    w = expm1f(dli * An[s]) * Ainv[s] * bq * dui;
+                                h[s] = fmaf(a, h[s], w);
                             }
                         }
                     }
-                }
+                });
             }
         });
     }
