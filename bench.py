@@ -186,6 +186,23 @@ class EventTimer:
         return sum(s.elapsed_time(e) for s, e in self.pairs) / max(1, len(self.pairs))
 
 
+SETTLE_MS = 60
+
+
+def settle(torch, fn, ms=SETTLE_MS):
+    """Untimed calls of fn for about ms of wall time (at least two), so that a
+    workload is timed at the loaded clocks and with its first-call effects
+    (fresh output pages, cold instruction caches) behind it."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < 2 or time.perf_counter() - t0 < ms * 1e-3:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -353,8 +370,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
         ssm.ssm_scan_bwd(u, P["dt_raw"], P["A_log"], P["B"], P["C"], P["dy"], dt_bias=P["dt_bias"],
                          Dskip=P["Dskip"], z=P["z"], out=out, workspace=ws)
 
-    for _ in range(2):
-        bwd()
+    settle(torch, bwd)
     tm = EventTimer(torch)
     for _ in range(reps):
         tm.run(bwd)
@@ -375,8 +391,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
                          Dskip=P["Dskip"], z=P["z"], conv_w=P["conv_w"], conv_b=P["conv_b"], out=outc,
                          workspace=wsc)
 
-    for _ in range(2):
-        bwd_conv()
+    settle(torch, bwd_conv)
     tm = EventTimer(torch)
     for _ in range(reps):
         tm.run(bwd_conv)
@@ -405,8 +420,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
     y2 = torch.empty(B2, L2, D, device="cuda")
     f2 = lambda: ssm.ssm_scan_fwd(Q["x"], Q["dt_raw"], Q["A_log"], Q["B"], Q["C"], dt_bias=Q["dt_bias"],
                                   Dskip=Q["Dskip"], z=Q["z"], conv_w=Q["conv_w"], conv_b=Q["conv_b"], y=y2)
-    for _ in range(3):
-        f2()
+    settle(torch, f2)
     tm = EventTimer(torch)
     for _ in range(reps):
         tm.run(f2)
@@ -427,8 +441,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
         yc = torch.empty(B, L, D, device="cuda")
         fc = lambda: ssm.ssm_scan_fwd(Cc["x"], None, Cc["A_log"], Cc["B"], Cc["C"], Dskip=Cc["Dskip"], z=Cc["z"],
                                       conv_w=Cc["conv_w"], conv_b=Cc["conv_b"], y=yc, disc=ssm.SSM_DECAY_CONST)
-        for _ in range(3):
-            fc()
+        settle(torch, fc)
         tm = EventTimer(torch)
         for _ in range(reps):
             tm.run(fc)
@@ -452,8 +465,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
     ws4 = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_size(desc)), dtype=torch.uint8, device="cuda")
     f4 = lambda: ssm.ssm_scan_fwd(R["x"], R["dt_raw"], R["A_log"], R["B"], R["C"], dt_bias=R["dt_bias"],
                                   Dskip=R["Dskip"], z=R["z"], y=y4, workspace=ws4)
-    for _ in range(2):
-        f4()
+    settle(torch, f4)
     tm = EventTimer(torch)
     for _ in range(reps):
         tm.run(f4)
@@ -472,8 +484,7 @@ def bench_extras(torch, np, si, ssm, dev, args):
     outb = {}
     b4 = lambda: ssm.ssm_scan_bwd(R["x"], R["dt_raw"], R["A_log"], R["B"], R["C"], R["dy"], dt_bias=R["dt_bias"],
                                   Dskip=R["Dskip"], z=R["z"], out=outb, workspace=wsb)
-    for _ in range(2):
-        b4()
+    settle(torch, b4)
     tm = EventTimer(torch)
     for _ in range(max(3, reps // 2)):
         tm.run(b4)
@@ -552,6 +563,23 @@ def bench_extras(torch, np, si, ssm, dev, args):
             "note": "state + history of the 6 blocks (%d MB) fit the 256 MB last-level cache"
                     % round(nblk * S * (D * N * (2 if nb == bytes16 else 4) + 3 * D * 4) / 1e6)}
         log("streaming %s: %.1f us per token step" % (name, ms * 1e3))
+    # The stacked step again, with the last-level cache emptied before every
+    # step (an untimed read and write of an unrelated 1 GiB buffer), so that
+    # the state streams from HBM: the gap to the resident loop above shows
+    # how much of that loop's state stayed in the 256 MB cache.
+    flush = torch.empty(1 << 28, device="cuda")
+    stacked(0)
+    tm = EventTimer(torch)
+    for t in range(64):
+        flush.add_(1.0)
+        tm.run(lambda: stacked(t % pool))
+    ms = tm.mean_ms()
+    ex["streaming_6blk_256streams_stacked_one_launch_cache_flushed"] = {
+        "tokens_per_s": S / (ms * 1e-3), "us_per_token_step": round(ms * 1e3, 2),
+        "algorithmic_GBps": round(nblk * per_block_bytes / (ms * 1e-3) / 1e9, 1),
+        "note": "each step timed alone after a 1 GiB pass over another buffer: the state comes from HBM"}
+    log("streaming stacked_one_launch, cache flushed before each step: %.1f us per token step" % (ms * 1e3))
+    del flush
     del h, cs, toks, ys, prm
     torch.cuda.empty_cache()
 

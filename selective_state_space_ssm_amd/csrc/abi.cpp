@@ -300,7 +300,9 @@ ssm_status ssm_scan_bwd(const ssm_scan_desc *desc, const void *x, const void *dt
         const int64_t KC = cdiv(std::max<int64_t>(L, 1), chunk);   // chunks along time
         if (!grid_ok({Bn, cdiv(D, 48), KC}) || !grid_ok({Bn, cdiv(std::max<int64_t>(L, 1) * N, 256)}) ||
             !grid_ok({Bn, KC, cdiv(8 * D, 256)}) || !grid_ok({Bn, cdiv(D * N, 256)}) ||
-            (W > 0 && !grid_ok({Bn, cdiv(cdiv(std::max<int64_t>(L, 1), 32) * D, 256)})))   // conv, conv backward
+            (W > 0 && !grid_ok({Bn, cdiv(cdiv(std::max<int64_t>(L, 1), 32) * D, 256)})) ||   // conv, conv backward
+            // the sums' launch: dB, dC blocks then the parameter blocks
+            cdiv(Bn * std::max<int64_t>(L, 1) * N, 256) + cdiv(std::max(D * N, D), 256) > kMaxGrid)
             return SSM_ERR_BAD_SHAPE;
     }
     const size_t need = ssm::scan_bwd_workspace_bytes(Bn, L, D, N, chunk, W, io_size(desc->io_dtype));

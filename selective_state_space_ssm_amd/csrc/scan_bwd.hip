@@ -794,26 +794,30 @@ __global__ __launch_bounds__(kThreads) void scan_bwd_kernel(BwdParams p) {
     }
 }
 
+// The cross-workgroup sums of the backward, in one launch: blocks below nbc
+// add the dB, dC partials over the G channel groups (in order of g), the
+// others add the dA_log, dDskip and d_dt_bias partials over the batch rows
+// and time chunks (in order).
 template <typename IOT>
-__global__ __launch_bounds__(256) void bwd_reduce_bc(const float *pB, const float *pC, int G, int64_t total,
-                                                     IOT *dB, IOT *dC) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= total) return;
-    float sb = 0.0f, sc = 0.0f;
-    // in order of g; unrolled so that several partials are in flight
+__global__ __launch_bounds__(256) void bwd_reduce(const float *pB, const float *pC, int G, int64_t total,
+                                                  IOT *dB, IOT *dC, int64_t nbc, const float *A_log,
+                                                  const float *pA, const float *pD, const float *pT, int64_t B,
+                                                  int64_t D, int64_t N, float *dA_log, float *dD, float *ddtb) {
+    if ((int64_t)blockIdx.x < nbc) {
+        const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+        if (i >= total) return;
+        float sb = 0.0f, sc = 0.0f;
+        // unrolled so that several partials are in flight
 #pragma unroll 8
-    for (int g = 0; g < G; ++g) {
-        sb += pB[(int64_t)g * total + i];
-        sc += pC[(int64_t)g * total + i];
+        for (int g = 0; g < G; ++g) {
+            sb += pB[(int64_t)g * total + i];
+            sc += pC[(int64_t)g * total + i];
+        }
+        if (dB) store_io(dB + i, sb);
+        if (dC) store_io(dC + i, sc);
+        return;
     }
-    if (dB) store_io(dB + i, sb);
-    if (dC) store_io(dC + i, sc);
-}
-
-__global__ __launch_bounds__(256) void bwd_reduce_params(const float *A_log, const float *pA, const float *pD,
-                                                         const float *pT, int64_t B, int64_t D, int64_t N,
-                                                         float *dA_log, float *dD, float *ddtb) {
-    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t i = ((int64_t)blockIdx.x - nbc) * blockDim.x + threadIdx.x;
     if (i < D * N && dA_log) {
         float s = 0.0f;
         for (int64_t b = 0; b < B; ++b) s += pA[b * D * N + i];
@@ -1188,15 +1192,11 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t total = a.B * a.L * a.N;
-    if ((a.dB || a.dC) && total > 0) {
-        hipLaunchKernelGGL((bwd_reduce_bc<IOT>), dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, w.pB,
-                           w.pC, G, total, static_cast<IOT *>(a.dB), static_cast<IOT *>(a.dC));
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
+    const int64_t nbc = ((a.dB || a.dC) && total > 0) ? (total + 255) / 256 : 0;
     const int64_t pn = std::max(a.D * a.N, a.D);
-    hipLaunchKernelGGL(bwd_reduce_params, dim3((unsigned)((pn + 255) / 256)), dim3(256), 0, s, a.A_log, w.pA,
-                       w.pD, w.pT, a.B * KC, a.D, a.N, a.dA_log, a.dD, a.ddt_bias);
+    hipLaunchKernelGGL((bwd_reduce<IOT>), dim3((unsigned)(nbc + (pn + 255) / 256)), dim3(256), 0, s, w.pB, w.pC,
+                       G, total, static_cast<IOT *>(a.dB), static_cast<IOT *>(a.dC), nbc, a.A_log, w.pA, w.pD,
+                       w.pT, a.B * KC, a.D, a.N, a.dA_log, a.dD, a.ddt_bias);
     return hipGetLastError();
 }
 
