@@ -242,6 +242,17 @@ def test_launch_grid_limit(ssm):
     assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24, N=1), y=_addr(0)) == ssm.SSM_ERR_ALIAS
 
 
+def test_bwd_sums_launch_grid_limit(ssm):
+    """The backward's cross-workgroup sums are one launch: the dB, dC blocks,
+    then the parameter blocks.  A shape whose dB, dC blocks alone fill the
+    2^31 - 1 workgroup limit (B*L*N / 256 of them) is rejected before any HIP
+    call once the parameter blocks are added; one row of blocks fewer passes
+    and stops at the missing workspace."""
+    L = 4 * (2 ** 31 - 1)              # L * 64 / 256 = 2^31 - 1 blocks at N = 64
+    assert _bwd(ssm, _desc(ssm, B=1, L=L, D=4, N=64)) == ssm.SSM_ERR_BAD_SHAPE
+    assert _bwd(ssm, _desc(ssm, B=1, L=L - 4, D=4, N=64)) == ssm.SSM_ERR_WORKSPACE
+
+
 def test_conv_validation(ssm):
     L = ssm.lib()
     d = ssm.ssm_conv_desc(2, 16, 32, 4, 1, 0, 0)
