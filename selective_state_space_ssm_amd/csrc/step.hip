@@ -14,7 +14,9 @@
 // A_log one contiguous kilobyte per wavefront (16 channels x 64 B).  The
 // per-channel work (conv, softplus, gate) is repeated in the LPC lanes, which
 // compute identical values; lane 0 of the channel stores y and the history.
-// Every load of a lane is issued before any arithmetic.
+// Every load of a lane is issued before any arithmetic.  The common shape
+// (fp32 io, N = 16, a 4-tap conv, D a multiple of 64) runs step_fast_kernel:
+// the same arithmetic with unconditional buffer loads on per-row bases.
 //
 // The state may be stored in bf16 (HT = bf16_t): it is loaded, updated and
 // read out in float32 and rounded to bf16 (nearest, ties to even) only when
@@ -182,6 +184,127 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
     }
 }
 
+// The common shape on a shorter path: fp32 io, N = 16 (four lanes of four
+// states per channel), a 4-tap conv, D a multiple of 64 (every lane of every
+// workgroup holds a channel).  The loads are unconditional buffer loads on
+// per-row scalar bases with 32-bit lane offsets (no guards, no per-lane 64-bit
+// addresses); the arithmetic is step_kernel's for this shape, operation by
+// operation, so the two agree bit for bit.
+template <typename HT, int DISC>
+__global__ __launch_bounds__(256) void step_fast_kernel(StepArgs a) {
+    const int64_t D = a.D, S = a.S;
+    const uint32_t bpr = (uint32_t)(D / 64);
+    const uint32_t row = blockIdx.x / bpr;                  // k * S + s
+    const uint32_t rk = row / (uint32_t)S;
+    const uint32_t gl = (blockIdx.x - row * bpr) * 256u + threadIdx.x;
+    const int q = (int)(gl & 3u);
+    const uint32_t d = gl >> 2;
+    const int n0 = q * kSPL;
+    const float *Xp = static_cast<const float *>(a.x);
+    const float *Zp = static_cast<const float *>(a.z);
+    float *Yp = static_cast<float *>(a.y);
+    HT *Hp = static_cast<HT *>(a.h) + (int64_t)row * D * 16;
+    const buf_t rH = make_buf(Hp, (uint64_t)D * 16 * sizeof(HT));
+    const buf_t rA = make_buf(a.A_log + (int64_t)rk * D * 16, (uint64_t)D * 64);
+    const buf_t rB = make_buf(static_cast<const float *>(a.Bm) + (int64_t)row * 16, 64);
+    const buf_t rC = make_buf(static_cast<const float *>(a.Cm) + (int64_t)row * 16, 64);
+    const buf_t rX = make_buf(Xp + (int64_t)row * D, (uint64_t)D * 4);
+    float *hist = a.conv_state + (int64_t)row * 3 * D;
+    const buf_t rHi = make_buf(hist, (uint64_t)D * 12);
+    const uint32_t od = d * 4u, oh = (d * 16u + (uint32_t)n0) * (uint32_t)sizeof(HT);
+
+    // ---- loads, all issued before any arithmetic
+    float hq[kSPL], Bq[kSPL], Cq[kSPL], al[kSPL], cw[4], hv[3];
+    if constexpr (sizeof(HT) == 4) {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b128(rH, oh, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) hq[i] = __uint_as_float(v[i]);
+    } else {
+        const auto v = __builtin_amdgcn_raw_buffer_load_b64(rH, oh, 0, 0);
+        hq[0] = __uint_as_float(v[0] << 16); hq[1] = __uint_as_float(v[0] & 0xffff0000u);
+        hq[2] = __uint_as_float(v[1] << 16); hq[3] = __uint_as_float(v[1] & 0xffff0000u);
+    }
+    {
+        const auto vb = __builtin_amdgcn_raw_buffer_load_b128(rB, (uint32_t)n0 * 4u, 0, 0);
+        const auto vc = __builtin_amdgcn_raw_buffer_load_b128(rC, (uint32_t)n0 * 4u, 0, 0);
+        const auto va = __builtin_amdgcn_raw_buffer_load_b128(rA, (d * 16u + (uint32_t)n0) * 4u, 0, 0);
+        const auto vw = __builtin_amdgcn_raw_buffer_load_b128(make_buf(a.conv_w + (int64_t)rk * D * 4, (uint64_t)D * 16),
+                                                             d * 16u, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            Bq[i] = __uint_as_float(vb[i]);
+            Cq[i] = __uint_as_float(vc[i]);
+            al[i] = __uint_as_float(va[i]);
+            cw[i] = __uint_as_float(vw[i]);
+        }
+    }
+    const float xr = buf_ld(rX, od, Xp);
+    float dtr = 0.0f;
+    if constexpr (DISC != DISC_CONST)
+        dtr = buf_ld(make_buf(static_cast<const float *>(a.dt) + (int64_t)row * D, (uint64_t)D * 4), od, Xp);
+    const float zr = Zp != nullptr ? buf_ld(make_buf(Zp + (int64_t)row * D, (uint64_t)D * 4), od, Xp) : 0.0f;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) hv[j] = buf_ld(rHi, (uint32_t)j * (uint32_t)D * 4u + od, Xp);
+    const int64_t kD = (int64_t)rk * D;
+    const float dtb = (DISC != DISC_CONST && a.dt_bias) ? buf_ld(make_buf(a.dt_bias + kD, (uint64_t)D * 4), od, Xp) : 0.0f;
+    const float Dd = a.Dskip ? buf_ld(make_buf(a.Dskip + kD, (uint64_t)D * 4), od, Xp) : 0.0f;
+    const float cb = a.conv_b ? buf_ld(make_buf(a.conv_b + kD, (uint64_t)D * 4), od, Xp) : 0.0f;
+
+    // ---- arithmetic (step_kernel's, W = 4, four valid states per lane)
+    float acc = cb;
+#pragma unroll
+    for (int j = 0; j < 3; ++j) acc = fmaf(cw[j], hv[j], acc);
+    acc = fmaf(cw[3], xr, acc);
+    const float uu = silu_f(acc);
+    const float dl = (DISC != DISC_CONST) ? softplus_f(dtr + dtb) : 1.0f;
+    const float du = dl * uu;
+    float part[kSPL];
+#pragma unroll
+    for (int j = 0; j < kSPL; ++j) part[j] = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kSPL; ++j) {
+        const float A = neg_exp_f(al[j]);
+        const float A2 = A * kLog2e;
+        if constexpr (DISC == DISC_CONST) {
+            hq[j] += fmaf(expm1f(A), hq[j], uu * Bq[j]);
+        } else {
+            const float dec = hw_exp2(dl * A2);
+            float w;
+            if constexpr (DISC == DISC_DB)
+                w = du * Bq[j];
+            else
+                w = expm1f(dl * A) * (1.0f / A) * Bq[j] * uu;
+            hq[j] = fmaf(dec, hq[j], w);
+        }
+        part[j] = fmaf(Cq[j], hq[j], part[j]);
+    }
+    if constexpr (sizeof(HT) == 4) {
+        __attribute__((ext_vector_type(4))) unsigned int v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __float_as_uint(hq[i]);
+        __builtin_amdgcn_raw_buffer_store_b128(v, rH, oh, 0, 0);
+    } else {
+        __attribute__((ext_vector_type(2))) unsigned int v;
+        v[0] = (uint32_t)bf16_rne(hq[0]) | ((uint32_t)bf16_rne(hq[1]) << 16);
+        v[1] = (uint32_t)bf16_rne(hq[2]) | ((uint32_t)bf16_rne(hq[3]) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(v, rH, oh, 0, 0);
+    }
+    float ysum;
+    if constexpr (DISC != DISC_CONST)
+        ysum = (part[0] + part[3]) + (part[1] + part[2]);
+    else
+        ysum = (part[0] + part[1]) + (part[2] + part[3]);
+    ysum = group_sum<4>(ysum);
+    float yv = ysum + Dd * uu;
+    if (Zp != nullptr) yv *= silu_f(zr);
+    if (q == 0) {
+        buf_st(make_buf(Yp + (int64_t)row * D, (uint64_t)D * 4), od, Yp, yv);
+        buf_st(rHi, od, hist, hv[1]);
+        buf_st(rHi, (uint32_t)D * 4u + od, hist, hv[2]);
+        buf_st(rHi, 2u * (uint32_t)D * 4u + od, hist, xr);
+    }
+}
+
 // One run of workgroups per (block, stream) row: ceil(D*LPC / 256) each.
 template <int LPC>
 unsigned step_blocks(const StepArgs &a) {
@@ -237,6 +360,21 @@ hipError_t launch_step_dtproj(const StepArgs &a, hipStream_t s) {
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     if (a.nblk * a.S * a.D == 0) return hipSuccess;
+    if (!a.bf16 && a.N == 16 && a.W == 4 && a.D % 64 == 0) {
+        const dim3 grid((unsigned)(a.nblk * a.S * (a.D / 64)));
+#define SSM_STEP_FAST(DI)                                                                            \
+    if (a.disc == DI) {                                                                              \
+        if (a.state_bf16)                                                                            \
+            hipLaunchKernelGGL((step_fast_kernel<bf16_t, DI>), grid, dim3(256), 0, s, a);            \
+        else                                                                                         \
+            hipLaunchKernelGGL((step_fast_kernel<float, DI>), grid, dim3(256), 0, s, a);             \
+        return hipGetLastError();                                                                    \
+    }
+        SSM_STEP_FAST(DISC_DB)
+        SSM_STEP_FAST(DISC_ZOH)
+        SSM_STEP_FAST(DISC_CONST)
+#undef SSM_STEP_FAST
+    }
     if (a.state_bf16) {
         if (a.bf16) return launch_io<bf16_t, bf16_t>(a, s);
         return launch_io<float, bf16_t>(a, s);

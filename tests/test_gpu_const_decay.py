@@ -203,7 +203,7 @@ def _step_oracle(p, steps, state_bf16=False, gate=True):
     return np.stack(ys, 1), h, cs
 
 
-@pytest.mark.parametrize("S,D,N,W", [(4, 40, 16, 4), (3, 8, 1, 3), (2, 16, 33, 2), (5, 24, 64, 1)])
+@pytest.mark.parametrize("S,D,N,W", [(4, 40, 16, 4), (3, 8, 1, 3), (2, 16, 33, 2), (5, 24, 64, 1), (4, 128, 16, 4)])
 def test_const_step_parity(ssm, S, D, N, W):
     p = _rand(48, S, 12, D, N, W)
     y, h, cs = _step_gpu(ssm, p, 12)
@@ -228,11 +228,12 @@ def test_const_fwd_many_channel_groups(ssm):
     assert torch.equal(cs, cso)
 
 
-@pytest.mark.parametrize("N", [16, 1, 33])
-def test_const_step_loop_equals_forward(ssm, N):
+@pytest.mark.parametrize("N,D", [(16, 48), (1, 48), (33, 48), (16, 128)])
+def test_const_step_loop_equals_forward(ssm, N, D):
     """Token-by-token decode with the constant source reproduces the
-    sequence kernel bit for bit."""
-    p = _rand(49, 3, 25, 48, N, 4)
+    sequence kernel bit for bit (D = 128 at N = 16 takes the common shape's
+    step path)."""
+    p = _rand(49, 3, 25, D, N, 4)
     y, hT, cso = _fwd_gpu(ssm, p, torch.float32)
     ys, h, cs = _step_gpu(ssm, p, 25)
     assert torch.equal(ys, y)
@@ -240,10 +241,10 @@ def test_const_step_loop_equals_forward(ssm, N):
     assert torch.equal(cs, cso)
 
 
-@pytest.mark.parametrize("io", [torch.float32, torch.bfloat16])
-def test_const_step_bf16_state(ssm, io):
+@pytest.mark.parametrize("io,D", [(torch.float32, 32), (torch.bfloat16, 32), (torch.float32, 64)])
+def test_const_step_bf16_state(ssm, io, D):
     steps = 40
-    p = _rand(50, 4, steps, 32, 16, 4, bf16=io == torch.bfloat16, slow=True)
+    p = _rand(50, 4, steps, D, 16, 4, bf16=io == torch.bfloat16, slow=True)
     y, h, _ = _step_gpu(ssm, p, steps, io=io, state_dtype=torch.bfloat16)
     yr, hr, _ = _step_oracle(p, steps, state_bf16=True)
     assert h.dtype == torch.bfloat16

@@ -407,6 +407,59 @@ def test_step_loop_equals_forward(ssm, disc):
     assert torch.equal(cs[0], cso)
 
 
+@pytest.mark.parametrize("disc", [DB, ZOH])
+@pytest.mark.parametrize("gate", [True, False])
+@pytest.mark.parametrize("state_bf16", [False, True])
+@pytest.mark.parametrize("params", [True, False])
+def test_step_common_shape_parity(ssm, disc, gate, state_bf16, params):
+    """The common shape's path (fp32 io, N = 16, a 4-tap conv, D a multiple of
+    64; D = 128 is two workgroups per stream) against the oracle's step over
+    12 tokens: gated and ungated, float32 and bf16 stored state, with and
+    without dt_bias, Dskip and conv_b."""
+    S, D, steps = 5, 128, 12
+    p = _rand(19, S, steps, D, 16, 4)
+    if not params:
+        p["dt_bias"] = np.zeros_like(p["dt_bias"])
+        p["Dskip"] = np.zeros_like(p["Dskip"])
+        p["conv_b"] = np.zeros_like(p["conv_b"])
+    y_ref, h_ref, cs_ref = _step_oracle_loop(p, steps, disc=disc, gate=gate, state_bf16=state_bf16)
+    h = dev(p["h0"], torch.bfloat16 if state_bf16 else torch.float32)[None].contiguous()
+    cs = dev(p["conv_state"])[None].contiguous()
+    opt = lambda k: dev(p[k])[None] if params else None
+    ys = []
+    for t in range(steps):
+        ys.append(ssm.ssm_step(h, dev(p["x"][:, t])[None], dev(p["dt_raw"][:, t])[None], dev(p["A_log"])[None],
+                               dev(p["B"][:, t])[None], dev(p["C"][:, t])[None], conv_state=cs,
+                               z=dev(p["z"][:, t])[None] if gate else None, conv_w=dev(p["conv_w"])[None],
+                               conv_b=opt("conv_b"), dt_bias=opt("dt_bias"), Dskip=opt("Dskip"), disc=disc)[0])
+    torch.cuda.synchronize()
+    tol = BF16_TOL if state_bf16 else FP32_TOL
+    assert rel_linf(torch.stack(ys, 1), y_ref) <= tol
+    assert rel_linf(h[0], h_ref) <= tol
+    np.testing.assert_array_equal(host(cs[0]), cs_ref)
+
+
+@pytest.mark.parametrize("disc", [DB, ZOH])
+def test_step_common_shape_loop_equals_forward(ssm, disc):
+    """At the common shape (D = 192, three workgroups per stream) the
+    token-by-token decode still reproduces the full forward bit for bit."""
+    p = _rand(21, 3, 25, 192, 16, 4)
+    y, hT, cso = _fwd_gpu(ssm, p, torch.float32, disc=disc)
+    h = dev(p["h0"])[None].contiguous()
+    cs = dev(p["conv_state"])[None].contiguous()
+    ys = []
+    for t in range(25):
+        ys.append(ssm.ssm_step(h, dev(p["x"][:, t])[None], dev(p["dt_raw"][:, t])[None], dev(p["A_log"])[None],
+                               dev(p["B"][:, t])[None], dev(p["C"][:, t])[None], conv_state=cs,
+                               z=dev(p["z"][:, t])[None], conv_w=dev(p["conv_w"])[None],
+                               conv_b=dev(p["conv_b"])[None], dt_bias=dev(p["dt_bias"])[None],
+                               Dskip=dev(p["Dskip"])[None], disc=disc)[0])
+    torch.cuda.synchronize()
+    assert torch.equal(torch.stack(ys, 1), y)
+    assert torch.equal(h[0], hT)
+    assert torch.equal(cs[0], cso)
+
+
 def test_step_graph_replay(ssm):
     """Streaming steps captured in a HIP graph (as the decode benchmark runs
     them): every replay, with eager work and synchronisation in between,
