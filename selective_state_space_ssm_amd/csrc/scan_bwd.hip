@@ -1029,12 +1029,25 @@ __global__ __launch_bounds__(256) void bwd_carry_kernel(const float *A_log, cons
     const int64_t n = i % N, d = (i / N) % D, b = i / (N * D);
     const float A = neg_exp_f(A_log[d * N + n]);
     float G = dhT ? dhT[i] : 0.0f;
-    for (int k = KC - 1; k >= 0; --k) {
-        const int64_t o = ((b * KC + k) * D + d) * N + n;
-        const float Rk = k > 0 ? RG[o] : 0.0f;
-        RG[o] = G;
-        // Lambda_k G + R_k in complement form, G + ((Lambda_k - 1) G + R_k)
-        if (k > 0) G += fmaf(expm1f(A * Sdt[(b * KC + k) * D + d]), G, Rk);
+    // eight chunks' summaries loaded ahead of their links of the chain (see
+    // carry_kernel)
+    for (int k1 = KC - 1; k1 >= 0; k1 -= 8) {
+        float Rv[8], Sv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = k1 - j;
+            Rv[j] = k > 0 ? RG[((b * KC + k) * D + d) * N + n] : 0.0f;
+            Sv[j] = k > 0 ? Sdt[(b * KC + k) * D + d] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int k = k1 - j;
+            if (k >= 0) {
+                RG[((b * KC + k) * D + d) * N + n] = G;
+                // Lambda_k G + R_k in complement form, G + ((Lambda_k - 1) G + R_k)
+                if (k > 0) G += fmaf(expm1f(A * Sv[j]), G, Rv[j]);
+            }
+        }
     }
 }
 

@@ -740,11 +740,25 @@ __global__ __launch_bounds__(256) void carry_kernel(const float *A_log, const fl
         const int64_t n = i % N, d = (i / N) % D, b = i / (N * D);
         const float A = neg_exp_f(A_log[d * N + n]);
         float H = h0 ? h0[i] : 0.0f;
-        for (int k = 0; k < K; ++k) {
-            const int64_t o = ((b * K + k) * D + d) * N + n;
-            const float Wk = agg_h[o];
-            agg_h[o] = H;
-            if (k + 1 < K) H += fmaf(expm1f(A * agg_s[(b * K + k) * D + d]), H, Wk);
+        // Eight chunks' summaries are loaded before their links of the chain
+        // are taken: loaded one at a time, each load would wait for the store
+        // before it (the compiler cannot tell them apart).
+        for (int k0 = 0; k0 < K; k0 += 8) {
+            float Wv[8], Sv[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = k0 + j;
+                Wv[j] = k < K ? agg_h[((b * K + k) * D + d) * N + n] : 0.0f;
+                Sv[j] = k + 1 < K ? agg_s[(b * K + k) * D + d] : 0.0f;
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int k = k0 + j;
+                if (k < K) {
+                    agg_h[((b * K + k) * D + d) * N + n] = H;
+                    if (k + 1 < K) H += fmaf(expm1f(A * Sv[j]), H, Wv[j]);
+                }
+            }
         }
     }
     if (conv_in != nullptr)
