@@ -96,8 +96,11 @@ __global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a) {
 // conv1d_bwd_reduce.
 constexpr int kBL = 64;
 
-template <typename IOT>
+// CW > 0: the width is known to be CW, and only the last CW of the 8 tap slots
+// (the nonzero ones) enter the sums.
+template <typename IOT, int CW = 0>
 __global__ __launch_bounds__(256) void conv1d_bwd_kernel(ConvBwdArgs a) {
+    constexpr int K0 = CW > 0 ? 8 - CW : 0;   // first nonzero tap slot
     const IOT *X = static_cast<const IOT *>(a.x);
     const IOT *DU = static_cast<const IOT *>(a.du);
     IOT *DX = static_cast<IOT *>(a.dx);
@@ -157,13 +160,13 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(ConvBwdArgs a) {
                 win[q] = xv[q];   // x_s, in the slot of x_{s-8}
                 float acc = cb;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], win[(q + 1 + i) & 7], acc);
+                for (int i = K0; i < 8; ++i) acc = fmaf(wk[i], win[(q + 1 + i) & 7], acc);
                 const float sgm = sigmoid_f(acc);
                 gxs = dv[q] * (sgm * (1.0f + acc * (1.0f - sgm)));
                 if (s < t1) {
                     pb += gxs;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) pw[i] = fmaf(gxs, win[(q + 1 + i) & 7], pw[i]);
+                    for (int i = K0; i < 8; ++i) pw[i] = fmaf(gxs, win[(q + 1 + i) & 7], pw[i]);
                 }
             }
             gr[q] = gxs;
@@ -171,7 +174,7 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(ConvBwdArgs a) {
             if (t < t1 && s < t1 + 7 && (t >= t0 || (run == 0 && t >= -(int64_t)(W - 1)))) {
                 float acc = 0.0f;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], gr[(q - i) & 7], acc);   // gx_{t+7-i}
+                for (int i = K0; i < 8; ++i) acc = fmaf(wk[i], gr[(q - i) & 7], acc);   // gx_{t+7-i}
                 if (t >= 0) {
                     store_io(DX + (b * L + t) * D + d, acc);
                 } else if (a.dstate != nullptr) {
@@ -182,7 +185,7 @@ __global__ __launch_bounds__(256) void conv1d_bwd_kernel(ConvBwdArgs a) {
     }
     float *pp = a.ws + (b * runs + run) * 9 * D + d;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pp[i * D] = pw[i];
+    for (int i = K0; i < 8; ++i) pp[i * D] = pw[i];   // slots below 8 - W are never read
     pp[8 * D] = pb;
 }
 
@@ -224,8 +227,12 @@ hipError_t launch_conv1d_bwd(const ConvBwdArgs &a, hipStream_t s) {
     const int64_t threads = a.B * runs * a.D;
     if (threads == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((threads + 255) / 256);
-    if (a.bf16)
+    if (a.bf16 && a.W == 4)
+        hipLaunchKernelGGL((conv1d_bwd_kernel<bf16_t, 4>), dim3(blocks), dim3(256), 0, s, a);
+    else if (a.bf16)
         hipLaunchKernelGGL(conv1d_bwd_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, a);
+    else if (a.W == 4)
+        hipLaunchKernelGGL((conv1d_bwd_kernel<float, 4>), dim3(blocks), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(conv1d_bwd_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
     hipError_t e = hipGetLastError();
