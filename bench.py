@@ -474,7 +474,24 @@ def bench_extras(torch, np, si, ssm, dev, args):
     ex["forward_bf16_B1_L65536_chunked"] = {"us_per_call": round(ms * 1e3, 2),
                                             "elements_per_s": L4 * D * N / (ms * 1e-3),
                                             "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
-    del y4, ws4
+    # the same long sequence with the 4-tap conv fused (x in instead of u; the
+    # conv-fused forward splits time with the headline kernel's layout)
+    cw4, cb4 = dev(r["conv_w"]), dev(r["conv_b"])
+    descc = ssm.ssm_scan_desc(1, L4, D, N, 4, 1, 0, 0)
+    ws4c = torch.empty(max(1, ssm.ssm_scan_fwd_workspace_size(descc)), dtype=torch.uint8, device="cuda")
+    f4c = lambda: ssm.ssm_scan_fwd(R["x"], R["dt_raw"], R["A_log"], R["B"], R["C"], dt_bias=R["dt_bias"],
+                                   Dskip=R["Dskip"], z=R["z"], conv_w=cw4, conv_b=cb4, y=y4, workspace=ws4c)
+    settle(torch, f4c)
+    tm = EventTimer(torch)
+    for _ in range(reps):
+        tm.run(f4c)
+    ms = tm.mean_ms()
+    nb = fwd_bytes(1, L4, D, N, 4, 2, conv=True)
+    ex["forward_bf16_B1_L65536_chunked_conv_fused"] = {"us_per_call": round(ms * 1e3, 2),
+                                                       "elements_per_s": L4 * D * N / (ms * 1e-3),
+                                                       "algorithmic_GBps": round(nb / (ms * 1e-3) / 1e9, 1)}
+    log("long bf16 forward, conv fused: %.1f us" % (ms * 1e3))
+    del y4, ws4, ws4c
     torch.cuda.empty_cache()
 
     # backward of the same workload, split in time by the library
