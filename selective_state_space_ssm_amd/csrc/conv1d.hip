@@ -22,8 +22,12 @@ namespace {
 
 constexpr int kTL = 32;
 
-template <typename IOT>
+// CW > 0: the width is known to be CW; only the last CW of the 8 tap slots
+// (the nonzero ones) enter the sum, and only the CW-1 inputs before a tile
+// are loaded.
+template <typename IOT, int CW = 0>
 __global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a) {
+    constexpr int K0 = CW > 0 ? 8 - CW : 0;   // first nonzero tap slot
     const IOT *X = static_cast<const IOT *>(a.x);
     IOT *Y = static_cast<IOT *>(a.y);
     const int64_t D = a.D, L = a.L;
@@ -48,10 +52,12 @@ __global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a) {
     for (int i = 0; i < 7; ++i) {
         const int64_t tt = t0 - 7 + i;
         float v = 0.0f;
-        if (tt >= 0)
-            v = to_f32(X[(b * L + tt) * D + d]);
-        else if (a.state_in != nullptr && tt >= -(int64_t)(W - 1))
-            v = a.state_in[(b * (W - 1) + (W - 1) + tt) * D + d];
+        if (i >= K0 - 1) {   // slots below are shifted out before any tap reads them
+            if (tt >= 0)
+                v = to_f32(X[(b * L + tt) * D + d]);
+            else if (a.state_in != nullptr && tt >= -(int64_t)(W - 1))
+                v = a.state_in[(b * (W - 1) + (W - 1) + tt) * D + d];
+        }
         win[i] = v;
     }
     win[7] = 0.0f;
@@ -67,7 +73,7 @@ __global__ __launch_bounds__(256) void conv1d_kernel(ConvArgs a) {
                 win[7] = xv[q];
                 float acc = cb;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc = fmaf(wk[i], win[i], acc);
+                for (int i = K0; i < 8; ++i) acc = fmaf(wk[i], win[i], acc);
 #pragma unroll
                 for (int i = 0; i < 7; ++i) win[i] = win[i + 1];
                 store_io(Y + (b * L + tg + q) * D + d, a.silu ? silu_f(acc) : acc);
@@ -251,8 +257,12 @@ hipError_t launch_conv1d(const ConvArgs &a, hipStream_t s) {
     const int64_t threads = a.B * tiles * a.D;
     if (threads == 0) return hipSuccess;
     const unsigned blocks = (unsigned)((threads + 255) / 256);
-    if (a.bf16)
+    if (a.bf16 && a.W == 4)
+        hipLaunchKernelGGL((conv1d_kernel<bf16_t, 4>), dim3(blocks), dim3(256), 0, s, a);
+    else if (a.bf16)
         hipLaunchKernelGGL(conv1d_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, a);
+    else if (a.W == 4)
+        hipLaunchKernelGGL((conv1d_kernel<float, 4>), dim3(blocks), dim3(256), 0, s, a);
     else
         hipLaunchKernelGGL(conv1d_kernel<float>, dim3(blocks), dim3(256), 0, s, a);
     return hipGetLastError();
