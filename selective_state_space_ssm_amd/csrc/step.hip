@@ -186,7 +186,8 @@ __global__ __launch_bounds__(256) void step_kernel(StepArgs a) {
 
 // The common shape on a shorter path: fp32 io, N = 16 (four lanes of four
 // states per channel), a 4-tap conv, D a multiple of 64 (every lane of every
-// workgroup holds a channel).  The loads are unconditional buffer loads on
+// workgroup holds a channel) and below 2^26 (a row's 16 * D state words fit
+// 32-bit byte offsets).  The loads are unconditional buffer loads on
 // per-row scalar bases with 32-bit lane offsets (no guards, no per-lane 64-bit
 // addresses); the arithmetic is step_kernel's for this shape, operation by
 // operation, so the two agree bit for bit.
@@ -360,7 +361,8 @@ hipError_t launch_step_dtproj(const StepArgs &a, hipStream_t s) {
 
 hipError_t launch_step(const StepArgs &a, hipStream_t s) {
     if (a.nblk * a.S * a.D == 0) return hipSuccess;
-    if (!a.bf16 && a.N == 16 && a.W == 4 && a.D % 64 == 0) {
+    // the fast path's lane offsets are 32-bit: D * 64 bytes of state per row
+    if (!a.bf16 && a.N == 16 && a.W == 4 && a.D % 64 == 0 && a.D < ((int64_t)1 << 26)) {
         const dim3 grid((unsigned)(a.nblk * a.S * (a.D / 64)));
 #define SSM_STEP_FAST(DI)                                                                            \
     if (a.disc == DI) {                                                                              \

@@ -460,6 +460,39 @@ def test_step_common_shape_loop_equals_forward(ssm, disc):
     assert torch.equal(cs[0], cso)
 
 
+def test_step_widest_rows_sampled(ssm):
+    """D = 2^26 channels per stream (16 * D state words = 4 GiB per row, past
+    the common-shape path's 32-bit offsets, so the general path runs): two
+    tokens, then sampled channels at the ends of the row and around the
+    powers of two compared with the oracle's step on those channels alone.
+    Inputs are drawn on the device from a seeded generator."""
+    S, D, N, W = 2, 1 << 26, 16, 4
+    g = torch.Generator(device="cuda").manual_seed(23)
+    rn = lambda *s: torch.randn(*s, generator=g, device="cuda")
+    h = rn(1, S, D, N)
+    cs = rn(1, S, W - 1, D)
+    prm = dict(A_log=0.5 * rn(1, D, N), conv_w=rn(1, D, W), conv_b=rn(1, D), dt_bias=0.3 * rn(1, D),
+               Dskip=rn(1, D))
+    tok = [dict(x=rn(1, S, D), dt_raw=rn(1, S, D), B=rn(1, S, N), C=rn(1, S, N), z=rn(1, S, D)) for _ in range(2)]
+    idx = torch.tensor([0, 1, 63, 64, (1 << 24) - 1, 1 << 24, (1 << 25) + 7, D - 65, D - 2, D - 1], device="cuda")
+    pick = lambda t, dim: np.ascontiguousarray(host(t.index_select(dim, idx)), dtype=np.float64)
+    ho, co = pick(h[0], 1), pick(cs[0], 2)
+    po = {k: pick(v[0], 0) for k, v in prm.items()}
+    ys = []
+    for tk in tok:
+        ys.append(ssm.ssm_step(h, tk["x"], tk["dt_raw"], prm["A_log"], tk["B"], tk["C"], conv_state=cs, z=tk["z"],
+                               conv_w=prm["conv_w"], conv_b=prm["conv_b"], dt_bias=prm["dt_bias"],
+                               Dskip=prm["Dskip"])[0].index_select(1, idx))
+    torch.cuda.synchronize()
+    for t, tk in enumerate(tok):
+        yr = oracle.step(ho, co, pick(tk["x"][0], 1), pick(tk["dt_raw"][0], 1), host(tk["B"][0]), host(tk["C"][0]),
+                         po["A_log"], z=pick(tk["z"][0], 1), conv_w=po["conv_w"], conv_b=po["conv_b"],
+                         dt_bias=po["dt_bias"], Dskip=po["Dskip"])
+        assert rel_linf(ys[t], yr) <= FP32_TOL, t
+    assert rel_linf(h[0].index_select(1, idx), ho) <= FP32_TOL
+    np.testing.assert_array_equal(host(cs[0].index_select(2, idx)), co)
+
+
 def test_step_graph_replay(ssm):
     """Streaming steps captured in a HIP graph (as the decode benchmark runs
     them): every replay, with eager work and synchronisation in between,
