@@ -88,7 +88,10 @@ typedef int32_t ssm_status;
 
 #define SSM_MAX_DSTATE 64
 #define SSM_MAX_CONV_WIDTH 8
-#define SSM_MAX_SCAN_DIM (1 << 24)   /* channels of a sequence scan: the kernels' tile offsets are 32-bit */
+#define SSM_MAX_SCAN_DIM ((1 << 24) - 1)   /* channels of a sequence scan: a 64-token tile of one
+                                             [B, L, D] float32 tensor, and one backward state
+                                             checkpoint (D * N <= 64 * D floats), stay under 2^32
+                                             bytes, the reach of the kernels' 32-bit offsets */
 #define SSM_STATIC_SCRATCH_BYTES (16u << 20)   /* ssm_scan_fwd_static's device buffer, per GPU */
 
 /* Descriptor of a sequence scan (forward or backward). */

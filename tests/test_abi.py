@@ -236,10 +236,22 @@ def test_launch_grid_limit(ssm):
     assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 40, D=16, N=1, chunk=1)) == ssm.SSM_ERR_BAD_SHAPE
     # accepted: stops at the missing workspace the split needs
     assert _fwd(ssm, _desc(ssm, B=1, L=2 ** 20, D=16, N=1, chunk=1)) == ssm.SSM_ERR_WORKSPACE
-    # channels past the sequence kernels' 32-bit tile offsets
-    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24 + 1, N=1)) == ssm.SSM_ERR_BAD_SHAPE
+    # channels past the sequence kernels' 32-bit tile offsets: a 64-token
+    # float32 tile of 2^24 channels is 2^32 bytes
+    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24, N=1)) == ssm.SSM_ERR_BAD_SHAPE
     # accepted: stops at y overlapping x
-    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24, N=1), y=_addr(0)) == ssm.SSM_ERR_ALIAS
+    assert _fwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24 - 1, N=1), y=_addr(0)) == ssm.SSM_ERR_ALIAS
+
+
+def test_bwd_checkpoint_offset_limit(ssm):
+    """The backward's state checkpoints (D * N floats a tile) take 32-bit byte
+    offsets; the channel limit keeps the widest one, N = 64 at the most
+    channels, under 2^32 bytes: it passes every shape check and stops at the
+    missing workspace, and one channel more is rejected."""
+    d = _desc(ssm, B=1, L=4, D=2 ** 24 - 1, N=64)
+    assert ssm.ssm_scan_bwd_workspace_size(d) > 0
+    assert _bwd(ssm, d) == ssm.SSM_ERR_WORKSPACE
+    assert _bwd(ssm, _desc(ssm, B=1, L=4, D=2 ** 24, N=64)) == ssm.SSM_ERR_BAD_SHAPE
 
 
 def test_bwd_sums_launch_grid_limit(ssm):
