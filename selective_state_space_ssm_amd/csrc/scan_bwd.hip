@@ -1158,26 +1158,33 @@ hipError_t launch_bwd_typed(const ScanBwdArgs &a, const BwdWs &w, hipStream_t s)
         if ((e = hipEventRecord(ss->fork, s)) != hipSuccess) return e;
         if ((e = hipStreamWaitEvent(ss->stream, ss->fork, 0)) != hipSuccess) return e;
         e = launch_scan_chunk_starts(f, a.chunk / sub, w.agg_h, w.agg_s, ss->stream);
+        // from here on the caller's stream waits for the side stream on every
+        // path, errors included, so that nothing it runs next (a free of the
+        // workspace) overtakes work already queued there
+        const hipError_t ej = hipEventRecord(ss->join, ss->stream);
+        if (e == hipSuccess) e = ej;
+        if (e == hipSuccess) {
+            // local end-to-start adjoints of chunks 1.., then the end adjoints
+            BwdLocalParams q{};
+            q.dt = a.dt; q.Cm = a.Cm; q.z = a.z; q.dy = a.dy; q.dt_bias = a.dt_bias; q.A_log = a.A_log;
+            q.R = w.RG; q.Sdt = w.Sdt;
+            q.B = a.B; q.L = a.L; q.D = a.D; q.N = a.N; q.chunk = a.chunk; q.KC = (int)KC; q.G = G;
+            const dim3 lgrid((unsigned)(a.B * (KC - 1) * G));
+            if (a.disc == DISC_CONST)
+                hipLaunchKernelGGL((bwd_local_kernel<IOT, S, true>), lgrid, dim3(kThreads), 0, s, q);
+            else
+                hipLaunchKernelGGL((bwd_local_kernel<IOT, S, false>), lgrid, dim3(kThreads), 0, s, q);
+            e = hipGetLastError();
+        }
+        if (e == hipSuccess) {
+            const int64_t nstate = a.B * a.D * a.N;
+            hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, a.A_log,
+                               a.dhT, w.RG, w.Sdt, a.B, a.D, a.N, (int)KC);
+            e = hipGetLastError();
+        }
+        const hipError_t ew = ej == hipSuccess ? hipStreamWaitEvent(s, ss->join, 0) : ej;
         if (e != hipSuccess) return e;
-        if ((e = hipEventRecord(ss->join, ss->stream)) != hipSuccess) return e;
-        // local end-to-start adjoints of chunks 1.., then the end adjoints
-        BwdLocalParams q{};
-        q.dt = a.dt; q.Cm = a.Cm; q.z = a.z; q.dy = a.dy; q.dt_bias = a.dt_bias; q.A_log = a.A_log;
-        q.R = w.RG; q.Sdt = w.Sdt;
-        q.B = a.B; q.L = a.L; q.D = a.D; q.N = a.N; q.chunk = a.chunk; q.KC = (int)KC; q.G = G;
-        const dim3 lgrid((unsigned)(a.B * (KC - 1) * G));
-        if (a.disc == DISC_CONST)
-            hipLaunchKernelGGL((bwd_local_kernel<IOT, S, true>), lgrid, dim3(kThreads), 0, s, q);
-        else
-            hipLaunchKernelGGL((bwd_local_kernel<IOT, S, false>), lgrid, dim3(kThreads), 0, s, q);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const int64_t nstate = a.B * a.D * a.N;
-        hipLaunchKernelGGL(bwd_carry_kernel, dim3((unsigned)((nstate + 255) / 256)), dim3(256), 0, s, a.A_log,
-                           a.dhT, w.RG, w.Sdt, a.B, a.D, a.N, (int)KC);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        if ((e = hipStreamWaitEvent(s, ss->join, 0)) != hipSuccess) return e;
+        if (ew != hipSuccess) return ew;
         const int64_t KS = num_bwd_chunks(a.L, a.chunk / sub);
         p.h0 = w.agg_h; p.h0_bs = KS * a.D * a.N; p.h0_ks = sub * a.D * a.N;
         p.dhT = w.RG; p.dhT_bs = KC * a.D * a.N; p.dhT_ks = a.D * a.N;
