@@ -26,6 +26,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 COPY_PROBE_ELEMS = 1 << 26          # 256 MiB read + 256 MiB written
 PREWARM_MS = 200                    # untimed headline launches before the warmup steps (clock ramp)
+CPU_SAMPLE_S = 10.0                 # host seconds the oracle is timed for on the headline workload
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "scan_fwd_B8_L2048_traffic.md")
 FWD_SOURCE = os.path.join(ROOT, "selective_state_space_ssm_amd", "csrc", "scan_fwd.hip")
 
@@ -654,8 +655,8 @@ def bench_extras(torch, np, si, ssm, dev, args):
 def cpu_baseline(np, si):
     """The float64 oracle, as it stands, on the host cores: the whole
     headline forward (conv, then the scan with the gate) over all 8 batch
-    rows with every host thread, five times (the mean is reported), and
-    batch row 0 alone on one thread."""
+    rows with every host thread, repeated for about CPU_SAMPLE_S seconds (the
+    mean per run is reported), and batch row 0 alone on one thread."""
     import oracle
     oracle.build(force=False)
     Bs, L, D, N, W = 8, 2048, 1536, 16, 4
@@ -671,11 +672,14 @@ def cpu_baseline(np, si):
                         Dskip=args["Dskip"], z=sl("z"))
 
     cores = oracle.num_threads()
-    reps, times = 5, []
-    for _ in range(reps):
+    # whole-workload runs repeated until about CPU_SAMPLE_S seconds of host
+    # time are spent (at least two runs, at most 500)
+    times, t_start = [], time.perf_counter()
+    while len(times) < 2 or (time.perf_counter() - t_start < CPU_SAMPLE_S and len(times) < 500):
         t0 = time.perf_counter()
         run(slice(0, Bs))
         times.append(time.perf_counter() - t0)
+    reps = len(times)
     dt = sum(times) / reps
     oracle.set_num_threads(1)
     t0 = time.perf_counter()
@@ -684,7 +688,7 @@ def cpu_baseline(np, si):
     oracle.set_num_threads(cores)
     return {"value": Bs * L * D * N / dt, "unit": "elements/s", "cores": cores, "kind": "oracle",
             "sample": "the whole forward workload (conv + scan + gate, B=8, L=2048, D=1536, N=16, float64), "
-                      "%d runs, mean %.3f s per run" % (reps, dt),
+                      "%d runs in %.1f s, mean %.3f s per run" % (reps, sum(times), dt),
             "single_thread": {"value": L * D * N / dt1, "unit": "elements/s", "cores": 1,
                               "sample": "batch row 0 of the same workload, %.2f s" % dt1}}
 
