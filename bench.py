@@ -218,6 +218,9 @@ def main():
                     help="also run a plain 1 GiB device copy (counter calibration under rocprofv3)")
     ap.add_argument("--probe", action="store_true",
                     help="only measure instruction rates, clock and the copy ceiling, print them as JSON")
+    ap.add_argument("--decode-eager", type=int, default=0, metavar="S",
+                    help="only run 12 whole-model decode steps of S streams, eagerly (no graph), for counter "
+                         "passes under rocprofv3; print a JSON line")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -239,6 +242,9 @@ def main():
               flush=True)
         return
     dev = lambda a, dt=torch.float32: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to("cuda", dt)
+    if args.decode_eager > 0:
+        decode_eager(torch, si, ssm, dev, args.decode_eager)
+        return
 
     # ------------------------------------------------------------ headline
     B, L, D, N, W = 8, 2048, 1536, 16, 4
@@ -650,6 +656,29 @@ def bench_extras(torch, np, si, ssm, dev, args):
         log("model decode, %d stream(s): %.1f us per token step" % (Sm, ms * 1e3))
         del ws, hm, cm, tk, lg
     return ex
+
+
+def decode_eager(torch, si, ssm, dev, S, steps=12):
+    """Mamba-mini decode steps of S streams launched one by one (no graph),
+    so that a profiler sees every dispatch of every step."""
+    cfg = si.MAMBA_MINI
+    mp = si.model_params(cfg)
+    emb = dev(mp["emb"])
+    nfw, nfb = dev(mp["norm_f_w"]), dev(mp["norm_f_b"])
+    layers = ssm.ModelLayers([{k: dev(v) for k, v in lay.items()} for lay in mp["layers"]])
+    desc = ssm.model_desc(cfg, S)
+    ws = torch.empty(ssm.ssm_model_decode_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    hm = torch.zeros(cfg["n_layers"], S, cfg["d_inner"], cfg["d_state"], device="cuda")
+    cm = torch.zeros(cfg["n_layers"], S, cfg["conv_width"] - 1, cfg["d_inner"], device="cuda")
+    tk = torch.from_numpy(si.model_tokens(cfg, S, steps).T.copy()).cuda()   # [steps, S]
+    lg = torch.empty(S, cfg["vocab"], device="cuda")
+    for t in range(steps):
+        ssm.ssm_model_decode_step(desc, emb, layers, tk[t], hm, cm, logits=lg, norm_f_w=nfw, norm_f_b=nfb,
+                                  workspace=ws)
+        torch.cuda.synchronize()
+        log("decode step %d of %d streams done" % (t, S))
+    print(json.dumps({"decode_eager": {"streams": S, "steps": steps,
+                                       "logits_finite": bool(torch.isfinite(lg).all())}}), flush=True)
 
 
 def cpu_baseline(np, si):
